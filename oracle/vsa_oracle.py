@@ -1,0 +1,301 @@
+"""CPU oracle for the Video Sparse Attention (VSA) hot path -- TEST INFRASTRUCTURE.
+
+This module is test infrastructure, not product code.  Only the test suite,
+the package's smoke check and the benchmark's CPU-baseline leg may import or
+run it.  It shares no code with the HIP path (no kernels, headers, tables or
+helpers) and imports nothing from it.
+
+It is a plain, slow, obviously correct float64 implementation of what the hot
+path computes, written from the pages:
+
+* "FastVideo VSA" (vllm-omni user guide), intro: the post-patch latent grid is
+  partitioned into spatiotemporal blocks; for every query block the key/value
+  blocks are scored and attention is computed only against the selected
+  top-k blocks.
+* same guide, "Choose top-k": the routing log line (seq_len, dit_seq_shape,
+  block_size, num_blocks, topk, keep_ratio); top-k counts key/value blocks
+  kept per query block; topk > num_blocks is invalid.
+* same guide, "Enable the backend": top-k must be positive.
+* same guide, intro and "Verify routing and fallback": non-causal
+  self-attention, equal Q/KV lengths, standard head_size**-0.5 scaling, equal
+  Q/K/V head counts, no mask, 256-token blocks.
+* FastVideo h3-perf-stack commit log, sm_100a tile-64 route entry: a boolean
+  block map compacted into per-row index lists with NON-uniform per-row counts
+  and zero-count rows; text-prefix query tiles dense, video tiles prefix +
+  top-k.
+* same log, FastH3 example entry: the gate branch pools per tile (the block
+  score uses per-block pooled queries and keys).
+
+Readings where the pages are silent (each also listed with the design notes):
+  R1 tokens are in raster order s = (t*H + h)*W + w;
+  R2 blocks are numbered raster-wise over the block grid, t-major;
+  R3 a block's pooled vector is the mean over its VALID tokens (edge blocks
+     divide by their own token count, not by the full block volume);
+  R4 the block score is the raw dot product of pooled query and pooled key
+     (no scale, no softmax -- both are monotone per row);
+  R5 ties in the top-k go to the lower block index; the decision is taken on
+     scores rounded to fp32, the precision the device path scores in;
+  R6 a selected row is reported sorted ascending by block index;
+  R7 no block is forced into its own row (pure top-k);
+  R8 an empty row gives O = 0 and LSE = -inf;
+  R9 padded tokens of edge blocks take no part in any softmax (masked).
+
+Parity pins for every function live in tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "Plan", "make_plan", "routing_line", "token_block_ids", "block_token_lists",
+    "pool_blocks", "block_scores", "select_topk", "selection_to_csr",
+    "map_to_csr", "block_sparse_attention", "vsa_reference", "valid_flops",
+]
+
+
+class Plan:
+    """Partition of a (T, H, W) latent grid into (bt, bh, bw) blocks.
+
+    "FastVideo VSA" guide, intro and "Choose top-k": num_blocks is the number
+    of spatiotemporal blocks the post-patch latent grid is cut into; edge
+    blocks are partial (readings R1, R2).
+    """
+
+    def __init__(self, seq_len, dit_seq_shape, block_size, topk=None):
+        t, h, w = (int(x) for x in dit_seq_shape)
+        bt, bh, bw = (int(x) for x in block_size)
+        if min(t, h, w, bt, bh, bw) < 1:
+            raise ValueError("grid and block sizes must be positive")
+        if int(seq_len) != t * h * w:
+            raise ValueError(f"seq_len {seq_len} != T*H*W = {t * h * w}")
+        self.seq_len = int(seq_len)
+        self.dit_seq_shape = (t, h, w)
+        self.block_size = (bt, bh, bw)
+        self.block_grid = (math.ceil(t / bt), math.ceil(h / bh), math.ceil(w / bw))
+        nt, nh, nw = self.block_grid
+        self.num_blocks = nt * nh * nw
+        self.block_volume = bt * bh * bw
+        if topk is not None:
+            topk = int(topk)
+            # "Enable the backend": top-k must be positive.
+            # "Choose top-k": topk > num_blocks is invalid for the shape.
+            if topk < 1 or topk > self.num_blocks:
+                raise ValueError(f"topk {topk} outside [1, {self.num_blocks}]")
+        self.topk = topk
+
+    def block_extent(self, beta):
+        """(origin, size) of block ``beta`` along t, h, w (sizes clipped at the grid edge)."""
+        nt, nh, nw = self.block_grid
+        it, rem = divmod(int(beta), nh * nw)
+        ih, iw = divmod(rem, nw)
+        org = (it * self.block_size[0], ih * self.block_size[1], iw * self.block_size[2])
+        size = tuple(min(b, g - o) for b, g, o in zip(self.block_size, self.dit_seq_shape, org))
+        return org, size
+
+    def block_counts(self):
+        """Valid-token count of every block, in block-id order."""
+        return np.array([int(np.prod(self.block_extent(b)[1])) for b in range(self.num_blocks)],
+                        dtype=np.int64)
+
+    def keep_ratio(self):
+        return None if self.topk is None else self.topk / self.num_blocks
+
+
+def make_plan(seq_len, dit_seq_shape, block_size, topk=None) -> Plan:
+    return Plan(seq_len, dit_seq_shape, block_size, topk)
+
+
+def routing_line(plan: Plan) -> str:
+    """The fields of the routing log line ("FastVideo VSA" guide, "Choose top-k").
+
+    keep_ratio is topk / num_blocks as a percentage with one decimal.  The route
+    is VSA for a sparse selection and VSA_ALL_BLOCKS when every block is kept
+    (the all-block path of "Choose top-k"; this path always runs the sparse
+    computation, it never switches to dense SDPA).
+    """
+    t, h, w = plan.dit_seq_shape
+    bt, bh, bw = plan.block_size
+    parts = [f"seq_len={plan.seq_len}", f"dit_seq_shape=({t}, {h}, {w})",
+             f"block_size=({bt}, {bh}, {bw})", f"num_blocks={plan.num_blocks}"]
+    if plan.topk is not None:
+        parts.append(f"topk={plan.topk}")
+        parts.append(f"keep_ratio={100.0 * plan.topk / plan.num_blocks:.1f}%")
+        parts.append("route=" + ("VSA_ALL_BLOCKS" if plan.topk == plan.num_blocks else "VSA"))
+    return ", ".join(parts)
+
+
+def token_block_ids(plan: Plan) -> np.ndarray:
+    """Block id of every token s (readings R1, R2)."""
+    t, h, w = plan.dit_seq_shape
+    bt, bh, bw = plan.block_size
+    nt, nh, nw = plan.block_grid
+    tt, hh, ww = np.meshgrid(np.arange(t), np.arange(h), np.arange(w), indexing="ij")
+    beta = ((tt // bt) * nh + (hh // bh)) * nw + (ww // bw)
+    return beta.reshape(-1)
+
+
+def block_token_lists(plan: Plan):
+    """For every block, the token indices it holds, ascending (raster order)."""
+    beta = token_block_ids(plan)
+    order = np.argsort(beta, kind="stable")
+    bounds = np.searchsorted(beta[order], np.arange(plan.num_blocks + 1))
+    return [order[bounds[b]:bounds[b + 1]] for b in range(plan.num_blocks)]
+
+
+def pool_blocks(x, plan: Plan) -> np.ndarray:
+    """Per-(batch, head, block) mean of x over the block's valid tokens (R3).
+
+    x: [B, S, heads, D] (any float dtype; upcast to float64).
+    Returns [B, heads, num_blocks, D] float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    lists = block_token_lists(plan)
+    out = np.empty((x.shape[0], x.shape[2], plan.num_blocks, x.shape[3]))
+    for b_id, toks in enumerate(lists):
+        out[:, :, b_id, :] = x[:, toks, :, :].mean(axis=1)
+    return out
+
+
+def block_scores(qbar, kbar) -> np.ndarray:
+    """Coarse block score sigma[i, j] = qbar_i . kbar_j per (batch, head) (R4).
+
+    "FastVideo VSA" guide, intro: for every query block VSA scores the
+    key/value blocks.  qbar, kbar: [B, heads, nb, D] -> [B, heads, nb, nb].
+    """
+    return np.matmul(np.asarray(qbar, np.float64), np.swapaxes(np.asarray(kbar, np.float64), -1, -2))
+
+
+def select_topk(scores, k):
+    """Per-row top-k of the block scores ("FastVideo VSA" guide, intro and "Choose top-k").
+
+    Keeps the k highest-scoring key blocks of each query-block row.  The
+    decision is taken on the scores rounded to fp32 with ties to the lower
+    block index (R5); each row is returned sorted ascending (R6).
+
+    Returns (sel int64 [..., nb, k], margin float64 [..., nb]) where margin is
+    the gap between the k-th and (k+1)-th largest float64 scores of the row
+    (+inf when k == nb): rows with a small margin are near-ties.
+    """
+    s64 = np.asarray(scores, np.float64)
+    nb = s64.shape[-1]
+    if not 1 <= k <= nb:
+        raise ValueError(f"topk {k} outside [1, {nb}]")
+    s32 = s64.astype(np.float32)
+    rows = s32.reshape(-1, nb)
+    rows64 = s64.reshape(-1, nb)
+    sel = np.empty((rows.shape[0], k), dtype=np.int64)
+    margin = np.empty(rows.shape[0])
+    idx = np.arange(nb)
+    for r in range(rows.shape[0]):
+        # primary key: score descending; secondary key: block index ascending
+        order = np.lexsort((idx, -rows[r].astype(np.float64)))
+        sel[r] = np.sort(order[:k])
+        desc = np.sort(rows64[r])[::-1]
+        margin[r] = math.inf if k == nb else desc[k - 1] - desc[k]
+    return sel.reshape(*s64.shape[:-1], k), margin.reshape(s64.shape[:-1])
+
+
+def selection_to_csr(sel):
+    """Uniform selection [B, heads, nb, k] -> CSR (row_ptr, col_idx), rows (b, h, i)."""
+    sel = np.asarray(sel)
+    k = sel.shape[-1]
+    rows = int(np.prod(sel.shape[:-1]))
+    row_ptr = np.arange(rows + 1, dtype=np.int64) * k
+    return row_ptr, sel.reshape(-1).astype(np.int64)
+
+
+def map_to_csr(block_map):
+    """Compact a boolean block map [..., nq, nk] into CSR lists.
+
+    FastVideo h3-perf-stack commit log, sm_100a tile-64 route entry: the
+    boolean map is compacted into per-row index lists whose counts may differ
+    from row to row and may be zero.  Rows are the flattened leading indices.
+    """
+    m = np.asarray(block_map, dtype=bool)
+    flat = m.reshape(-1, m.shape[-1])
+    counts = flat.sum(axis=1)
+    row_ptr = np.zeros(flat.shape[0] + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.nonzero(flat)[1].astype(np.int64)
+    return row_ptr, col_idx
+
+
+def block_sparse_attention(q, k, v, plan: Plan, row_ptr, col_idx, query_rows=None):
+    """Exact softmax attention of each query over the tokens of its row's blocks.
+
+    "FastVideo VSA" guide, intro: attention is computed only against the
+    selected blocks; "Verify routing and fallback": non-causal, scale
+    head_size**-0.5, equal head counts, no mask.  Padded positions do not exist
+    here: each block contributes only its valid tokens (R9).  Empty rows give
+    O = 0, LSE = -inf (R8).
+
+    q, k, v: [B, S, heads, D].  row_ptr/col_idx: CSR over rows (b, h, i).
+    query_rows: optional iterable of row ids (b*heads + h)*nb + i to compute;
+    other rows are left as NaN (for sampled checks of large shapes).
+    Returns (O [B, S, heads, D] float64, LSE [B, S, heads] float64, natural log).
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    bsz, s, nh, d = q.shape
+    nb = plan.num_blocks
+    lists = block_token_lists(plan)
+    scale = 1.0 / math.sqrt(d)
+    full = query_rows is None
+    out = np.zeros_like(q) if full else np.full_like(q, np.nan)
+    lse = np.full((bsz, s, nh), -np.inf) if full else np.full((bsz, s, nh), np.nan)
+    rows = range(bsz * nh * nb) if full else query_rows
+    for r in rows:
+        b, rem = divmod(int(r), nh * nb)
+        h, i = divmod(rem, nb)
+        qtok = lists[i]
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        if len(cols) == 0:
+            out[b, qtok, h, :] = 0.0
+            lse[b, qtok, h] = -np.inf
+            continue
+        ktok = np.concatenate([lists[j] for j in cols])
+        logits = (q[b, qtok, h, :] @ k[b, ktok, h, :].T) * scale
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)
+        denom = p.sum(axis=1, keepdims=True)
+        out[b, qtok, h, :] = (p @ v[b, ktok, h, :]) / denom
+        lse[b, qtok, h] = (mx + np.log(denom))[:, 0]
+    return out, lse
+
+
+def vsa_reference(q, k, v, dit_seq_shape, block_size, topk):
+    """Whole hot path: plan -> pool -> score -> top-k -> attention.
+
+    Returns a dict with the plan, pooled means, scores, selection, margins,
+    CSR, and the attention output / LSE.
+    """
+    s = q.shape[1]
+    plan = make_plan(s, dit_seq_shape, block_size, topk)
+    qbar = pool_blocks(q, plan)
+    kbar = pool_blocks(k, plan)
+    sc = block_scores(qbar, kbar)
+    sel, margin = select_topk(sc, topk)
+    row_ptr, col_idx = selection_to_csr(sel)
+    o, lse = block_sparse_attention(q, k, v, plan, row_ptr, col_idx)
+    return dict(plan=plan, qbar=qbar, kbar=kbar, scores=sc, sel=sel, margin=margin,
+                row_ptr=row_ptr, col_idx=col_idx, out=o, lse=lse)
+
+
+def valid_flops(plan: Plan, row_ptr, col_idx, head_dim) -> int:
+    """Multiply-add work of the attention counted on valid tokens only.
+
+    For every row (query block i) and every selected block j: 2*D flops for
+    q.k and 2*D for p*v per (valid query, valid key) pair.
+    """
+    c = plan.block_counts()
+    nb = plan.num_blocks
+    row_ptr = np.asarray(row_ptr, np.int64)
+    col_idx = np.asarray(col_idx, np.int64)
+    rows = len(row_ptr) - 1
+    keys_per_row = np.add.reduceat(np.append(c[col_idx], 0), row_ptr[:-1]) if len(col_idx) else np.zeros(rows, np.int64)
+    keys_per_row = np.where(np.diff(row_ptr) > 0, keys_per_row, 0)
+    q_counts = np.tile(c, rows // nb)
+    return int(4 * head_dim * np.sum(q_counts * keys_per_row))

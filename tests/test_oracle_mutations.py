@@ -1,0 +1,130 @@
+"""Plant plausible mistakes in the CPU oracle and check that a pin catches each.
+
+Every mutation here is applied to the oracle only, on the CPU, for the
+duration of one test (monkeypatch).  A mutation that no pin catches would mean
+the pins leave that part of the oracle unchecked.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.vsa_oracle as ov
+import tests.test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(ov, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(check, *args):
+    with pytest.raises(AssertionError):
+        check(*args)
+
+
+def test_pool_divided_by_block_volume_is_caught(monkeypatch):
+    def bad_pool(x, plan):
+        x = np.asarray(x, np.float64)
+        out = np.empty((x.shape[0], x.shape[2], plan.num_blocks, x.shape[3]))
+        for b_id, toks in enumerate(ov.block_token_lists(plan)):
+            out[:, :, b_id, :] = x[:, toks].sum(axis=1) / plan.block_volume
+        return out
+    _patch(monkeypatch, "pool_blocks", bad_pool)
+    _fails(pins.test_pool_planted_means_exact, (7, 13, 10))
+
+
+def test_transposed_scores_are_caught(monkeypatch):
+    _patch(monkeypatch, "block_scores",
+           lambda qb, kb: np.matmul(np.asarray(kb, float), np.swapaxes(np.asarray(qb, float), -1, -2)))
+    _fails(pins.test_score_planted_integer_products)
+
+
+def test_tie_to_higher_index_is_caught(monkeypatch):
+    orig = ov.select_topk
+
+    def bad(scores, k):
+        s = np.asarray(scores, np.float64)
+        flipped, m = orig(s[..., ::-1], k)
+        return np.sort(s.shape[-1] - 1 - flipped, axis=-1), m
+    _patch(monkeypatch, "select_topk", bad)
+    _fails(pins.test_topk_hand_examples_with_ties)
+
+
+def test_keeping_smallest_scores_is_caught(monkeypatch):
+    orig = ov.select_topk
+    _patch(monkeypatch, "select_topk", lambda s, k: orig(-np.asarray(s, np.float64), k))
+    _fails(pins.test_topk_hand_examples_with_ties)
+
+
+def _attention_with(logit_fn):
+    def att(q, k, v, plan, row_ptr, col_idx, query_rows=None):
+        q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+        bsz, s, nh, d = q.shape
+        nb = plan.num_blocks
+        lists = ov.block_token_lists(plan)
+        out = np.zeros_like(q)
+        lse = np.full((bsz, s, nh), -np.inf)
+        for r in range(bsz * nh * nb):
+            b, rem = divmod(r, nh * nb)
+            h, i = divmod(rem, nb)
+            cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+            if len(cols) == 0:
+                continue
+            qt = lists[i]
+            kt = np.concatenate([lists[j] for j in cols])
+            lg = logit_fn(q[b, qt, h], k[b, kt, h], d)
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            out[b, qt, h] = p @ v[b, kt, h] / p.sum(axis=1, keepdims=True)
+            lse[b, qt, h] = np.log(np.exp(lg).sum(axis=1))
+        return out, lse
+    return att
+
+
+def test_missing_softmax_scale_is_caught(monkeypatch):
+    _patch(monkeypatch, "block_sparse_attention", _attention_with(lambda qq, kk, d: qq @ kk.T))
+    _fails(pins.test_all_blocks_equals_library_dense_attention, "tiny")
+
+
+def test_wrong_scale_sign_is_caught(monkeypatch):
+    _patch(monkeypatch, "block_sparse_attention",
+           _attention_with(lambda qq, kk, d: -(qq @ kk.T) / math.sqrt(d)))
+    _fails(pins.test_attention_matches_dense_masked_bruteforce, 4)
+
+
+def test_keys_from_query_block_is_caught(monkeypatch):
+    # a wrong index: attend to the query block's own tokens instead of the row's blocks
+    orig = ov.block_sparse_attention
+
+    def bad(q, k, v, plan, row_ptr, col_idx, query_rows=None):
+        nb = plan.num_blocks
+        rows = len(row_ptr) - 1
+        cnt = np.diff(row_ptr)
+        ci = np.concatenate([np.full(cnt[r], r % nb) for r in range(rows)]).astype(np.int64)
+        return orig(q, k, v, plan, row_ptr, ci, query_rows)
+    _patch(monkeypatch, "block_sparse_attention", bad)
+    _fails(pins.test_attention_matches_dense_masked_bruteforce, 4)
+
+
+def test_w_major_block_numbering_is_caught(monkeypatch):
+    def bad_ids(plan):
+        t, h, w = plan.dit_seq_shape
+        bt, bh, bw = plan.block_size
+        nt, nh, nw = plan.block_grid
+        tt, hh, ww = np.meshgrid(np.arange(t), np.arange(h), np.arange(w), indexing="ij")
+        return (((ww // bw) * nh + (hh // bh)) * nt + (tt // bt)).reshape(-1)
+    _patch(monkeypatch, "token_block_ids", bad_ids)
+    _fails(pins.test_token_partition_hand_points_and_invariants)
+
+
+def test_floor_block_grid_is_caught(monkeypatch):
+    class FloorPlan(ov.Plan):
+        def __init__(self, *a, **kw):
+            super().__init__(*a, **kw)
+            self.block_grid = tuple(g // b for g, b in zip(self.dit_seq_shape, self.block_size))
+            nt, nh, nw = self.block_grid
+            self.num_blocks = nt * nh * nw
+    _patch(monkeypatch, "make_plan", lambda *a, **kw: FloorPlan(*a, **kw))
+    _fails(pins.test_routing_line_matches_page_worked_example, pins.os.path.join(
+        pins.os.path.dirname(pins.__file__), "golden"))
