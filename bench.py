@@ -1,0 +1,228 @@
+"""Benchmark of the VSA hot path on one MI355X.
+
+A step is one pass of the whole hot path over one layer's synthetic input
+(inputs resident in HBM): gather Q, K (with block mean-pooling) and V into
+block-major form, score the pooled blocks and pick the top-k per query block,
+run the block-sparse attention, scatter O back to raster order.  Every stage is
+a kernel of libvsa_amd.so launched through the C ABI on torch's current
+stream; HIP events on that stream bracket each stage of every timed step.
+
+Metric: effective TFLOP/s counting the selected blocks' valid tokens only
+(4 * D * sum over query blocks i of c_i * sum_{j in row i} c_j, from the map
+the step produced), divided by the whole step time; ms/layer is reported
+alongside.  The attention kernel's own rate against the bf16 MFMA peak is the
+roofline object.
+
+Default workload: the 27280-token (31, 22, 40) layer, block (4, 8, 8),
+24 heads, head_dim 128, topk 64, bf16 -- the shape of the routing example in
+the "FastVideo VSA" user guide ("Choose top-k").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--cpu-seconds S] [--only-attention]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import block_sparse_video_tile_amd as vsa  # noqa: E402
+from vsa_inputs import WORKLOADS, make_qkv, make_tile64_map  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "scatter"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def step_flops(plan, col_host, row_ptr_host, uniform_k):
+    counts = np.asarray(vsa.vsa_plan_block_counts(plan), dtype=np.int64)
+    nb = plan.num_blocks
+    rows = plan.num_rows()
+    if row_ptr_host is None:
+        keys = counts[col_host.reshape(rows, uniform_k)].sum(axis=1)
+        nnz = rows * uniform_k
+    else:
+        keys = np.zeros(rows, np.int64)
+        cnt = np.diff(row_ptr_host)
+        nz = np.nonzero(cnt)[0]
+        sums = np.add.reduceat(counts[col_host], row_ptr_host[:-1][nz]) if len(nz) else []
+        keys[nz] = sums
+        nnz = int(row_ptr_host[-1])
+    qc = np.tile(counts, rows // nb)
+    f_valid = 4 * plan.head_dim * int(np.sum(qc * keys))
+    f_nominal = 4 * plan.head_dim * plan.info["block_volume"] ** 2 * nnz
+    return f_valid, f_nominal
+
+
+def cpu_baseline(wl, q, k, v, budget_s):
+    """Time the CPU oracle on whole heads of the same layer until ~budget_s of work."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    heads_done, flops, t_total = 0, 0, 0.0
+    while heads_done < wl.heads and t_total < budget_s:
+        h = heads_done
+        qs, ks, vs = (t[:, :, h:h + 1].to(torch.float64).numpy() for t in (q, k, v))
+        t0 = time.perf_counter()
+        if wl.topk:
+            ref = oracle.vsa_reference(qs, ks, vs, wl.dit_seq_shape, wl.block_size, wl.topk)
+            rp, ci, plan = ref["row_ptr"], ref["col_idx"], ref["plan"]
+        else:
+            plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
+            rp_all, ci_all, _ = make_tile64_map(wl)
+            nb = plan.num_blocks
+            rp = rp_all[h * nb:(h + 1) * nb + 1] - rp_all[h * nb]
+            ci = ci_all[rp_all[h * nb]:rp_all[(h + 1) * nb]]
+            oracle.block_sparse_attention(qs, ks, vs, plan, rp, ci)
+        t_total += time.perf_counter() - t0
+        flops += oracle.valid_flops(plan, rp, ci, wl.head_dim)
+        heads_done += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads_done} of {wl.heads} heads of the same layer, whole hot path "
+                      f"(pool, score, top-k, attention) in float64 numpy; {t_total:.1f} s; "
+                      f"nproc={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan5b_k64", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"))
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; "
+                          f"--gpus {args.gpus} is not supported (no multi-GPU path)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {wl.name}: generating inputs")
+    q, k, v = make_qkv(wl)
+    dq, dk, dv = (t.to(dev) for t in (q, k, v))
+    plan = vsa.vsa_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, batch=wl.batch,
+                        num_heads=wl.heads, head_dim=wl.head_dim, topk=wl.topk or 0)
+    log(f"[bench] {vsa.vsa_plan_describe(plan)}")
+    qb = torch.empty(plan.blocked_shape(), dtype=torch.bfloat16, device=dev)
+    kb = torch.empty_like(qb)
+    ob = torch.empty_like(qb)
+    vb = torch.empty(plan.blocked_vt_shape(), dtype=torch.bfloat16, device=dev)
+    qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=dev)
+    kp = torch.empty_like(qp)
+    out = torch.empty(plan.raster_shape(), dtype=torch.bfloat16, device=dev)
+    if wl.topk:
+        col = torch.empty(plan.num_rows() * wl.topk, dtype=torch.int32, device=dev)
+        rp_dev, rp_host, uk = None, None, wl.topk
+        nnz = col.numel()
+    else:
+        rp_host, ci_host, _ = make_tile64_map(wl)
+        rp_dev = torch.as_tensor(rp_host).to(dev)
+        col = torch.as_tensor(ci_host).to(dev)
+        uk, nnz = 0, col.numel()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        def mark(n):
+            if ev is not None:
+                ev[n].record(stream)
+        mark(0)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, dq, qb, qp)
+        mark(1)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dk, kb, kp)
+        mark(2)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vb)
+        mark(3)
+        if wl.topk:
+            vsa.vsa_score_topk(plan, qp, kp, wl.topk, col)
+        mark(4)
+        vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vb, rp_dev, col, uk, nnz, ob)
+        mark(5)
+        vsa.vsa_scatter(plan, ob, out)
+        mark(6)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {name: [] for name in STAGES}
+    for ev in events:
+        for n, name in enumerate(STAGES):
+            stage_ms[name].append(ev[n].elapsed_time(ev[n + 1]))
+    gpu_ms = events[0][0].elapsed_time(events[-1][6]) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, gpu_ms)
+    col_host = col.cpu().numpy().astype(np.int64)
+    f_valid, f_nominal = step_flops(plan, col_host, None if rp_host is None else rp_host.astype(np.int64), uk)
+    t_attn = float(np.mean(stage_ms["attention"]))
+    attn_tflops = f_valid / (t_attn * 1e-3) / 1e12
+    value = f_valid / (ms_per_step * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == wl.name:
+            traffic = tj.get("bytes_per_launch")
+    result = {
+        "metric": "effective TFLOP/s (selected blocks) + ms/layer, 27280 tok, topk=64, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) tokens plus a per-block N(0,0.25) mean vector, bf16",
+        "config": {"workload": wl.name, "dit_seq_shape": list(wl.dit_seq_shape),
+                   "block_size": list(wl.block_size), "seq_len": wl.seq_len,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "batch": wl.batch,
+                   "topk": wl.topk, "num_blocks": plan.num_blocks,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in stage_ms.items()},
+        "flops_valid": f_valid,
+        "flops_nominal": f_nominal,
+        "attention_tflops_nominal": round(f_nominal / (t_attn * 1e-3) / 1e12, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+// Raster <-> block-major data movement for the VSA hot path on gfx950.
+//
+// "FastVideo VSA" user guide, intro: the post-patch latent grid is cut into
+// spatiotemporal blocks; "Choose top-k" notes the padding overhead this
+// introduces for shapes that do not divide evenly.  Edge blocks are padded
+// to the block volume with zero rows that the attention kernel masks.
+//
+// All three kernels are HBM-bound streams: one workgroup per (batch, head,
+// block), 16-byte loads and stores, one token row of one head (D = 128 bf16)
+// is 16 lanes x 16 bytes.
+
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnitsPerRow = kHeadDim * 2 / 16;  // 16-byte units per token row
+
+struct BlockBox {
+  int t0, h0, w0, ct, ch, cw, cnt;
+};
+
+__device__ inline BlockBox block_box(const VsaGeom& g, int beta) {
+  const int plane = g.nbh * g.nbw;
+  const int it = beta / plane;
+  const int rem = beta - it * plane;
+  const int ih = rem / g.nbw;
+  const int iw = rem - ih * g.nbw;
+  BlockBox b;
+  b.t0 = it * g.bt;
+  b.h0 = ih * g.bh;
+  b.w0 = iw * g.bw;
+  b.ct = min(g.bt, g.T - b.t0);
+  b.ch = min(g.bh, g.H - b.h0);
+  b.cw = min(g.bw, g.W - b.w0);
+  b.cnt = b.ct * b.ch * b.cw;
+  return b;
+}
+
+// Raster token index of the r-th valid token of a block (raster order inside the box).
+__device__ inline int64_t token_of(const VsaGeom& g, const BlockBox& b, int r) {
+  const int dw = r % b.cw;
+  const int q = r / b.cw;
+  const int dh = q % b.ch;
+  const int dt = q / b.ch;
+  return (int64_t(b.t0 + dt) * g.H + (b.h0 + dh)) * g.W + (b.w0 + dw);
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Q/K: raster [B,S,NH,D] -> blocked [B,NH,Npad,D], optional fp32 block means.
+__global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __restrict__ x,
+                                                             uint4* __restrict__ xb,
+                                                             float* __restrict__ pooled,
+                                                             VsaGeom g) {
+  __shared__ float red[kThreads / kUnitsPerRow][kHeadDim + 1];
+  const int wg = blockIdx.x;
+  const int beta = wg % g.nb;
+  const int bh = wg / g.nb;  // b * heads + h
+  const int h = bh % g.heads;
+  const int b = bh / g.heads;
+  const BlockBox box = block_box(g, beta);
+  const int unit = threadIdx.x % kUnitsPerRow;
+  const int lt = threadIdx.x / kUnitsPerRow;  // token lane, 16 tokens per pass
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  uint4* dst = xb + (int64_t(bh) * g.npad + int64_t(beta) * g.vol) * kUnitsPerRow;
+  for (int r = lt; r < g.vol; r += kThreads / kUnitsPerRow) {
+    uint4 val = make_uint4(0u, 0u, 0u, 0u);
+    if (r < box.cnt) {
+      const int64_t s = token_of(g, box, r);
+      val = x[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit];
+      acc[0] += bf16_lo(val.x); acc[1] += bf16_hi(val.x);
+      acc[2] += bf16_lo(val.y); acc[3] += bf16_hi(val.y);
+      acc[4] += bf16_lo(val.z); acc[5] += bf16_hi(val.z);
+      acc[6] += bf16_lo(val.w); acc[7] += bf16_hi(val.w);
+    }
+    dst[int64_t(r) * kUnitsPerRow + unit] = val;
+  }
+  if (pooled != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[lt][unit * 8 + i] = acc[i];
+    __syncthreads();
+    if (threadIdx.x < kHeadDim) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < kThreads / kUnitsPerRow; ++k) s += red[k][threadIdx.x];
+      pooled[(int64_t(bh) * g.nb + beta) * kHeadDim + threadIdx.x] = s / float(box.cnt);
+    }
+  }
+}
+
+// V: raster [B,S,NH,D] -> blocked-V^T [B,NH,Npad/64,D,64] (each 64-token
+// chunk stored d-major), transposed through LDS.
+__global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restrict__ x,
+                                                            uint4* __restrict__ xbt, VsaGeom g) {
+  // [token][d]; the 16-byte row pad keeps the 16-byte row stores aligned.
+  __shared__ __align__(16) uint16_t tile[kKvChunk][kHeadDim + 8];
+  const int wg = blockIdx.x;
+  const int beta = wg % g.nb;
+  const int bh = wg / g.nb;
+  const int h = bh % g.heads;
+  const int b = bh / g.heads;
+  const BlockBox box = block_box(g, beta);
+  const int chunks = g.vol / kKvChunk;
+  for (int c = 0; c < chunks; ++c) {
+    // load 64 token rows: 64 x 16 units, 4 per thread
+#pragma unroll
+    for (int p = 0; p < kKvChunk * kUnitsPerRow / kThreads; ++p) {
+      const int idx = threadIdx.x + p * kThreads;
+      const int tok = idx / kUnitsPerRow;
+      const int unit = idx % kUnitsPerRow;
+      const int r = c * kKvChunk + tok;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (r < box.cnt) {
+        const int64_t s = token_of(g, box, r);
+        val = x[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit];
+      }
+      *reinterpret_cast<uint4*>(&tile[tok][unit * 8]) = val;
+    }
+    __syncthreads();
+    // write 128 d-rows x 64 tokens: 128 x 8 units of 8 tokens, 4 per thread
+    uint4* dst = xbt + ((int64_t(bh) * (g.npad / kKvChunk) + int64_t(beta) * chunks + c) *
+                        kHeadDim) * (kKvChunk * 2 / 16);
+#pragma unroll
+    for (int p = 0; p < kHeadDim * 8 / kThreads; ++p) {
+      const int idx = threadIdx.x + p * kThreads;
+      // d fastest across lanes: the 2-byte column reads of one instruction
+      // then touch consecutive LDS words (no bank conflicts)
+      const int d = idx % kHeadDim;
+      const int ku = idx / kHeadDim;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = tile[ku * 8 + 2 * e][d];
+        const uint32_t hi = tile[ku * 8 + 2 * e + 1][d];
+        w[e] = lo | (hi << 16);
+      }
+      dst[int64_t(d) * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    __syncthreads();
+  }
+}
+
+// O: blocked [B,NH,Npad,D] -> raster [B,S,NH,D]; pad rows are not read.
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restrict__ ob,
+                                                           uint4* __restrict__ o, VsaGeom g) {
+  const int wg = blockIdx.x;
+  const int beta = wg % g.nb;
+  const int bh = wg / g.nb;
+  const int h = bh % g.heads;
+  const int b = bh / g.heads;
+  const BlockBox box = block_box(g, beta);
+  const int unit = threadIdx.x % kUnitsPerRow;
+  const int lt = threadIdx.x / kUnitsPerRow;
+  const uint4* src = ob + (int64_t(bh) * g.npad + int64_t(beta) * g.vol) * kUnitsPerRow;
+  for (int r = lt; r < box.cnt; r += kThreads / kUnitsPerRow) {
+    const int64_t s = token_of(g, box, r);
+    o[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit] =
+        src[int64_t(r) * kUnitsPerRow + unit];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* pooled,
+                            hipStream_t s) {
+  const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
+  hipLaunchKernelGGL(gather_qk_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                     static_cast<const uint4*>(x), static_cast<uint4*>(xb), pooled, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, hipStream_t s) {
+  const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
+  hipLaunchKernelGGL(gather_v_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                     static_cast<const uint4*>(x), static_cast<uint4*>(xbt), g);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const VsaGeom& g, const void* ob, void* o, hipStream_t s) {
+  const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
+  hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                     static_cast<const uint4*>(ob), static_cast<uint4*>(o), g);
+  return hipGetLastError();
+}
+
+}  // namespace vsa

@@ -1,0 +1,286 @@
+// Host side of the C ABI declared in include/vsa.h: plan validation, the
+// routing line, argument checks, and the sequencing of kernel launches.
+// Every argument check runs before the first HIP call.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "vsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vsa_status fail(vsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+vsa_status ok() {
+  g_last_error.clear();
+  return VSA_OK;
+}
+
+vsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(VSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+struct Workspace {
+  size_t q, k, v, o, qp, kp, col, total;
+};
+
+Workspace workspace_layout(const vsa_plan_s& p) {
+  const VsaGeom& g = p.g;
+  const size_t blk = size_t(g.batch) * g.heads * g.npad * g.head_dim * 2;
+  const size_t pooled = size_t(g.batch) * g.heads * g.nb * g.head_dim * 4;
+  const size_t col = size_t(g.batch) * g.heads * g.nb * (p.topk > 0 ? p.topk : 0) * 4;
+  Workspace w;
+  size_t off = 0;
+  w.q = off; off += align256(blk);
+  w.k = off; off += align256(blk);
+  w.v = off; off += align256(blk);
+  w.o = off; off += align256(blk);
+  w.qp = off; off += align256(pooled);
+  w.kp = off; off += align256(pooled);
+  w.col = off; off += align256(col);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(vsa_status st) {
+  switch (st) {
+    case VSA_OK: return "VSA_OK";
+    case VSA_ERR_INVALID_ARGUMENT: return "VSA_ERR_INVALID_ARGUMENT";
+    case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+    case VSA_ERR_HIP: return "VSA_ERR_HIP";
+  }
+  return "VSA_ERR_UNKNOWN";
+}
+
+const char* vsa_last_error(void) { return g_last_error.c_str(); }
+
+vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
+  if (!d || !out) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: null desc or out pointer");
+  *out = nullptr;
+  for (int i = 0; i < 3; ++i) {
+    if (d->dit_seq_shape[i] < 1)
+      return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: dit_seq_shape[%d] = %d must be >= 1", i,
+                  d->dit_seq_shape[i]);
+    if (d->block_size[i] < 1)
+      return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: block_size[%d] = %d must be >= 1", i,
+                  d->block_size[i]);
+  }
+  if (d->batch < 1 || d->num_heads < 1 || d->head_dim < 1)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: batch, num_heads, head_dim must be >= 1");
+  const int64_t T = d->dit_seq_shape[0], H = d->dit_seq_shape[1], W = d->dit_seq_shape[2];
+  if (d->seq_len != T * H * W)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: seq_len %lld != T*H*W = %lld",
+                (long long)d->seq_len, (long long)(T * H * W));
+  const int64_t nbt = (T + d->block_size[0] - 1) / d->block_size[0];
+  const int64_t nbh = (H + d->block_size[1] - 1) / d->block_size[1];
+  const int64_t nbw = (W + d->block_size[2] - 1) / d->block_size[2];
+  const int64_t nb = nbt * nbh * nbw;
+  const int64_t vol = int64_t(d->block_size[0]) * d->block_size[1] * d->block_size[2];
+  if (d->topk < 0 || d->topk > nb)
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_plan: topk %d outside [1, num_blocks=%lld] (0 selects map mode)", d->topk,
+                (long long)nb);
+  if (d->dtype != VSA_DTYPE_BF16)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: dtype %d not implemented (bf16 only)", d->dtype);
+  if (d->head_dim != vsa::kHeadDim)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: head_dim %d not implemented (128 only)",
+                d->head_dim);
+  if (vol % 64 != 0 || vol > 256)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "vsa_plan: block volume %lld not implemented (64, 128, 192 or 256)",
+                (long long)vol);
+  const int64_t npad = nb * vol;
+  const int64_t elems = int64_t(d->batch) * d->num_heads * npad * d->head_dim;
+  if (nb > (int64_t(1) << 20) || elems > (int64_t(1) << 40) ||
+      int64_t(d->batch) * d->num_heads * nb > (int64_t(1) << 30))
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: problem too large for this implementation");
+  vsa_plan_s* p = new (std::nothrow) vsa_plan_s;
+  if (!p) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: out of host memory");
+  VsaGeom& g = p->g;
+  g.T = int32_t(T); g.H = int32_t(H); g.W = int32_t(W);
+  g.bt = d->block_size[0]; g.bh = d->block_size[1]; g.bw = d->block_size[2];
+  g.nbt = int32_t(nbt); g.nbh = int32_t(nbh); g.nbw = int32_t(nbw);
+  g.nb = int32_t(nb);
+  g.vol = int32_t(vol);
+  g.heads = d->num_heads;
+  g.batch = d->batch;
+  g.head_dim = d->head_dim;
+  g.S = d->seq_len;
+  g.npad = npad;
+  p->topk = d->topk;
+  p->dtype = d->dtype;
+  *out = p;
+  return ok();
+}
+
+vsa_status vsa_plan_destroy(vsa_plan_t plan) {
+  delete plan;
+  return ok();
+}
+
+vsa_status vsa_plan_get_info(vsa_plan_t p, vsa_plan_info* out) {
+  if (!p || !out) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan_get_info: null argument");
+  const VsaGeom& g = p->g;
+  out->block_grid[0] = g.nbt;
+  out->block_grid[1] = g.nbh;
+  out->block_grid[2] = g.nbw;
+  out->num_blocks = g.nb;
+  out->block_volume = g.vol;
+  out->padded_len = g.npad;
+  out->blocked_elems = int64_t(g.batch) * g.heads * g.npad * g.head_dim;
+  out->pooled_elems = int64_t(g.batch) * g.heads * g.nb * g.head_dim;
+  out->num_rows = int64_t(g.batch) * g.heads * g.nb;
+  return ok();
+}
+
+vsa_status vsa_plan_describe(vsa_plan_t p, char* buf, size_t n) {
+  if (!p || !buf) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan_describe: null argument");
+  const VsaGeom& g = p->g;
+  char line[512];
+  int len = snprintf(line, sizeof(line),
+                     "seq_len=%lld, dit_seq_shape=(%d, %d, %d), block_size=(%d, %d, %d), "
+                     "num_blocks=%d",
+                     (long long)g.S, g.T, g.H, g.W, g.bt, g.bh, g.bw, g.nb);
+  if (p->topk > 0) {
+    len += snprintf(line + len, sizeof(line) - len, ", topk=%d, keep_ratio=%.1f%%, route=%s",
+                    p->topk, 100.0 * p->topk / g.nb,
+                    p->topk == g.nb ? "VSA_ALL_BLOCKS" : "VSA");
+  }
+  if (size_t(len) + 1 > n)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan_describe: buffer of %zu bytes < %d needed",
+                n, len + 1);
+  memcpy(buf, line, size_t(len) + 1);
+  return ok();
+}
+
+vsa_status vsa_plan_block_counts(vsa_plan_t p, int32_t* counts, int64_t n) {
+  if (!p || !counts) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan_block_counts: null argument");
+  if (n < p->g.nb)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan_block_counts: n = %lld < num_blocks = %d",
+                (long long)n, p->g.nb);
+  for (int b = 0; b < p->g.nb; ++b) counts[b] = vsa::block_count(p->g, b);
+  return ok();
+}
+
+vsa_status vsa_gather(vsa_plan_t p, int32_t role, const void* x, void* xb, float* pooled,
+                      void* stream) {
+  if (!p || !x || !xb) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: null argument");
+  if (role != VSA_ROLE_Q && role != VSA_ROLE_K && role != VSA_ROLE_V)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: unknown role %d", role);
+  if (role == VSA_ROLE_V) {
+    if (pooled) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: pooled must be NULL for V");
+    return hip_status(vsa::launch_gather_v(p->g, x, xb, hipStream_t(stream)), "vsa_gather(V)");
+  }
+  return hip_status(vsa::launch_gather_qk(p->g, x, xb, pooled, hipStream_t(stream)),
+                    "vsa_gather(Q/K)");
+}
+
+vsa_status vsa_scatter(vsa_plan_t p, const void* ob, void* o, void* stream) {
+  if (!p || !ob || !o) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter: null argument");
+  return hip_status(vsa::launch_scatter(p->g, ob, o, hipStream_t(stream)), "vsa_scatter");
+}
+
+vsa_status vsa_score_topk(vsa_plan_t p, const float* qp, const float* kp, int32_t topk,
+                          int32_t* col, float* scores, void* stream) {
+  if (!p || !qp || !kp || !col)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_score_topk: null argument");
+  if (topk < 1 || topk > p->g.nb)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_score_topk: topk %d outside [1, %d]", topk,
+                p->g.nb);
+  if (p->g.nb > 1024)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_score_topk: num_blocks %d > 1024 not implemented",
+                p->g.nb);
+  return hip_status(vsa::launch_score_topk(p->g, qp, kp, topk, col, scores, hipStream_t(stream)),
+                    "vsa_score_topk");
+}
+
+vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k, const void* v,
+                                     const int32_t* row_ptr, const int32_t* col,
+                                     int32_t uniform_k, int64_t nnz, void* o, float* lse,
+                                     void* stream) {
+  if (!p || !q || !k || !v || !o)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: null argument");
+  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: nnz < 0");
+  if (nnz > 0 && !col)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: null col_idx with nnz > 0");
+  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
+  if (!row_ptr) {
+    if (uniform_k < 0 || uniform_k > p->g.nb)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_fwd: uniform_k %d outside [0, %d]", uniform_k, p->g.nb);
+    if (nnz < rows * uniform_k)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_fwd: nnz %lld < rows*uniform_k = %lld", (long long)nnz,
+                  (long long)(rows * uniform_k));
+  }
+  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                         hipStream_t(stream)),
+                    "vsa_block_sparse_attn_fwd");
+}
+
+vsa_status vsa_forward_workspace_size(vsa_plan_t p, size_t* bytes) {
+  if (!p || !bytes) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_workspace_size: null");
+  *bytes = workspace_layout(*p).total;
+  return ok();
+}
+
+vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v, void* out,
+                       void* ws, size_t ws_bytes, int32_t* col_out, float* lse, void* stream) {
+  if (!p || !q || !k || !v || !out || !ws)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: null argument");
+  if (p->topk < 1)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: plan is in map mode (topk == 0)");
+  if (p->g.nb > 1024)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_forward: num_blocks %d > 1024 not implemented",
+                p->g.nb);
+  const Workspace w = workspace_layout(*p);
+  if (ws_bytes < w.total)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: workspace %zu bytes < %zu needed",
+                ws_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: workspace not 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  void* qb = base + w.q;
+  void* kb = base + w.k;
+  void* vb = base + w.v;
+  void* ob = base + w.o;
+  float* qp = reinterpret_cast<float*>(base + w.qp);
+  float* kp = reinterpret_cast<float*>(base + w.kp);
+  int32_t* col = col_out ? col_out : reinterpret_cast<int32_t*>(base + w.col);
+  hipStream_t s = hipStream_t(stream);
+  const VsaGeom& g = p->g;
+  const int64_t nnz = int64_t(g.batch) * g.heads * g.nb * p->topk;
+  hipError_t e;
+  if ((e = vsa::launch_gather_qk(g, q, qb, qp, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather Q");
+  if ((e = vsa::launch_gather_qk(g, k, kb, kp, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather K");
+  if ((e = vsa::launch_gather_v(g, v, vb, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather V");
+  if ((e = vsa::launch_score_topk(g, qp, kp, p->topk, col, nullptr, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward: score/top-k");
+  if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward: attention");
+  if ((e = vsa::launch_scatter(g, ob, out, s)) != hipSuccess) return hip_status(e, "vsa_forward: scatter");
+  return ok();
+}
+
+}  // extern "C"

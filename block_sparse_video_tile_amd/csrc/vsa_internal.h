@@ -1,0 +1,58 @@
+// Internal declarations shared by the host ABI (vsa_api.cpp) and the HIP
+// kernel sources.  Not part of the public interface (include/vsa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "vsa.h"
+
+// Geometry of one plan, passed to kernels by value.
+struct VsaGeom {
+  int32_t T, H, W;        // latent grid
+  int32_t bt, bh, bw;     // block size
+  int32_t nbt, nbh, nbw;  // block grid
+  int32_t nb;             // number of blocks
+  int32_t vol;            // block volume V
+  int32_t heads;
+  int32_t batch;
+  int32_t head_dim;
+  int64_t S;              // tokens
+  int64_t npad;           // nb * vol
+};
+
+struct vsa_plan_s {
+  VsaGeom g;
+  int32_t topk;   // 0 = map mode
+  int32_t dtype;
+};
+
+namespace vsa {
+
+constexpr int kHeadDim = 128;
+constexpr int kKvChunk = 64;  // keys per attention sub-tile and per V^T chunk
+
+// Valid-token count of block `beta` (host and device).
+__host__ __device__ inline int block_count(const VsaGeom& g, int beta) {
+  const int plane = g.nbh * g.nbw;
+  const int it = beta / plane;
+  const int rem = beta - it * plane;
+  const int ih = rem / g.nbw;
+  const int iw = rem - ih * g.nbw;
+  const int ct = min(g.bt, g.T - it * g.bt);
+  const int ch = min(g.bh, g.H - ih * g.bh);
+  const int cw = min(g.bw, g.W - iw * g.bw);
+  return ct * ch * cw;
+}
+
+hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* pooled,
+                            hipStream_t s);
+hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, hipStream_t s);
+hipError_t launch_scatter(const VsaGeom& g, const void* ob, void* o, hipStream_t s);
+hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp, int topk,
+                             int32_t* col, float* scores, hipStream_t s);
+hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
+                           const int32_t* row_ptr, const int32_t* col, int uniform_k,
+                           int64_t nnz, void* o, float* lse, hipStream_t s);
+
+}  // namespace vsa

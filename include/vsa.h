@@ -1,0 +1,206 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) Video Sparse Attention hot path.
+ *
+ * What the path computes (the "FastVideo VSA" user guide, intro): the
+ * post-patch latent grid (T, H, W) of a video DiT layer is cut into
+ * spatiotemporal blocks; every key/value block is scored for every query
+ * block, and exact softmax attention runs only against the top-k key/value
+ * blocks of each query block.  The same guide's "Choose top-k" section gives
+ * the shape vocabulary (seq_len, dit_seq_shape, block_size, num_blocks, topk,
+ * keep_ratio) and states that top-k counts key/value blocks kept per query
+ * block; "Verify routing and fallback" lists the kernel's operating
+ * conditions (bf16/fp16 tensors, 256-token blocks, head_size**-0.5 scaling,
+ * equal head counts, no mask, no sequence parallelism).  FastVideo's
+ * h3-perf-stack commit log (sm_100a tile-64 route entry) adds 64-token 1-D
+ * tiles and compacted block maps whose per-row counts differ from row to row
+ * and may be zero.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns vsa_status; on failure vsa_last_error() returns
+ *     a thread-local reason string.  Nothing aborts and no C++ exception
+ *     crosses this boundary.
+ *   - Device pointers are caller-owned HIP device allocations on the current
+ *     device; the library never allocates, frees or retains them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued asynchronously on it; no call synchronises the
+ *     host.  Device faults surface at the caller's next synchronisation.
+ *   - Element types: bf16 tensors are 2-byte IEEE bfloat16, fp32 are IEEE
+ *     binary32, indices are int32.
+ *   - Host-side argument checks happen before any HIP call, so every
+ *     VSA_ERR_INVALID_ARGUMENT / VSA_ERR_UNSUPPORTED path works without a GPU.
+ *
+ * Layouts (B = batch, NH = heads, D = head_dim = 128, S = seq_len,
+ * nb = num_blocks, V = block volume = bt*bh*bw, Npad = nb*V):
+ *   raster   [B, S, NH, D]   token s = (t*H + h)*W + w, w fastest.
+ *   blocked  [B, NH, Npad, D]  block b occupies rows b*V .. b*V+V-1; its
+ *            c_b valid tokens come first in raster order, the remaining
+ *            V - c_b rows are zero padding.  Used for Q, K and O.
+ *   blocked-V^T [B, NH, Npad/64, D, 64]  the same token rows cut into
+ *            64-token chunks, each chunk stored d-major (token index
+ *            fastest), padding zero.  Used for V.
+ *   pooled   [B, NH, nb, D] fp32.
+ *   scores   [B, NH, nb, nb] fp32, row = query block, column = key block.
+ *   CSR rows r = (b*NH + h)*nb + i; col_idx entries are key-block ids in
+ *            [0, nb) of the same (b, h).
+ *   lse      [B, NH, Npad] fp32, natural log; -inf on empty rows and pads.
+ */
+#ifndef VSA_H_
+#define VSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vsa_status {
+  VSA_OK = 0,
+  VSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, inconsistent or out-of-range size */
+  VSA_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels implement */
+  VSA_ERR_HIP = 3               /* a HIP runtime call or kernel launch failed */
+} vsa_status;
+
+typedef enum vsa_dtype { VSA_DTYPE_BF16 = 0, VSA_DTYPE_FP16 = 1 } vsa_dtype;
+
+typedef enum vsa_role { VSA_ROLE_Q = 0, VSA_ROLE_K = 1, VSA_ROLE_V = 2 } vsa_role;
+
+/* Shape of one attention layer call ("FastVideo VSA" guide, "Choose top-k":
+ * the fields of its routing log line). */
+typedef struct vsa_plan_desc {
+  int64_t seq_len;          /* S; must equal T*H*W */
+  int32_t dit_seq_shape[3]; /* (T, H, W) post-patch latent grid, each >= 1 */
+  int32_t block_size[3];    /* (bt, bh, bw); V = bt*bh*bw in {64, 128, 192, 256} */
+  int32_t batch;            /* B >= 1 */
+  int32_t num_heads;        /* NH >= 1; equal for Q, K and V */
+  int32_t head_dim;         /* D; 128 is implemented */
+  int32_t topk;             /* key blocks kept per query block, 1..nb; 0 = the
+                               caller supplies a block map (CSR) instead */
+  int32_t dtype;            /* vsa_dtype; VSA_DTYPE_BF16 is implemented */
+} vsa_plan_desc;
+
+/* Derived sizes of a plan (host values). */
+typedef struct vsa_plan_info {
+  int32_t block_grid[3];    /* (ceil(T/bt), ceil(H/bh), ceil(W/bw)) */
+  int32_t num_blocks;       /* nb = product of block_grid */
+  int32_t block_volume;     /* V */
+  int64_t padded_len;       /* Npad = nb*V */
+  int64_t blocked_elems;    /* B*NH*Npad*D elements of one blocked tensor */
+  int64_t pooled_elems;     /* B*NH*nb*D */
+  int64_t num_rows;         /* B*NH*nb CSR rows */
+} vsa_plan_info;
+
+typedef struct vsa_plan_s* vsa_plan_t;
+
+/* Validate `desc` and build an immutable host-side plan.  Makes no HIP call.
+ * Block ids are raster-ordered over the block grid (t-major); a block's valid
+ * count is the product over t, h, w of min(b_d, G_d - i_d*b_d).
+ * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes,
+ *   seq_len != T*H*W, topk < 0 or topk > nb ("Choose top-k": larger than
+ *   num_blocks is invalid; "Enable the backend": it must be positive, with 0
+ *   reserved here for map mode); UNSUPPORTED for head_dim != 128, dtype other
+ *   than bf16, or V not in {64, 128, 192, 256}.
+ * Ownership: *out is owned by the caller and released with vsa_plan_destroy;
+ * a plan may be shared across threads and streams. */
+vsa_status vsa_plan(const vsa_plan_desc* desc, vsa_plan_t* out);
+
+/* Release a plan (NULL is accepted and ignored). */
+vsa_status vsa_plan_destroy(vsa_plan_t plan);
+
+/* Copy the derived sizes of `plan` into *out. */
+vsa_status vsa_plan_get_info(vsa_plan_t plan, vsa_plan_info* out);
+
+/* Write the NUL-terminated routing line of the plan into buf[0..buf_len):
+ * "seq_len=S, dit_seq_shape=(T, H, W), block_size=(bt, bh, bw),
+ *  num_blocks=nb, topk=k, keep_ratio=P%, route=VSA" with P = 100*k/nb to one
+ * decimal, the fields of the routing log line in "Choose top-k".  The route
+ * is VSA_ALL_BLOCKS when k == nb (the all-block path always runs the sparse
+ * kernel) and the topk/keep_ratio/route fields are omitted in map mode.
+ * Errors: INVALID_ARGUMENT if buf is NULL or buf_len is too small (nothing is
+ * written beyond buf_len). */
+vsa_status vsa_plan_describe(vsa_plan_t plan, char* buf, size_t buf_len);
+
+/* Host array of the nb per-block valid-token counts, in block-id order.
+ * `n` must be >= nb. */
+vsa_status vsa_plan_block_counts(vsa_plan_t plan, int32_t* counts, int64_t n);
+
+/* Raster -> blocked gather with tail padding (pad rows written as zero).
+ * role Q or K: writes x_blk in the blocked layout and, if `pooled` is not
+ * NULL, the fp32 mean of each block's valid tokens (the per-block pooled
+ * vector the block score is built from: the guide's intro has every key block
+ * scored per query block, and the h3 FastH3 log entry pools per tile).
+ * role V: writes x_blk in the blocked-V^T layout; `pooled` must be NULL.
+ * x_raster: device, B*S*NH*D bf16.  x_blk: device, B*NH*Npad*D bf16.
+ * pooled: device, B*NH*nb*D fp32, or NULL. */
+vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void* x_blk,
+                      float* pooled, void* stream);
+
+/* Blocked -> raster scatter of an output tensor (pad rows are dropped).
+ * o_blk: device, blocked layout, bf16.  o_raster: device, raster layout, bf16. */
+vsa_status vsa_scatter(vsa_plan_t plan, const void* o_blk, void* o_raster, void* stream);
+
+/* Block score and per-row top-k ("FastVideo VSA" guide, intro: every key
+ * block is scored for every query block and the top-k are kept).
+ * score[i][j] = dot(q_pooled[i], k_pooled[j]) in fp32 per (b, h); each row
+ * keeps its `topk` largest scores, ties going to the lower block index, and
+ * writes their block ids ascending to col_idx[row*topk .. row*topk+topk).
+ * The rows are uniform CSR rows (row_ptr[r] = r*topk).
+ * q_pooled, k_pooled: device fp32 pooled layout.  col_idx: device int32,
+ * B*NH*nb*topk entries.  scores: device fp32 [B,NH,nb,nb] or NULL.
+ * Errors: INVALID_ARGUMENT for null inputs or topk outside [1, nb]. */
+vsa_status vsa_score_topk(vsa_plan_t plan, const float* q_pooled, const float* k_pooled,
+                          int32_t topk, int32_t* col_idx, float* scores, void* stream);
+
+/* Block-sparse attention forward on blocked tensors ("FastVideo VSA" guide,
+ * intro: attention only against the selected blocks; "Verify routing and
+ * fallback": non-causal, equal Q/KV lengths, scale head_dim**-0.5, equal head
+ * counts; h3-perf-stack log, sm_100a entry: non-uniform and zero-count rows).
+ * For every valid query token of block i in row r the output is
+ *   softmax_j(q . k_j / sqrt(D)) v_j over the valid tokens of the blocks
+ *   listed in row r,
+ * padded keys masked; an empty row yields O = 0 and LSE = -inf; pad query
+ * rows are written as 0 (LSE -inf).
+ * q_blk, k_blk: device bf16 blocked layout.  v_blk: device bf16 blocked-V^T.
+ * row_ptr: device int32 [B*NH*nb + 1] CSR offsets into col_idx, or NULL for
+ *   uniform rows of `uniform_k` entries each (row r uses entries
+ *   r*uniform_k .. r*uniform_k + uniform_k - 1).
+ * col_idx: device int32 block ids, `nnz` entries (nnz = B*NH*nb*uniform_k in
+ *   uniform mode).  Row offsets are clamped to [0, nnz] and ids outside
+ *   [0, nb) are skipped, so a malformed map cannot read out of bounds.  Ids in
+ *   a row must be unique (a repeated id weighs that block twice); ascending
+ *   order is recommended for cache reuse, the result does not depend on it.
+ * o_blk: device bf16 blocked layout.  lse: device fp32 [B,NH,Npad] or NULL.
+ * Errors: INVALID_ARGUMENT for null pointers, nnz < 0, uniform_k outside
+ *   [0, nb] in uniform mode. */
+vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t plan, const void* q_blk, const void* k_blk,
+                                     const void* v_blk, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t uniform_k, int64_t nnz,
+                                     void* o_blk, float* lse, void* stream);
+
+/* Bytes of device workspace vsa_forward needs for this plan (blocked Q, K,
+ * V, O, pooled Q and K, and the selected block ids, each 256-byte aligned). */
+vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
+
+/* The whole hot path for a plan with topk >= 1, raster in and raster out:
+ * gather Q, K (with pooling) and V; score and top-k; block-sparse attention;
+ * scatter O.  q, k, v: device bf16 raster.  out: device bf16 raster.
+ * workspace: device buffer of at least vsa_forward_workspace_size bytes,
+ * 256-byte aligned, not shared with a concurrently running call.
+ * col_idx_out: optional device int32 copy target for the selected ids
+ * (B*NH*nb*topk) or NULL.  lse: optional device fp32 [B,NH,Npad] or NULL.
+ * Errors: INVALID_ARGUMENT for null pointers or a map-mode plan (topk == 0). */
+vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void* v, void* out,
+                       void* workspace, size_t workspace_bytes, int32_t* col_idx_out,
+                       float* lse, void* stream);
+
+/* Static description of a status code. */
+const char* vsa_status_string(vsa_status status);
+
+/* Reason for the most recent failure on the calling thread ("" if none). */
+const char* vsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H_ */

@@ -1,0 +1,147 @@
+"""Host-side tests of the C ABI: no GPU needed.
+
+The library must load, export every function include/vsa.h declares, and
+reject every malformed request with the documented status before any HIP
+call (mirroring host-side route checks that need no device).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import block_sparse_video_tile_amd as vsa
+import oracle
+from tests.test_oracle_pins import _golden_fields, _line_fields
+
+FAKE = 1 << 20   # a non-NULL address; every call below fails validation before using it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vsa.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = vsa.exported_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(vsa.__all__)
+
+
+def test_status_strings(lib):
+    assert vsa.vsa_status_string(0) == "VSA_OK"
+    assert vsa.vsa_status_string(3) == "VSA_ERR_HIP"
+
+
+def test_describe_matches_page_worked_example(golden_dir):
+    page = _golden_fields(os.path.join(golden_dir, "routing_line.txt"))
+    plan = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), batch=1, num_heads=24, topk=64)
+    ours = _line_fields(vsa.vsa_plan_describe(plan))
+    for key in page:
+        if key != "checkpoint_mode":
+            assert ours[key] == page[key], key
+
+
+def test_describe_all_blocks_and_map_mode():
+    p = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), topk=120)
+    assert vsa.vsa_plan_describe(p).endswith("keep_ratio=100.0%, route=VSA_ALL_BLOCKS")
+    p = vsa.vsa_plan(33280, (1, 1, 33280), (1, 1, 64), topk=0)
+    assert vsa.vsa_plan_describe(p) == ("seq_len=33280, dit_seq_shape=(1, 1, 33280), "
+                                        "block_size=(1, 1, 64), num_blocks=520")
+
+
+def test_describe_small_buffer_is_rejected():
+    p = vsa.vsa_plan(2048, (8, 16, 16), (4, 8, 8), topk=4)
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_plan_describe(p, buf_len=10)
+    assert e.value.status == vsa.VSA_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("shape,block", [((31, 22, 40), (4, 8, 8)), ((81, 30, 52), (4, 8, 8)),
+                                         ((7, 13, 10), (4, 8, 8)), ((1, 1, 33280), (1, 1, 64)),
+                                         ((5, 9, 17), (2, 8, 8)), ((3, 5, 70), (1, 4, 48))])
+def test_plan_geometry_agrees_with_oracle(shape, block):
+    s = int(np.prod(shape))
+    p = vsa.vsa_plan(s, shape, block, batch=2, num_heads=3)
+    o = oracle.make_plan(s, shape, block)
+    assert p.info["block_grid"] == o.block_grid
+    assert p.num_blocks == o.num_blocks
+    assert p.padded_len == o.num_blocks * o.block_volume
+    assert vsa.vsa_plan_block_counts(p) == o.block_counts().tolist()
+    assert p.info["num_rows"] == 2 * 3 * o.num_blocks
+    assert p.info["blocked_elems"] == 2 * 3 * p.padded_len * 128
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(seq_len=27281), vsa.VSA_ERR_INVALID_ARGUMENT),             # S != T*H*W
+    (dict(topk=121), vsa.VSA_ERR_INVALID_ARGUMENT),                  # topk > num_blocks
+    (dict(topk=-1), vsa.VSA_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), vsa.VSA_ERR_INVALID_ARGUMENT),
+    (dict(num_heads=0), vsa.VSA_ERR_INVALID_ARGUMENT),
+    (dict(dit_seq_shape=(0, 22, 40), seq_len=0), vsa.VSA_ERR_INVALID_ARGUMENT),
+    (dict(block_size=(4, 8, 0)), vsa.VSA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=64), vsa.VSA_ERR_UNSUPPORTED),
+    (dict(dtype=vsa.VSA_DTYPE_FP16), vsa.VSA_ERR_UNSUPPORTED),
+    (dict(block_size=(2, 4, 4)), vsa.VSA_ERR_UNSUPPORTED),           # V = 32
+    (dict(block_size=(4, 8, 16)), vsa.VSA_ERR_UNSUPPORTED),          # V = 512
+])
+def test_plan_rejects(kwargs, status):
+    args = dict(seq_len=27280, dit_seq_shape=(31, 22, 40), block_size=(4, 8, 8), batch=1,
+                num_heads=24, head_dim=128, topk=64, dtype=vsa.VSA_DTYPE_BF16)
+    args.update(kwargs)
+    with pytest.raises(vsa.VsaError) as e:
+        vsa.vsa_plan(**args)
+    assert e.value.status == status
+    assert vsa.vsa_last_error()            # a reason is always given
+
+
+@pytest.fixture
+def plan():
+    return vsa.vsa_plan(2048, (8, 16, 16), (4, 8, 8), batch=1, num_heads=2, topk=4)
+
+
+def _raw(fn_name, *args):
+    return getattr(vsa.load_library(), fn_name)(*args)
+
+
+def test_null_and_range_checks_before_any_device_call(plan):
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    assert _raw("vsa_gather", h, 0, None, FAKE, None, None) == bad
+    assert _raw("vsa_gather", h, 0, FAKE, None, None, None) == bad
+    assert _raw("vsa_gather", h, 7, FAKE, FAKE, None, None) == bad          # unknown role
+    assert _raw("vsa_gather", h, 2, FAKE, FAKE, FAKE, None) == bad          # pooled with V
+    assert _raw("vsa_scatter", h, None, FAKE, None) == bad
+    assert _raw("vsa_score_topk", h, FAKE, FAKE, 0, FAKE, None, None) == bad   # topk < 1
+    assert _raw("vsa_score_topk", h, FAKE, FAKE, 9, FAKE, None, None) == bad   # topk > nb
+    assert _raw("vsa_score_topk", h, None, FAKE, 4, FAKE, None, None) == bad
+    f = "vsa_block_sparse_attn_fwd"
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 9, 9 * 16, FAKE, None, None) == bad  # k > nb
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 63, FAKE, None, None) == bad      # nnz short
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE, 0, -1, FAKE, None, None) == bad      # nnz < 0
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, None, 0, 5, FAKE, None, None) == bad       # col NULL
+    assert _raw(f, h, None, FAKE, FAKE, None, FAKE, 4, 64, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 64, None, None, None) == bad
+    assert _raw("vsa_plan_block_counts", h, None, 8) == bad
+
+
+def test_forward_checks(plan):
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    need = vsa.vsa_forward_workspace_size(plan)
+    assert need > 0 and need % 256 == 0
+    f = "vsa_forward"
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, None, None, None) == bad  # alignment
+    assert _raw(f, h, FAKE, None, FAKE, FAKE, FAKE, need, None, None, None) == bad
+    mp = vsa.vsa_plan(2048, (8, 16, 16), (4, 8, 8), topk=0)
+    assert _raw(f, mp.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None, None) == bad
+    assert "map mode" in vsa.vsa_last_error()
+
+
+def test_binding_rejects_host_tensors(plan):
+    import torch
+    x = torch.zeros(plan.raster_shape(), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, x, x)

@@ -104,7 +104,7 @@ def make_qkv(wl: Workload, dtype=torch.bfloat16):
         mu = torch.randn(wl.batch, nh, *cells, wl.head_dim, generator=g) * 0.5
         eps = torch.randn(wl.batch, wl.seq_len, nh, wl.head_dim, generator=g)
         x = eps + _piecewise_field(mu, wl.dit_seq_shape, wl.block_size)
-        out.append(x.to(dtype))
+        out.append(x.to(dtype).contiguous())
         del mu, eps, x
     return tuple(out)
 
@@ -157,7 +157,7 @@ def make_planted_block_means(seed, batch, heads, dit_seq_shape, block_size,
     cells = _coarse_cells(dit_seq_shape, block_size)
     mu = torch.randint(lo, hi + 1, (batch, heads, *cells, head_dim), generator=g)
     x = _piecewise_field(mu.to(torch.float32), dit_seq_shape, block_size)
-    return x.to(dtype), mu
+    return x.to(dtype).contiguous(), mu
 
 
 def bf16_to_f64(x: torch.Tensor) -> np.ndarray:
