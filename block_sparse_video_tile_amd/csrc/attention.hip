@@ -15,9 +15,11 @@
 //   heads, and its L2 serves their shared key/value blocks.
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
-//   loaded).  K (64 x 128) and V^T (128 x 64) sub-tiles go HBM/L2 -> VGPR ->
-//   LDS, double-buffered, one barrier per sub-tile; the next sub-tile's global
-//   loads are in flight while the current one is computed.
+//   loaded).  K (64 x 128) and V^T (128 x 64) sub-tiles are copied HBM/L2 ->
+//   LDS directly (global_load_lds_dwordx4, no VGPR staging), double-buffered,
+//   one barrier per sub-tile.  K runs one sub-tile ahead of V so that the
+//   next sub-tile's QK^T can run on the matrix cores while this sub-tile's
+//   softmax runs on the VALU (software pipeline inside each wave).
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, D[m][n] += A[m][k] B[k][n];
 // lane l holds A row m = l%32, B column n = l%32, and accumulator register
@@ -35,11 +37,12 @@
 //   the keys of PV step c are the contiguous run 16c + 8*(l/32) + 0..7 and the
 //   matching V^T operand is one 16-byte LDS read.
 //
-// Online softmax (exact up to rounding): running max m and sum l per query in
-// fp32, p = exp2(s*log2(e)/sqrt(D) - m*log2(e)/sqrt(D)) on the transcendental
-// unit, P rounded to bf16 for the PV product, O rescaled by exp2 of the max
-// change.  Padded keys of a partial sub-tile are masked to -inf.  A row
-// without blocks leaves l = 0 and writes O = 0, LSE = -inf.
+// Online softmax (exact up to rounding): running reference max m and sum l per
+// query in fp32, p = exp2(s*log2(e)/sqrt(D) - m*log2(e)/sqrt(D)) on the
+// transcendental unit, l summed from the fp32 p, P rounded to bf16 for the PV
+// product, O rescaled by exp2 of the max change only when the max grows by
+// more than 2^8 (so p <= 256).  Padded keys of a partial sub-tile are masked
+// to -inf.  A row without blocks leaves l = 0 and writes O = 0, LSE = -inf.
 
 #include "vsa_internal.h"
 
@@ -64,21 +67,31 @@ __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
 __device__ inline int kappa(int key) {
   return (key & ~0xc) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
-// 16-byte-unit swizzles that keep the MFMA operand reads conflict-free.
-__device__ inline int k_pos(int row, int unit) { return row * 16 + (unit ^ (row & 15)); }
-__device__ inline int v_pos(int d, int unit) { return d * 8 + (unit ^ ((d ^ (d >> 3)) & 7)); }
+
+// LDS tiles use padded rows so that every MFMA operand read is one base
+// register plus an immediate offset and the 16-byte reads of 8 (or 16)
+// consecutive lanes fall on distinct banks:
+//   K   : 64 rows (keys, kappa-permuted) x (16 + 1) 16-byte units = 17 KB
+//   V^T : 128 rows (d) x (8 + 1) units = 18 KB
+// The pad unit of each row is filled with a copy of the row's first unit.
+constexpr int kKRow = 17, kVRow = 9;
+constexpr int kKUnits = 64 * kKRow;    // 1088
+constexpr int kVUnits = 128 * kVRow;   // 1152
+constexpr int kKChunks = kKUnits / 64;  // 17 wave-loads of 1 KB
+constexpr int kVChunks = kVUnits / 64;  // 18
+constexpr int kORow = 17;               // epilogue O staging row: 272 B
 
 struct TileCursor {
-  int64_t e;   // CSR entry
-  int sub;     // 64-key sub-tile inside the block
-  int j;       // key block id
-  int cj;      // its valid-token count
+  int e;    // CSR entry, relative to the row start
+  int sub;  // 64-key sub-tile inside the block
+  int j;    // key block id
+  int cj;   // its valid-token count
 };
 
 // Move to the first sub-tile of the next valid CSR entry after `c.e`.
-__device__ inline bool next_entry(TileCursor& c, int64_t end, const int32_t* __restrict__ col,
+__device__ inline bool next_entry(TileCursor& c, int len, const int32_t* __restrict__ col,
                                   const VsaGeom& g) {
-  for (++c.e; c.e < end; ++c.e) {
+  for (++c.e; c.e < len; ++c.e) {
     const int j = col[c.e];
     if (j >= 0 && j < g.nb) {
       c.j = j;
@@ -90,25 +103,72 @@ __device__ inline bool next_entry(TileCursor& c, int64_t end, const int32_t* __r
   return false;
 }
 
-__device__ inline bool next_tile(TileCursor& c, int64_t end, const int32_t* __restrict__ col,
+__device__ inline bool next_tile(TileCursor& c, int len, const int32_t* __restrict__ col,
                                  const VsaGeom& g) {
   if ((c.sub + 1) * kKvChunk < c.cj) {
     ++c.sub;
     return true;
   }
-  return next_entry(c, end, col, g);
+  return next_entry(c, len, col, g);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One wave copies 64 x 16 bytes from global memory straight into LDS: lane l
+// reads `src + off` and its 16 bytes land at `dst + 16*l`.
+__device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* dst) {
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + off),
+                                   (lds_ptr_t)(dst), 16, 0, 0);
+}
+
+// S^T (2 tiles of 32 keys x 32 queries) = K sub-tile (LDS) x Q^T (VGPRs).
+__device__ inline void qk_tile(const uint4* __restrict__ kl, const bf16x8 (&qf)[8],
+                               f32x16 (&st)[2]) {
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) st[mt][j] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const bf16x8 a = as_bf16x8(kl[mt * 32 * kKRow + 2 * s]);
+      st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[mt], 0, 0, 0);
+    }
+  }
+}
+
+// p = exp2(s*c - mb) for the 32 scores of this lane: fp32 partial sums for l,
+// bf16 values grouped as the B operands of the 4 PV steps (16 keys each).
+__device__ inline void exp_tile(const f32x16 (&st)[2], float c, float mb, bf16x8 (&pb)[4],
+                                float& rs0, float& rs1) {
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(st[cc / 2][8 * (cc % 2) + t], c, -mb));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(st[cc / 2][8 * (cc % 2) + t + 1], c, -mb));
+      rs0 += p0;
+      rs1 += p1;
+      pb[cc][t] = __bf16(p0);
+      pb[cc][t + 1] = __bf16(p1);
+    }
 }
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ vt,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
-    int64_t nnz, uint2* __restrict__ o, float* __restrict__ lse, VsaGeom g, float scale_log2,
+    int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, VsaGeom g, float scale_log2,
     float scale) {
-  constexpr int kThreads = NW * 64;
-  constexpr int kPer = (kUnits + kThreads - 1) / kThreads;  // 16-byte units per thread
-  constexpr bool kEven = kUnits % kThreads == 0;
-  __shared__ __align__(16) uint4 lds[2][2][kUnits];  // [stage][K | V^T][unit]
+  static_assert(2 * (kKUnits + kVUnits) >= NW * 32 * kORow, "O staging must fit in LDS");
+  const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
+  // K runs one sub-tile ahead of V: while sub-tile n is finished, K buffer
+  // n^1 holds K_{n+1} (read) and buffer n receives K_{n+2}; V buffer n holds
+  // V_n (read) and buffer n^1 receives V_{n+1}.
+  __shared__ __align__(16) uint4 smem[2 * kKUnits + 2 * kVUnits];
+  uint4* const kbuf0 = smem;
+  uint4* const vbuf0 = smem + 2 * kKUnits;
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   const int64_t r = xcd_remap(blockIdx.x, nrows);
@@ -116,11 +176,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: lives in an SGPR
   const int lane = tid % 64;
   const int half = lane / 32;
-  const int qrow = wave * 32 + (lane & 31);  // this lane's query row inside the block
-  const bool active = wave * 32 < cq;        // wave-uniform
+  const int l32 = lane & 31;
+  const int qrow = wave * 32 + l32;      // this lane's query row inside the block
+  const bool active = wave * 32 < cq;    // wave-uniform
 
   int64_t beg, end;
   if (row_ptr != nullptr) {
@@ -130,6 +191,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     beg = r * uniform_k;
     end = beg + uniform_k;
   }
+  const int32_t* rcol = col + beg;
+  const int len = int(end - beg);
 
   const int64_t qk_row0 = bh * g.npad + int64_t(i) * g.vol;  // first token row of block i
   bf16x8 qf[8];
@@ -147,129 +210,164 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int64_t kv_chunks_per_head = g.npad / kKvChunk;
+  const uint4* const kbase = k + bh * g.npad * 16;
+  const uint4* const vbase = vt + bh * (g.npad / kKvChunk) * kUnits;
   const int chunks_per_block = g.vol / kKvChunk;
-  uint4 pk[kPer], pv[kPer];
-
-  auto load_tile = [&](const TileCursor& c) {
-    const uint4* ks = k + (bh * g.npad + int64_t(c.j) * g.vol + int64_t(c.sub) * kKvChunk) * 16;
-    const uint4* vs =
-        vt + (bh * kv_chunks_per_head + int64_t(c.j) * chunks_per_block + c.sub) * kUnits;
+  // per-lane source offsets (16-byte units inside a sub-tile) of this wave's
+  // chunk loads; the same for every sub-tile
+  constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
+  uint32_t koff[kMaxK], voff[kMaxV];
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      if (kEven || tid + p * kThreads < kUnits) {
-        pk[p] = ks[tid + p * kThreads];
-        pv[p] = vs[tid + p * kThreads];
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-      const int idx = tid + p * kThreads;
-      if (kEven || idx < kUnits) {
-        lds[stage][0][k_pos(kappa(idx / 16), idx % 16)] = pk[p];
-        lds[stage][1][v_pos(idx / 8, idx % 8)] = pv[p];
-      }
-    }
-  };
-
-  TileCursor cur;
-  cur.e = beg - 1;
-  bool have = next_entry(cur, end, col, g);
-  if (have) {
-    load_tile(cur);
-    store_tile(0);
+  for (int u = 0; u < kMaxK; ++u) {
+    const int pos = (wave + u * NW) * 64 + lane;
+    const int row = pos / kKRow, unit = pos % kKRow;
+    koff[u] = kappa(row) * 16 + (unit < 16 ? unit : 0);
   }
+#pragma unroll
+  for (int u = 0; u < kMaxV; ++u) {
+    const int pos = (wave + u * NW) * 64 + lane;
+    const int row = pos / kVRow, unit = pos % kVRow;
+    voff[u] = row * 8 + (unit < 8 ? unit : 0);
+  }
+  auto load_k = [&](const TileCursor& c, int b) {
+    const uint4* src = kbase + (int64_t(c.j) * g.vol + c.sub * kKvChunk) * 16;
+#pragma unroll
+    for (int u = 0; u < kMaxK; ++u)
+      if (wave + u * NW < kKChunks)
+        wave_copy_to_lds(src, koff[u], kbuf0 + b * kKUnits + (wave + u * NW) * 64);
+  };
+  auto load_v = [&](const TileCursor& c, int b) {
+    const uint4* src = vbase + (int64_t(c.j) * chunks_per_block + c.sub) * kUnits;
+#pragma unroll
+    for (int u = 0; u < kMaxV; ++u)
+      if (wave + u * NW < kVChunks)
+        wave_copy_to_lds(src, voff[u], vbuf0 + b * kVUnits + (wave + u * NW) * 64);
+  };
+  auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // cursors of sub-tiles n, n+1, n+2
+  TileCursor c0, c1, c2;
+  c0.e = -1;
+  bool h0 = next_entry(c0, len, rcol, g);
+  c1 = c0;
+  bool h1 = h0 && next_tile(c1, len, rcol, g);
+  c2 = c1;
+  bool h2 = h1 && next_tile(c2, len, rcol, g);
+  if (h0) {
+    load_k(c0, 0);
+    load_v(c0, 0);
+  }
+  if (h1) load_k(c1, 1);
+  wait_loads();
   __syncthreads();
-  int stage = 0;
 
-  while (have) {
-    TileCursor nxt = cur;
-    const bool have_next = next_tile(nxt, end, col, g);
-    if (have_next) load_tile(nxt);
+  // per-lane operand bases: K row l32 (+ half unit), V^T row l32 (+ half unit)
+  const int kread = l32 * kKRow + half;
+  const int vread = l32 * kVRow + half;
 
+  f32x16 sa[2], sb[2];
+  if (h0 && active) qk_tile(kbuf0 + kread, qf, sa);
+
+  // Finish sub-tile n (scores in `cur`) and compute the scores of n+1 into `nxt`.
+  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const int n) {
+    if (h2) load_k(c2, n);      // K_{n+2} replaces K_n
+    if (h1) load_v(c1, n ^ 1);  // V_{n+1} replaces V_{n-1}
     if (active) {
-      const uint4* kl = lds[stage][0];
-      const uint4* vl = lds[stage][1];
-      // ---- S^T = K Q^T for the 64 keys of this sub-tile (2 tiles of 32 keys)
-      f32x16 st[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) st[mt][j] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int row = mt * 32 + (lane & 31);
-          const bf16x8 a = as_bf16x8(kl[k_pos(row, 2 * s + half)]);
-          st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[mt], 0, 0, 0);
-        }
-      }
-      // ---- mask keys past the block's valid count (only in its last sub-tile)
-      const int valid = cur.cj - cur.sub * kKvChunk;
+      // mask keys past the block's valid count (only in its last sub-tile)
+      const int valid = c0.cj - c0.sub * kKvChunk;
       if (valid < kKvChunk) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = mt * 32 + 16 * (j / 8) + 8 * half + (j % 8);
-            if (key >= valid) st[mt][j] = -INFINITY;
+            if (key >= valid) cur[mt][j] = -INFINITY;
           }
       }
-      // ---- online softmax: row max over this lane's 32 keys and the partner lane's
-      float mx = st[0][0];
+      // row max over this lane's 32 keys and the partner lane's (l ^ 32)
+      float mx = cur[0][0];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[mt][j]);
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[mt][j]);
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      m_run = m_new;
-      const float mb = m_new * scale_log2;
-      float rs = 0.f;
+      // Lazy rescale: the reference max m_run only moves (and O, l are only
+      // rescaled) when a score exceeds it by more than 8 in log2 units, so
+      // every p = exp2((s - m_run) * scale * log2 e) stays <= 2^8.  The final
+      // O / l is the same softmax whichever reference max was used.
+      if (__ballot(mx > m_run + rescale_thr) != 0) {  // wave-uniform branch
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(st[mt][j], scale_log2, -mb));
-          st[mt][j] = p;
-          rs += p;
+          for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+      }
+      const float mb = m_run * scale_log2;
+      bf16x8 pb[4];
+      float rs0 = 0.f, rs1 = 0.f;
+      if (h1) {
+        // next sub-tile's QK^T on the matrix cores, interleaved with this
+        // sub-tile's exponentials on the VALU
+        qk_tile(kbuf0 + (n ^ 1) * kKUnits + kread, qf, nxt);
+        exp_tile(cur, scale_log2, mb, pb, rs0, rs1);
+        // K operand reads run 4 ahead of the MFMAs that consume them; every
+        // MFMA is followed by 7 VALU instructions of the softmax
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
         }
-      l_run = l_run * alpha + rs;
+      } else {
+        exp_tile(cur, scale_log2, mb, pb, rs0, rs1);
+      }
+      l_run += rs0 + rs1;
+      // O^T += V^T P^T, 4 steps of 16 keys
+      const uint4* vl = vbuf0 + n * kVUnits + vread;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
-      // ---- O^T += V^T P^T, 4 steps of 16 keys
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bf16x8 pb;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pb[t] = __bf16(st[c / 2][8 * (c % 2) + t]);
+      for (int cc = 0; cc < 4; ++cc) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int d = dt * 32 + (lane & 31);
-          const bf16x8 a = as_bf16x8(vl[v_pos(d, 2 * c + half)]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
+          const bf16x8 a = as_bf16x8(vl[dt * 32 * kVRow + 2 * cc]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[dt], 0, 0, 0);
         }
       }
+      // V operand reads run 2 ahead of the MFMAs that consume them
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (u < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
     }
-
-    if (have_next) store_tile(stage ^ 1);
+    wait_loads();
     __syncthreads();
-    stage ^= 1;
-    cur = nxt;
-    have = have_next;
+    TileCursor c3 = c2;
+    const bool h3 = h2 && next_tile(c3, len, rcol, g);
+    c0 = c1;
+    h0 = h1;
+    c1 = c2;
+    h1 = h2;
+    c2 = c3;
+    h2 = h3;
+  };
+
+  while (h0) {
+    step(sa, sb, 0);
+    if (!h0) break;
+    step(sb, sa, 1);
   }
 
-  // ---- epilogue: combine the two lane halves' partial sums, normalise, store
+  // ---- epilogue: combine the two lane halves' partial sums, normalise, and
+  // store O through LDS so that every global store is a full 256-byte row.
   {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
                                                      __float_as_uint(l_run), false, false);
@@ -277,18 +375,29 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
   const bool row_valid = active && qrow < cq;
   const float inv = (row_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
-  uint2* orow = o + (qk_row0 + qrow) * (kHeadDim / 4);
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  uint2* const ostage = reinterpret_cast<uint2*>(smem + wave * 32 * kORow);  // 32 rows x 272 B
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       // registers 4jj..4jj+3 hold d = 32dt + 8jj + 4*half + 0..3
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       bf16x4 w;
 #pragma unroll
       for (int t = 0; t < 4; ++t) w[t] = __bf16(oacc[dt][4 * jj + t] * inv);
-      orow[(dt * 32 + 8 * jj + 4 * half) / 4] = __builtin_bit_cast(uint2, w);
+      ostage[l32 * (kORow * 2) + (dt * 32 + 8 * jj + 4 * half) / 4] = __builtin_bit_cast(uint2, w);
     }
+  // the staging area of wave w is only touched by wave w
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint4* const orows = smem + wave * 32 * kORow;
+  uint4* const odst = o + (qk_row0 + wave * 32) * 16;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int rr = p * 4 + lane / 16;
+    odst[rr * 16 + (lane & 15)] = orows[rr * kORow + (lane & 15)];
+  }
   if (lse != nullptr && half == 0) {
     lse[qk_row0 + qrow] =
         (row_valid && l_run > 0.f) ? m_run * scale + __logf(l_run) : -INFINITY;
@@ -305,7 +414,7 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
   hipLaunchKernelGGL(attn_fwd_kernel<NW>, dim3(unsigned(rows)), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(q), static_cast<const uint4*>(k),
                      static_cast<const uint4*>(vt), row_ptr, col, uniform_k, nnz,
-                     static_cast<uint2*>(o), lse, g, scale_log2, scale);
+                     static_cast<uint4*>(o), lse, g, scale_log2, scale);
   return hipGetLastError();
 }
 
