@@ -121,38 +121,24 @@ __device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* d
                                    (lds_ptr_t)(dst), 16, 0, 0);
 }
 
-// S^T (2 tiles of 32 keys x 32 queries) = K sub-tile (LDS) x Q^T (VGPRs).
-__device__ inline void qk_tile(const uint4* __restrict__ kl, const bf16x8 (&qf)[8],
-                               f32x16 (&st)[2]) {
+// Keep the scheduler from moving work across this point: the main loop is
+// laid out slot by slot (one MFMA, its operand prefetch and a share of the
+// softmax VALU work per slot) and each slot is fenced.
+__device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Materialise a VALU result where it is written in the source (an empty
+// volatile asm that reads and writes the register), so that pure arithmetic
+// is not sunk towards its first use and stays in its slot.
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// Row max over the 32 scores this lane holds.
+__device__ inline float tile_max(const f32x16 (&st)[2]) {
+  float mx = st[0][0];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) st[mt][j] = 0.f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const bf16x8 a = as_bf16x8(kl[mt * 32 * kKRow + 2 * s]);
-      st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], st[mt], 0, 0, 0);
-    }
-  }
-}
-
-// p = exp2(s*c - mb) for the 32 scores of this lane: fp32 partial sums for l,
-// bf16 values grouped as the B operands of the 4 PV steps (16 keys each).
-__device__ inline void exp_tile(const f32x16 (&st)[2], float c, float mb, bf16x8 (&pb)[4],
-                                float& rs0, float& rs1) {
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-    for (int t = 0; t < 8; t += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(st[cc / 2][8 * (cc % 2) + t], c, -mb));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(st[cc / 2][8 * (cc % 2) + t + 1], c, -mb));
-      rs0 += p0;
-      rs1 += p1;
-      pb[cc][t] = __bf16(p0);
-      pb[cc][t + 1] = __bf16(p1);
-    }
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[mt][j]);
+  return mx;
 }
 
 template <int NW>
@@ -161,14 +147,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
     int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, VsaGeom g, float scale_log2,
     float scale) {
-  static_assert(2 * (kKUnits + kVUnits) >= NW * 32 * kORow, "O staging must fit in LDS");
+  static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits), "O staging must fit in LDS");
   const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
-  // K runs one sub-tile ahead of V: while sub-tile n is finished, K buffer
-  // n^1 holds K_{n+1} (read) and buffer n receives K_{n+2}; V buffer n holds
-  // V_n (read) and buffer n^1 receives V_{n+1}.
-  __shared__ __align__(16) uint4 smem[2 * kKUnits + 2 * kVUnits];
-  uint4* const kbuf0 = smem;
-  uint4* const vbuf0 = smem + 2 * kKUnits;
+  // Sub-tile buffers.  K runs one sub-tile ahead of V: while sub-tile n is
+  // finished, K buffer (n+1)%2 holds K_{n+1} (read) and K buffer n%2 receives
+  // K_{n+2}; V buffer n%2 holds V_n (read) and V buffer (n+1)%2 receives
+  // V_{n+1}.  Four separate arrays let the compiler see that the in-flight
+  // copies never alias the buffers being read.
+  __shared__ __align__(16) uint4 kbuf0[kKUnits];
+  __shared__ __align__(16) uint4 kbuf1[kKUnits];
+  __shared__ __align__(16) uint4 vbuf0[kVUnits];
+  __shared__ __align__(16) uint4 vbuf1[kVUnits];
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   const int64_t r = xcd_remap(blockIdx.x, nrows);
@@ -214,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const uint4* const vbase = vt + bh * (g.npad / kKvChunk) * kUnits;
   const int chunks_per_block = g.vol / kKvChunk;
   // per-lane source offsets (16-byte units inside a sub-tile) of this wave's
-  // chunk loads; the same for every sub-tile
+  // chunk copies; the same for every sub-tile
   constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
   uint32_t koff[kMaxK], voff[kMaxV];
 #pragma unroll
@@ -229,19 +218,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const int row = pos / kVRow, unit = pos % kVRow;
     voff[u] = row * 8 + (unit < 8 ? unit : 0);
   }
-  auto load_k = [&](const TileCursor& c, int b) {
+  auto load_k = [&](const TileCursor& c, uint4* dst) {
     const uint4* src = kbase + (int64_t(c.j) * g.vol + c.sub * kKvChunk) * 16;
 #pragma unroll
     for (int u = 0; u < kMaxK; ++u)
-      if (wave + u * NW < kKChunks)
-        wave_copy_to_lds(src, koff[u], kbuf0 + b * kKUnits + (wave + u * NW) * 64);
+      if (wave + u * NW < kKChunks) wave_copy_to_lds(src, koff[u], dst + (wave + u * NW) * 64);
   };
-  auto load_v = [&](const TileCursor& c, int b) {
+  auto load_v = [&](const TileCursor& c, uint4* dst) {
     const uint4* src = vbase + (int64_t(c.j) * chunks_per_block + c.sub) * kUnits;
 #pragma unroll
     for (int u = 0; u < kMaxV; ++u)
-      if (wave + u * NW < kVChunks)
-        wave_copy_to_lds(src, voff[u], vbuf0 + b * kVUnits + (wave + u * NW) * 64);
+      if (wave + u * NW < kVChunks) wave_copy_to_lds(src, voff[u], dst + (wave + u * NW) * 64);
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -254,10 +241,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   c2 = c1;
   bool h2 = h1 && next_tile(c2, len, rcol, g);
   if (h0) {
-    load_k(c0, 0);
-    load_v(c0, 0);
+    load_k(c0, kbuf0);
+    load_v(c0, vbuf0);
   }
-  if (h1) load_k(c1, 1);
+  if (h1) load_k(c1, kbuf1);
   wait_loads();
   __syncthreads();
 
@@ -266,13 +253,30 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int vread = l32 * kVRow + half;
 
   f32x16 sa[2], sb[2];
-  if (h0 && active) qk_tile(kbuf0 + kread, qf, sa);
+  float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
+  if (h0 && active) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sa[mt][j] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s], sa[mt], 0, 0, 0);
+    mx_pre = tile_max(sa);
+  }
 
   // Finish sub-tile n (scores in `cur`) and compute the scores of n+1 into `nxt`.
-  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const int n) {
-    if (h2) load_k(c2, n);      // K_{n+2} replaces K_n
-    if (h1) load_v(c1, n ^ 1);  // V_{n+1} replaces V_{n-1}
+  // kn: K buffer holding K_{n+1}; kw: K buffer receiving K_{n+2};
+  // vn: V buffer holding V_n;     vw: V buffer receiving V_{n+1}.
+  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
+                  const uint4* vn, uint4* vw) {
+    if (h2) load_k(c2, kw);
+    if (h1) load_v(c1, vw);
     if (active) {
+      float mx = mx_pre;
       // mask keys past the block's valid count (only in its last sub-tile)
       const int valid = c0.cj - c0.sub * kKvChunk;
       if (valid < kKvChunk) {
@@ -283,13 +287,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
             const int key = mt * 32 + 16 * (j / 8) + 8 * half + (j % 8);
             if (key >= valid) cur[mt][j] = -INFINITY;
           }
+        mx = tile_max(cur);
       }
-      // row max over this lane's 32 keys and the partner lane's (l ^ 32)
-      float mx = cur[0][0];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, cur[mt][j]);
+      // row max including the partner lane's keys (l ^ 32)
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
@@ -310,43 +310,81 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
       }
       const float mb = m_run * scale_log2;
-      bf16x8 pb[4];
       float rs0 = 0.f, rs1 = 0.f;
-      if (h1) {
-        // next sub-tile's QK^T on the matrix cores, interleaved with this
-        // sub-tile's exponentials on the VALU
-        qk_tile(kbuf0 + (n ^ 1) * kKUnits + kread, qf, nxt);
-        exp_tile(cur, scale_log2, mb, pb, rs0, rs1);
-        // K operand reads run 4 ahead of the MFMAs that consume them; every
-        // MFMA is followed by 7 VALU instructions of the softmax
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 PV steps
+      float mxn = -INFINITY;
+
+      // ---- software-pipelined slots.  Slots 0..15: S_{n+1} = K_{n+1} Q^T
+      // (s = u/2, tile mt = u%2).  Slots 16..31: O^T += V^T_n P^T_n (step
+      // cc = (u-16)/4, d tile dt = (u-16)%4).  The 16 pairs of exponentials of sub-tile n are spread over the
+      // slots so that every P group is ready before its PV step, and the row
+      // max of S_{n+1} is taken in the last slots, after its MFMAs finished.
+      // LDS operands are read in groups of 4, one group ahead of the slots
+      // that consume them, so any wait for LDS data lands on reads issued
+      // four slots (about 130 cycles) earlier.
+      bf16x8 opk[8], opv[8];
+      auto read_k = [&](int u) {  // operand of QK slot u
+        opk[u % 8] = as_bf16x8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
+      };
+      auto read_v = [&](int w) {  // operand of PV slot w
+        opv[w % 8] = as_bf16x8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+      };
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (u < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      for (int u = 0; u < 4; ++u) read_k(u);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) nxt[mt][j] = 0.f;
+      slot_fence();
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (u < 16) {
+          const int s = u / 2, mt = u % 2;
+          if (u % 4 == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              if (u + 4 < 16) read_k(u + 4 + x);
+              else read_v(x);  // first V operands of the PV slots
+            }
+          }
+          nxt[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opk[u % 8], qf[s], nxt[mt], 0, 0, 0);
+        } else {
+          const int w = u - 16, cc = w / 4, dt = w % 4;
+          if (w % 4 == 0 && w + 4 < 16) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
+          }
+          const bf16x8 pb = __builtin_bit_cast(
+              bf16x8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opv[w % 8], pb, oacc[dt], 0, 0, 0);
         }
-      } else {
-        exp_tile(cur, scale_log2, mb, pb, rs0, rs1);
+        // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
+        // in even slots 0..22, pairs 12..15 in slots 24..27
+        const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+        if (e >= 0) {
+          const int cc = e / 4, t = 2 * (e % 4);
+          float p0 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -mb));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -mb));
+          rs0 += p0;
+          rs1 += p1;
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          const bf16x2 pr = {__bf16(p0), __bf16(p1)};
+          pw[cc][t / 2] = __builtin_bit_cast(uint32_t, pr);
+          pin(rs0);
+          pin(rs1);
+          pin(pw[cc][t / 2]);
+        }
+        // row max of S_{n+1}, 4 accumulator registers per slot in slots 24..31
+        if (u >= 24) {
+          const int mt = (u - 24) / 4, j0 = ((u - 24) % 4) * 4;
+          mxn = fmaxf(fmaxf(mxn, nxt[mt][j0]), nxt[mt][j0 + 1]);
+          mxn = fmaxf(fmaxf(mxn, nxt[mt][j0 + 2]), nxt[mt][j0 + 3]);
+          pin(mxn);
+        }
+        slot_fence();
       }
       l_run += rs0 + rs1;
-      // O^T += V^T P^T, 4 steps of 16 keys
-      const uint4* vl = vbuf0 + n * kVUnits + vread;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 a = as_bf16x8(vl[dt * 32 * kVRow + 2 * cc]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], oacc[dt], 0, 0, 0);
-        }
-      }
-      // V operand reads run 2 ahead of the MFMAs that consume them
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        if (u < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      }
+      mx_pre = mxn;
     }
     wait_loads();
     __syncthreads();
@@ -361,9 +399,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   };
 
   while (h0) {
-    step(sa, sb, 0);
+    step(sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
     if (!h0) break;
-    step(sb, sa, 1);
+    step(sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, and
@@ -376,7 +414,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const bool row_valid = active && qrow < cq;
   const float inv = (row_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  uint2* const ostage = reinterpret_cast<uint2*>(smem + wave * 32 * kORow);  // 32 rows x 272 B
+  // staging area of 32 rows x 272 B per wave: two waves per buffer
+  uint4* const sbase = wave < 2 ? kbuf0 : (wave < 4 ? kbuf1 : (wave < 6 ? vbuf0 : vbuf1));
+  uint4* const srows = sbase + (wave % 2) * 32 * kORow;
+  uint2* const ostage = reinterpret_cast<uint2*>(srows);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -391,12 +432,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const uint4* const orows = smem + wave * 32 * kORow;
   uint4* const odst = o + (qk_row0 + wave * 32) * 16;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int rr = p * 4 + lane / 16;
-    odst[rr * 16 + (lane & 15)] = orows[rr * kORow + (lane & 15)];
+    odst[rr * 16 + (lane & 15)] = srows[rr * kORow + (lane & 15)];
   }
   if (lse != nullptr && half == 0) {
     lse[qk_row0 + qrow] =
