@@ -23,6 +23,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -68,6 +69,28 @@ def step_flops(plan, col_host, row_ptr_host, uniform_k):
     return f_valid, f_nominal
 
 
+def attention_source_digest():
+    path = os.path.join(ROOT, "block_sparse_video_tile_amd", "csrc", "attention.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(path, workload):
+    """HBM bytes per attention launch from the committed PMC record, or None.
+
+    The record is only used when it was taken on this workload and on the
+    attention kernel source as it is now (same sha256); otherwise the counters
+    describe a different kernel and traffic is reported as null.
+    """
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != attention_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(wl, q, k, v, budget_s):
     """Time the CPU oracle on whole heads of the same layer until ~budget_s of work."""
     import oracle
@@ -106,7 +129,8 @@ def main():
     ap.add_argument("--workload", default="wan5b_k64", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "attention_traffic.json"))
+    ap.add_argument("--traffic-json",
+                    default=os.path.join(ROOT, "profiles", "attention_wan5b_k64_traffic.json"))
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -185,12 +209,7 @@ def main():
     t_attn = float(np.mean(stage_ms["attention"]))
     attn_tflops = f_valid / (t_attn * 1e-3) / 1e12
     value = f_valid / (ms_per_step * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        if tj.get("workload") == wl.name:
-            traffic = tj.get("bytes_per_launch")
+    traffic = recorded_traffic(args.traffic_json, wl.name)
     result = {
         "metric": "effective TFLOP/s (selected blocks) + ms/layer, 27280 tok, topk=64, 1 GPU",
         "value": round(value, 3),
