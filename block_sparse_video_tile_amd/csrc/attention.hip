@@ -15,11 +15,18 @@
 //   heads, and its L2 serves their shared key/value blocks.
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
-//   loaded).  K (64 x 128) and V^T (128 x 64) sub-tiles are copied HBM/L2 ->
-//   LDS directly (global_load_lds_dwordx4, no VGPR staging), double-buffered,
-//   one barrier per sub-tile.  K runs one sub-tile ahead of V so that the
-//   next sub-tile's QK^T can run on the matrix cores while this sub-tile's
-//   softmax runs on the VALU (software pipeline inside each wave).
+//   loaded).  The workgroup first flattens its CSR entries into a list of
+//   sub-tile descriptors in LDS, so the main loop carries no CSR walking, no
+//   divisions and no global index loads; the descriptor three sub-tiles ahead
+//   is read from LDS while the current one is being computed.
+//   K (64 x 128) and V^T (128 x 64) sub-tiles are copied HBM/L2 -> LDS
+//   directly (global_load_lds_dwordx4, no VGPR staging), double-buffered, one
+//   barrier per sub-tile.  The copies are issued from inside the MFMA slots
+//   (K in the QK^T half, V in the PV half) rather than as one burst, and
+//   unconditionally, so the slots stay a single basic block.  K runs one
+//   sub-tile ahead of V so that the next sub-tile's QK^T can run on the
+//   matrix cores while this sub-tile's softmax runs on the VALU (software
+//   pipeline inside each wave).
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16, D[m][n] += A[m][k] B[k][n];
 // lane l holds A row m = l%32, B column n = l%32, and accumulator register
@@ -81,36 +88,12 @@ constexpr int kKChunks = kKUnits / 64;  // 17 wave-loads of 1 KB
 constexpr int kVChunks = kVUnits / 64;  // 18
 constexpr int kORow = 17;               // epilogue O staging row: 272 B
 
-struct TileCursor {
-  int e;    // CSR entry, relative to the row start
-  int sub;  // 64-key sub-tile inside the block
-  int j;    // key block id
-  int cj;   // its valid-token count
-};
-
-// Move to the first sub-tile of the next valid CSR entry after `c.e`.
-__device__ inline bool next_entry(TileCursor& c, int len, const int32_t* __restrict__ col,
-                                  const VsaGeom& g) {
-  for (++c.e; c.e < len; ++c.e) {
-    const int j = col[c.e];
-    if (j >= 0 && j < g.nb) {
-      c.j = j;
-      c.sub = 0;
-      c.cj = block_count(g, j);
-      return true;
-    }
-  }
-  return false;
-}
-
-__device__ inline bool next_tile(TileCursor& c, int len, const int32_t* __restrict__ col,
-                                 const VsaGeom& g) {
-  if ((c.sub + 1) * kKvChunk < c.cj) {
-    ++c.sub;
-    return true;
-  }
-  return next_entry(c, len, col, g);
-}
+// A row's CSR entries are flattened, up to kListEntries at a time, into a list
+// of 64-key sub-tile descriptors in LDS:
+//   (64-token chunk index of the sub-tile within its head) << 7 | (valid keys - 1)
+// K rows of chunk c start at token row 64c of the head and V^T chunk c is the
+// c-th 64-token chunk, so the chunk index addresses both.
+constexpr int kListEntries = 1024;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -158,6 +141,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   __shared__ __align__(16) uint4 kbuf1[kKUnits];
   __shared__ __align__(16) uint4 vbuf0[kVUnits];
   __shared__ __align__(16) uint4 vbuf1[kVUnits];
+  // sub-tile descriptor list of the current pass over the row, and the
+  // per-entry scan that places each entry's descriptors
+  constexpr int kThreads = NW * 64;
+  constexpr int kListTiles = kListEntries * (32 * NW / kKvChunk);
+  __shared__ int tlist[kListTiles];
+  __shared__ int escan[kListEntries];
+  __shared__ int ntiles_sh;
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   const int64_t r = xcd_remap(blockIdx.x, nrows);
@@ -202,206 +192,268 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const uint4* const kbase = k + bh * g.npad * 16;
   const uint4* const vbase = vt + bh * (g.npad / kKvChunk) * kUnits;
   const int chunks_per_block = g.vol / kKvChunk;
-  // per-lane source offsets (16-byte units inside a sub-tile) of this wave's
-  // chunk copies; the same for every sub-tile
+  // Copy x of a sub-tile moves LDS chunk wave + x*NW (64 consecutive 16-byte
+  // units of the padded buffer); koff/voff are this lane's source offsets
+  // inside the sub-tile, the same for every sub-tile.  Chunk positions past
+  // the buffer belong to copies that the lane predicate switches off.
   constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
   uint32_t koff[kMaxK], voff[kMaxV];
 #pragma unroll
-  for (int u = 0; u < kMaxK; ++u) {
-    const int pos = (wave + u * NW) * 64 + lane;
+  for (int x = 0; x < kMaxK; ++x) {
+    const int pos = min((wave + x * NW) * 64 + lane, kKUnits - 1);
     const int row = pos / kKRow, unit = pos % kKRow;
-    koff[u] = kappa(row) * 16 + (unit < 16 ? unit : 0);
+    koff[x] = kappa(row) * 16 + (unit < 16 ? unit : 0);
   }
 #pragma unroll
-  for (int u = 0; u < kMaxV; ++u) {
-    const int pos = (wave + u * NW) * 64 + lane;
+  for (int x = 0; x < kMaxV; ++x) {
+    const int pos = min((wave + x * NW) * 64 + lane, kVUnits - 1);
     const int row = pos / kVRow, unit = pos % kVRow;
-    voff[u] = row * 8 + (unit < 8 ? unit : 0);
+    voff[x] = row * 8 + (unit < 8 ? unit : 0);
   }
-  auto load_k = [&](const TileCursor& c, uint4* dst) {
-    const uint4* src = kbase + (int64_t(c.j) * g.vol + c.sub * kKvChunk) * 16;
-#pragma unroll
-    for (int u = 0; u < kMaxK; ++u)
-      if (wave + u * NW < kKChunks) wave_copy_to_lds(src, koff[u], dst + (wave + u * NW) * 64);
+  auto src_of = [](const uint4* base, int desc) { return base + int64_t(desc >> 7) * kUnits; };
+  // The predicate is evaluated per lane (exec mask) rather than as a branch,
+  // so copies can sit inside the scheduled slots without splitting them.
+  auto copy_k = [&](const uint4* src, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, koff[x], dst + (wave + x * NW) * 64);
   };
-  auto load_v = [&](const TileCursor& c, uint4* dst) {
-    const uint4* src = vbase + (int64_t(c.j) * chunks_per_block + c.sub) * kUnits;
+  auto copy_v = [&](const uint4* src, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kVChunks) wave_copy_to_lds(src, voff[x], dst + (wave + x * NW) * 64);
+  };
+  auto load_k = [&](int desc, uint4* dst) {
 #pragma unroll
-    for (int u = 0; u < kMaxV; ++u)
-      if (wave + u * NW < kVChunks) wave_copy_to_lds(src, voff[u], dst + (wave + u * NW) * 64);
+    for (int x = 0; x < kMaxK; ++x) copy_k(src_of(kbase, desc), x, dst);
+  };
+  auto load_v = [&](int desc, uint4* dst) {
+#pragma unroll
+    for (int x = 0; x < kMaxV; ++x) copy_v(src_of(vbase, desc), x, dst);
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  // cursors of sub-tiles n, n+1, n+2
-  TileCursor c0, c1, c2;
-  c0.e = -1;
-  bool h0 = next_entry(c0, len, rcol, g);
-  c1 = c0;
-  bool h1 = h0 && next_tile(c1, len, rcol, g);
-  c2 = c1;
-  bool h2 = h1 && next_tile(c2, len, rcol, g);
-  if (h0) {
-    load_k(c0, kbuf0);
-    load_v(c0, vbuf0);
-  }
-  if (h1) load_k(c1, kbuf1);
-  wait_loads();
-  __syncthreads();
 
   // per-lane operand bases: K row l32 (+ half unit), V^T row l32 (+ half unit)
   const int kread = l32 * kKRow + half;
   const int vread = l32 * kVRow + half;
-
   f32x16 sa[2], sb[2];
   float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
-  if (h0 && active) {
+
+  for (int e0 = 0; e0 < len; e0 += kListEntries) {
+    const int m = min(kListEntries, len - e0);
+    // ---- flatten entries e0 .. e0+m-1 into the sub-tile list: per-entry
+    // sub-tile counts, an exclusive scan of them, then the descriptors
+    for (int e = tid; e < m; e += kThreads) {
+      const int j = rcol[e0 + e];
+      escan[e] = (j >= 0 && j < g.nb) ? (block_count(g, j) + kKvChunk - 1) / kKvChunk : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int kPerLane = kListEntries / 64;
+      int loc[kPerLane];
+      int sum = 0;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int x = 0; x < kPerLane; ++x) {
+        const int e = lane * kPerLane + x;
+        loc[x] = sum;
+        sum += e < m ? escan[e] : 0;
+      }
+      int incl = sum;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sa[mt][j] = 0.f;
+      for (int d = 1; d < 64; d *= 2) {
+        const int up = __shfl_up(incl, d);
+        if (lane >= d) incl += up;
+      }
+      const int base = incl - sum;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+      for (int x = 0; x < kPerLane; ++x) {
+        const int e = lane * kPerLane + x;
+        if (e < m) escan[e] = base + loc[x];
+      }
+      if (lane == 63) ntiles_sh = incl;
+    }
+    __syncthreads();
+    for (int e = tid; e < m; e += kThreads) {
+      const int j = rcol[e0 + e];
+      if (j >= 0 && j < g.nb) {
+        const int cj = block_count(g, j);
+        const int off = escan[e];
+        for (int sub = 0; sub * kKvChunk < cj; ++sub)
+          tlist[off + sub] =
+              ((j * chunks_per_block + sub) << 7) | (min(kKvChunk, cj - sub * kKvChunk) - 1);
+      }
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(ntiles_sh);  // uniform
+    if (T == 0) continue;
+    // descriptor of sub-tile n; past the end it repeats the last one, whose
+    // copies then land in a buffer that is not read again
+    auto desc_at = [&](int n) { return tlist[min(n, T - 1)]; };
+
+    int n = 0;
+    int d0 = __builtin_amdgcn_readfirstlane(desc_at(0));
+    int d1 = __builtin_amdgcn_readfirstlane(desc_at(1));
+    int d2 = __builtin_amdgcn_readfirstlane(desc_at(2));
+    load_k(d0, kbuf0);
+    load_v(d0, vbuf0);
+    load_k(d1, kbuf1);
+    wait_loads();
+    __syncthreads();
+    if (active) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
-        sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s], sa[mt], 0, 0, 0);
-    mx_pre = tile_max(sa);
-  }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sa[mt][j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s], sa[mt], 0, 0, 0);
+      mx_pre = tile_max(sa);
+    }
+    // the first step copies K_2 into kbuf0: every wave must be done with K_0
+    __syncthreads();
 
-  // Finish sub-tile n (scores in `cur`) and compute the scores of n+1 into `nxt`.
-  // kn: K buffer holding K_{n+1}; kw: K buffer receiving K_{n+2};
-  // vn: V buffer holding V_n;     vw: V buffer receiving V_{n+1}.
-  auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
-                  const uint4* vn, uint4* vw) {
-    if (h2) load_k(c2, kw);
-    if (h1) load_v(c1, vw);
-    if (active) {
-      float mx = mx_pre;
-      // mask keys past the block's valid count (only in its last sub-tile)
-      const int valid = c0.cj - c0.sub * kKvChunk;
-      if (valid < kKvChunk) {
+    // Finish sub-tile n (scores in `cur`) and compute the scores of n+1 into
+    // `nxt`.  kn: K buffer holding K_{n+1}; kw: K buffer receiving K_{n+2};
+    // vn: V buffer holding V_n; vw: V buffer receiving V_{n+1}.
+    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
+                    const uint4* vn, uint4* vw) {
+      const uint4* const sk = src_of(kbase, d2);
+      const uint4* const sv = src_of(vbase, d1);
+      const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
+      if (active) {
+        float mx = mx_pre;
+        // mask keys past the block's valid count (only in its last sub-tile)
+        const int valid = (d0 & 127) + 1;
+        if (valid < kKvChunk) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int key = mt * 32 + 16 * (j / 8) + 8 * half + (j % 8);
+              if (key >= valid) cur[mt][j] = -INFINITY;
+            }
+          mx = tile_max(cur);
+        }
+        // row max including the partner lane's keys (l ^ 32)
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        // Lazy rescale: the reference max m_run only moves (and O, l are only
+        // rescaled) when a score exceeds it by more than 8 in log2 units, so
+        // every p = exp2((s - m_run) * scale * log2 e) stays <= 2^8.  The final
+        // O / l is the same softmax whichever reference max was used.
+        if (__ballot(mx > m_run + rescale_thr) != 0) {  // wave-uniform branch
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+        }
+        const float mb = m_run * scale_log2;
+        float rs0 = 0.f, rs1 = 0.f;
+        uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 PV steps
+        float mxn = -INFINITY;
+
+        // ---- software-pipelined slots.  Slots 0..15: S_{n+1} = K_{n+1} Q^T
+        // (s = u/2, tile mt = u%2).  Slots 16..31: O^T += V^T_n P^T_n (step
+        // cc = (u-16)/4, d tile dt = (u-16)%4).  The 16 pairs of exponentials of sub-tile n are spread over the
+        // slots so that every P group is ready before its PV step, and the row
+        // max of S_{n+1} is taken in the last slots, after its MFMAs finished.
+        // LDS operands are read in groups of 4, one group ahead of the slots
+        // that consume them, so any wait for LDS data lands on reads issued
+        // four slots (about 130 cycles) earlier.
+        bf16x8 opk[8], opv[8];
+        auto read_k = [&](int u) {  // operand of QK slot u
+          opk[u % 8] = as_bf16x8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
+        };
+        auto read_v = [&](int w) {  // operand of PV slot w
+          opv[w % 8] = as_bf16x8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+        };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) read_k(u);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = mt * 32 + 16 * (j / 8) + 8 * half + (j % 8);
-            if (key >= valid) cur[mt][j] = -INFINITY;
-          }
-        mx = tile_max(cur);
-      }
-      // row max including the partner lane's keys (l ^ 32)
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                         false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      // Lazy rescale: the reference max m_run only moves (and O, l are only
-      // rescaled) when a score exceeds it by more than 8 in log2 units, so
-      // every p = exp2((s - m_run) * scale * log2 e) stays <= 2^8.  The final
-      // O / l is the same softmax whichever reference max was used.
-      if (__ballot(mx > m_run + rescale_thr) != 0) {  // wave-uniform branch
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
-      }
-      const float mb = m_run * scale_log2;
-      float rs0 = 0.f, rs1 = 0.f;
-      uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 PV steps
-      float mxn = -INFINITY;
-
-      // ---- software-pipelined slots.  Slots 0..15: S_{n+1} = K_{n+1} Q^T
-      // (s = u/2, tile mt = u%2).  Slots 16..31: O^T += V^T_n P^T_n (step
-      // cc = (u-16)/4, d tile dt = (u-16)%4).  The 16 pairs of exponentials of sub-tile n are spread over the
-      // slots so that every P group is ready before its PV step, and the row
-      // max of S_{n+1} is taken in the last slots, after its MFMAs finished.
-      // LDS operands are read in groups of 4, one group ahead of the slots
-      // that consume them, so any wait for LDS data lands on reads issued
-      // four slots (about 130 cycles) earlier.
-      bf16x8 opk[8], opv[8];
-      auto read_k = [&](int u) {  // operand of QK slot u
-        opk[u % 8] = as_bf16x8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
-      };
-      auto read_v = [&](int w) {  // operand of PV slot w
-        opv[w % 8] = as_bf16x8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
-      };
-#pragma unroll
-      for (int u = 0; u < 4; ++u) read_k(u);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) nxt[mt][j] = 0.f;
-      slot_fence();
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        if (u < 16) {
-          const int s = u / 2, mt = u % 2;
-          if (u % 4 == 0) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              if (u + 4 < 16) read_k(u + 4 + x);
-              else read_v(x);  // first V operands of the PV slots
-            }
-          }
-          nxt[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opk[u % 8], qf[s], nxt[mt], 0, 0, 0);
-        } else {
-          const int w = u - 16, cc = w / 4, dt = w % 4;
-          if (w % 4 == 0 && w + 4 < 16) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
-          }
-          const bf16x8 pb = __builtin_bit_cast(
-              bf16x8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opv[w % 8], pb, oacc[dt], 0, 0, 0);
-        }
-        // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
-        // in even slots 0..22, pairs 12..15 in slots 24..27
-        const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
-        if (e >= 0) {
-          const int cc = e / 4, t = 2 * (e % 4);
-          float p0 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -mb));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -mb));
-          rs0 += p0;
-          rs1 += p1;
-          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-          const bf16x2 pr = {__bf16(p0), __bf16(p1)};
-          pw[cc][t / 2] = __builtin_bit_cast(uint32_t, pr);
-          pin(rs0);
-          pin(rs1);
-          pin(pw[cc][t / 2]);
-        }
-        // row max of S_{n+1}, 4 accumulator registers per slot in slots 24..31
-        if (u >= 24) {
-          const int mt = (u - 24) / 4, j0 = ((u - 24) % 4) * 4;
-          mxn = fmaxf(fmaxf(mxn, nxt[mt][j0]), nxt[mt][j0 + 1]);
-          mxn = fmaxf(fmaxf(mxn, nxt[mt][j0 + 2]), nxt[mt][j0 + 3]);
-          pin(mxn);
-        }
+          for (int j = 0; j < 16; ++j) nxt[mt][j] = 0.f;
         slot_fence();
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          // this sub-tile's copies, K in the QK^T half and V in the PV half
+#pragma unroll
+          for (int x = 0; x < kMaxK; ++x)
+            if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
+#pragma unroll
+          for (int x = 0; x < kMaxV; ++x)
+            if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
+          if (u < 16) {
+            const int s = u / 2, mt = u % 2;
+            if (u % 4 == 0) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                if (u + 4 < 16) read_k(u + 4 + x);
+                else read_v(x);  // first V operands of the PV slots
+              }
+            }
+            nxt[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opk[u % 8], qf[s], nxt[mt], 0, 0, 0);
+          } else {
+            const int w = u - 16, cc = w / 4, dt = w % 4;
+            if (w % 4 == 0 && w + 4 < 16) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
+            }
+            const bf16x8 pb = __builtin_bit_cast(
+                bf16x8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opv[w % 8], pb, oacc[dt], 0, 0, 0);
+          }
+          // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
+          // in even slots 0..22, pairs 12..15 in slots 24..27
+          const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+          if (e >= 0) {
+            const int cc = e / 4, t = 2 * (e % 4);
+            float p0 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -mb));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -mb));
+            rs0 += p0;
+            rs1 += p1;
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 pr = {__bf16(p0), __bf16(p1)};
+            pw[cc][t / 2] = __builtin_bit_cast(uint32_t, pr);
+            pin(rs0);
+            pin(rs1);
+            pin(pw[cc][t / 2]);
+          }
+          // row max of S_{n+1}, 4 accumulator registers per slot in slots 24..31
+          if (u >= 24) {
+            const int mt = (u - 24) / 4, j0 = ((u - 24) % 4) * 4;
+            mxn = fmaxf(fmaxf(mxn, nxt[mt][j0]), nxt[mt][j0 + 1]);
+            mxn = fmaxf(fmaxf(mxn, nxt[mt][j0 + 2]), nxt[mt][j0 + 3]);
+            pin(mxn);
+          }
+          slot_fence();
+        }
+        l_run += rs0 + rs1;
+        mx_pre = mxn;
+      } else {
+        load_k(d2, kw);
+        load_v(d1, vw);
       }
-      l_run += rs0 + rs1;
-      mx_pre = mxn;
-    }
-    wait_loads();
-    __syncthreads();
-    TileCursor c3 = c2;
-    const bool h3 = h2 && next_tile(c3, len, rcol, g);
-    c0 = c1;
-    h0 = h1;
-    c1 = c2;
-    h1 = h2;
-    c2 = c3;
-    h2 = h3;
-  };
+      wait_loads();
+      __syncthreads();
+      ++n;
+      d0 = d1;
+      d1 = d2;
+      d2 = __builtin_amdgcn_readfirstlane(d3);
+    };
 
-  while (h0) {
-    step(sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
-    if (!h0) break;
-    step(sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+    while (true) {
+      step(sa, sb, kbuf1, kbuf0, vbuf0, vbuf1);
+      if (n >= T) break;
+      step(sb, sa, kbuf0, kbuf1, vbuf1, vbuf0);
+      if (n >= T) break;
+    }
   }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, and
