@@ -18,7 +18,20 @@ Default workload: the 27280-token (31, 22, 40) layer, block (4, 8, 8),
 the "FastVideo VSA" user guide ("Choose top-k").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--cpu-seconds S] [--only-attention]
+                       [--no-cpu-baseline] [--cpu-seconds S]
+
+Two helper modes serve the HBM traffic record of the attention kernel:
+  python bench.py --copy-calibration MIB
+      runs a plain device copy (dst = src * 1, fp32) of MIB MiB a few times, so
+      that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE can be read for a kernel
+      whose byte count is known;
+  python bench.py --record-traffic FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
+                  --cal-mib MIB [--workload NAME] [--traffic-json PATH]
+      turns the four counter_collection.csv files (attention runs, then the
+      calibration copy) into the JSON record that the default mode reads:
+      bytes per attention launch = FETCH_SIZE and WRITE_SIZE per dispatch,
+      each scaled by the ratio of the copy's known bytes to what the same
+      counter read for it, tagged with the sha256 of the kernel source.
 """
 from __future__ import annotations
 
@@ -91,6 +104,49 @@ def recorded_traffic(path, workload):
     return rec.get("bytes_per_launch")
 
 
+def copy_calibration(mib, reps=5):
+    """A plain device copy of a known size for counter calibration."""
+    n = mib * (1 << 20) // 4
+    src = torch.rand(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
+
+
+def _counter_means(path, name_filter):
+    """Mean Counter_Value per counter over the dispatches whose kernel name matches."""
+    import csv
+    import collections
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if name_filter in row["Kernel_Name"]:
+                acc[row["Counter_Name"]].append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def record_traffic(args):
+    fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.record_traffic
+    cal_bytes = args.cal_mib * (1 << 20)
+    out = {}
+    for label, att_csv, cal_csv, counter in (("fetch", fetch_csv, cal_fetch_csv, "FETCH_SIZE"),
+                                              ("write", write_csv, cal_write_csv, "WRITE_SIZE")):
+        att, n_att = _counter_means(att_csv, "attn_fwd_kernel")[counter]
+        cal, n_cal = _counter_means(cal_csv, "vectorized_elementwise_kernel")[counter]
+        factor = cal_bytes / (cal * 1024.0)   # counter reads KiB
+        out[label] = {"counter": counter, "kib_per_dispatch": att, "dispatches": n_att,
+                      "calibration_kib": cal, "calibration_dispatches": n_cal,
+                      "calibration_factor": factor, "bytes_per_launch": att * 1024.0 * factor}
+    rec = {"workload": args.workload, "kernel_source_sha256": attention_source_digest(),
+           "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
+           "fetch": out["fetch"], "write": out["write"], "calibration_copy_bytes": cal_bytes}
+    with open(args.traffic_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(wl, q, k, v, budget_s):
     """Time the CPU oracle on whole heads of the same layer until ~budget_s of work."""
     import oracle
@@ -131,8 +187,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic-json",
                     default=os.path.join(ROOT, "profiles", "attention_wan5b_k64_traffic.json"))
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB")
+    ap.add_argument("--record-traffic", nargs=4, metavar="CSV")
+    ap.add_argument("--cal-mib", type=int, default=1024)
     args = ap.parse_args()
 
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; "
                           f"--gpus {args.gpus} is not supported (no multi-GPU path)"}))
@@ -140,6 +202,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
