@@ -10,7 +10,7 @@ stream; HIP events on that stream bracket each stage of every timed step.
 Metric: effective TFLOP/s counting the selected blocks' valid tokens only
 (4 * D * sum over query blocks i of c_i * sum_{j in row i} c_j, from the map
 the step produced), divided by the whole step time; ms/layer is reported
-alongside.  The attention kernel's own rate against the bf16 MFMA peak is the
+alongside.  The attention kernel's own rate against the dense MFMA peak is the
 roofline object.
 
 Default workload: the 27280-token (31, 22, 40) layer, block (4, 8, 8),
@@ -52,7 +52,7 @@ if ROOT not in sys.path:
 import block_sparse_video_tile_amd as vsa  # noqa: E402
 from vsa_inputs import WORKLOADS, make_qkv, make_tile64_map  # noqa: E402
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_16BIT_PEAK_TFLOPS = 2500.0   # MI355X dense MFMA, bf16 and fp16 alike
 HBM_PEAK_GBS = 8000.0
 
 STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "scatter"]
@@ -88,7 +88,7 @@ def attention_source_digest():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(path, workload):
+def recorded_traffic(path, workload, dtype):
     """HBM bytes per attention launch from the committed PMC record, or None.
 
     The record is only used when it was taken on this workload and on the
@@ -99,7 +99,8 @@ def recorded_traffic(path, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != attention_source_digest():
+    if (rec.get("workload") != workload or rec.get("dtype", "bf16") != dtype
+            or rec.get("kernel_source_sha256") != attention_source_digest()):
         return None
     return rec.get("bytes_per_launch")
 
@@ -139,7 +140,8 @@ def record_traffic(args):
         out[label] = {"counter": counter, "kib_per_dispatch": att, "dispatches": n_att,
                       "calibration_kib": cal, "calibration_dispatches": n_cal,
                       "calibration_factor": factor, "bytes_per_launch": att * 1024.0 * factor}
-    rec = {"workload": args.workload, "kernel_source_sha256": attention_source_digest(),
+    rec = {"workload": args.workload, "dtype": args.dtype,
+           "kernel_source_sha256": attention_source_digest(),
            "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
            "fetch": out["fetch"], "write": out["write"], "calibration_copy_bytes": cal_bytes}
     with open(args.traffic_json, "w") as f:
@@ -183,6 +185,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan5b_k64", choices=sorted(WORKLOADS))
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
+                    help="element type of Q, K, V and O (the headline is bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic-json",
@@ -209,18 +213,20 @@ def main():
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     log(f"[bench] workload {wl.name}: generating inputs")
-    q, k, v = make_qkv(wl)
+    elem = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+    q, k, v = make_qkv(wl, dtype=elem)
     dq, dk, dv = (t.to(dev) for t in (q, k, v))
     plan = vsa.vsa_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, batch=wl.batch,
-                        num_heads=wl.heads, head_dim=wl.head_dim, topk=wl.topk or 0)
+                        num_heads=wl.heads, head_dim=wl.head_dim, topk=wl.topk or 0,
+                        dtype=vsa.VSA_DTYPE_FP16 if args.dtype == "fp16" else vsa.VSA_DTYPE_BF16)
     log(f"[bench] {vsa.vsa_plan_describe(plan)}")
-    qb = torch.empty(plan.blocked_shape(), dtype=torch.bfloat16, device=dev)
+    qb = torch.empty(plan.blocked_shape(), dtype=elem, device=dev)
     kb = torch.empty_like(qb)
     ob = torch.empty_like(qb)
-    vb = torch.empty(plan.blocked_vt_shape(), dtype=torch.bfloat16, device=dev)
+    vb = torch.empty(plan.blocked_vt_shape(), dtype=elem, device=dev)
     qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=dev)
     kp = torch.empty_like(qp)
-    out = torch.empty(plan.raster_shape(), dtype=torch.bfloat16, device=dev)
+    out = torch.empty(plan.raster_shape(), dtype=elem, device=dev)
     if wl.topk:
         col = torch.empty(plan.num_rows() * wl.topk, dtype=torch.int32, device=dev)
         rp_dev, rp_host, uk = None, None, wl.topk
@@ -274,7 +280,7 @@ def main():
     t_attn = float(np.mean(stage_ms["attention"]))
     attn_tflops = f_valid / (t_attn * 1e-3) / 1e12
     value = f_valid / (ms_per_step * 1e-3) / 1e12
-    traffic = recorded_traffic(args.traffic_json, wl.name)
+    traffic = recorded_traffic(args.traffic_json, wl.name, args.dtype)
     result = {
         "metric": "effective TFLOP/s (selected blocks) + ms/layer, 27280 tok, topk=64, 1 GPU",
         "value": round(value, 3),
@@ -286,16 +292,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic: seeded N(0,1) tokens plus a per-block N(0,0.25) mean vector, bf16",
+        "dtype": args.dtype,
+        "data": "synthetic: seeded N(0,1) tokens plus a per-block N(0,0.25) mean vector, "
+                + args.dtype,
         "config": {"workload": wl.name, "dit_seq_shape": list(wl.dit_seq_shape),
                    "block_size": list(wl.block_size), "seq_len": wl.seq_len,
                    "heads": wl.heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "topk": wl.topk, "num_blocks": plan.num_blocks,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / MFMA_16BIT_PEAK_TFLOPS, 4),
                      "traffic": traffic},
         "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in stage_ms.items()},
         "flops_valid": f_valid,

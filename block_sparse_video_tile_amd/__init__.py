@@ -161,6 +161,15 @@ class Plan:
         return self.info["num_blocks"]
 
     @property
+    def dtype(self):
+        return self.desc.dtype
+
+    def torch_dtype(self):
+        """torch element type of the Q, K, V and O tensors of this plan."""
+        import torch
+        return torch.float16 if self.desc.dtype == VSA_DTYPE_FP16 else torch.bfloat16
+
+    @property
     def padded_len(self):
         return self.info["padded_len"]
 
@@ -249,11 +258,6 @@ def _stream(stream, *tensors):
     return None
 
 
-def _bf16():
-    import torch
-    return torch.bfloat16
-
-
 def _f32():
     import torch
     return torch.float32
@@ -266,18 +270,20 @@ def _i32():
 
 def vsa_gather(plan: Plan, role: int, x_raster, x_blk, pooled=None, stream=None):
     n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
+    et = plan.torch_dtype()
     _check(load_library().vsa_gather(
-        plan.handle, int(role), _ptr(x_raster, n_raster, _bf16(), "x_raster"),
-        _ptr(x_blk, plan.info["blocked_elems"], _bf16(), "x_blk"),
+        plan.handle, int(role), _ptr(x_raster, n_raster, et, "x_raster"),
+        _ptr(x_blk, plan.info["blocked_elems"], et, "x_blk"),
         _ptr(pooled, plan.info["pooled_elems"], _f32(), "pooled"),
         _stream(stream, x_raster, x_blk)))
 
 
 def vsa_scatter(plan: Plan, o_blk, o_raster, stream=None):
     n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
+    et = plan.torch_dtype()
     _check(load_library().vsa_scatter(
-        plan.handle, _ptr(o_blk, plan.info["blocked_elems"], _bf16(), "o_blk"),
-        _ptr(o_raster, n_raster, _bf16(), "o_raster"), _stream(stream, o_blk, o_raster)))
+        plan.handle, _ptr(o_blk, plan.info["blocked_elems"], et, "o_blk"),
+        _ptr(o_raster, n_raster, et, "o_raster"), _stream(stream, o_blk, o_raster)))
 
 
 def vsa_score_topk(plan: Plan, q_pooled, k_pooled, topk: int, col_idx, scores=None, stream=None):
@@ -294,11 +300,12 @@ def vsa_block_sparse_attn_fwd(plan: Plan, q_blk, k_blk, v_blk, row_ptr, col_idx,
                               nnz: int, o_blk, lse=None, stream=None):
     be = plan.info["blocked_elems"]
     rows = plan.num_rows()
+    et = plan.torch_dtype()
     _check(load_library().vsa_block_sparse_attn_fwd(
-        plan.handle, _ptr(q_blk, be, _bf16(), "q_blk"), _ptr(k_blk, be, _bf16(), "k_blk"),
-        _ptr(v_blk, be, _bf16(), "v_blk"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
+        plan.handle, _ptr(q_blk, be, et, "q_blk"), _ptr(k_blk, be, et, "k_blk"),
+        _ptr(v_blk, be, et, "v_blk"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
         _ptr(col_idx, int(nnz), _i32(), "col_idx"), int(uniform_k), int(nnz),
-        _ptr(o_blk, be, _bf16(), "o_blk"),
+        _ptr(o_blk, be, et, "o_blk"),
         _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
         _stream(stream, q_blk, o_blk)))
 
@@ -319,9 +326,10 @@ def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
         ws_ptr, ws_len = _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
     else:
         ws_ptr, ws_len = int(workspace), ws_bytes
+    et = plan.torch_dtype()
     _check(load_library().vsa_forward(
-        plan.handle, _ptr(q, n_raster, _bf16(), "q"), _ptr(k, n_raster, _bf16(), "k"),
-        _ptr(v, n_raster, _bf16(), "v"), _ptr(out, n_raster, _bf16(), "out"), ws_ptr, ws_len,
+        plan.handle, _ptr(q, n_raster, et, "q"), _ptr(k, n_raster, et, "k"),
+        _ptr(v, n_raster, et, "v"), _ptr(out, n_raster, et, "out"), ws_ptr, ws_len,
         _ptr(col_idx_out, plan.num_rows() * max(plan.topk, 0), _i32(), "col_idx_out"),
         _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
         _stream(stream, q, out)))

@@ -28,7 +28,8 @@
 //   matrix cores while this sub-tile's softmax runs on the VALU (software
 //   pipeline inside each wave).
 //
-// MFMA formulation (v_mfma_f32_32x32x16_bf16, D[m][n] += A[m][k] B[k][n];
+// MFMA formulation (v_mfma_f32_32x32x16_bf16, or _f16 for fp16 tensors;
+// D[m][n] += A[m][k] B[k][n];
 // lane l holds A row m = l%32, B column n = l%32, and accumulator register
 // j holds row m = 8*(j/4) + 4*(l/32) + j%4 of column n = l%32):
 //   S^T = K Q^T :  A = K sub-tile rows (keys) from LDS, B = Q^T fragments
@@ -36,7 +37,7 @@
 //                  scores of ONE query (column n), so the softmax max and sum
 //                  are in-lane plus one exchange between lanes l and l^32.
 //   O^T += V^T P^T: A = V^T rows (d) from LDS, B = P^T taken straight from the
-//                  S^T accumulators after exp2 and bf16 rounding.
+//                  S^T accumulators after exp2 and rounding to the element type.
 //   For the second product the 8 keys a lane feeds at k-slot (l/32, t) must be
 //   the 8 keys its S^T accumulator holds.  Staging K row `key` into LDS row
 //   kappa(key) (kappa swaps bits 2 and 3 of the row index) makes accumulator
@@ -46,22 +47,51 @@
 //
 // Online softmax (exact up to rounding): running reference max m and sum l per
 // query in fp32, p = exp2(s*log2(e)/sqrt(D) - m*log2(e)/sqrt(D)) on the
-// transcendental unit, l summed from the fp32 p, P rounded to bf16 for the PV
-// product, O rescaled by exp2 of the max change only when the max grows by
-// more than 2^8 (so p <= 256).  Padded keys of a partial sub-tile are masked
+// transcendental unit, l summed from the fp32 p, P rounded to bf16 (fp16 for
+// fp16 tensors) for the PV product, O rescaled by exp2 of the max change only
+// when the max grows by more than 2^8 (so p <= 256).  Padded keys of a partial sub-tile are masked
 // to -inf.  A row without blocks leaves l = 0 and writes O = 0, LSE = -inf.
+
+#include <type_traits>
 
 #include "vsa_internal.h"
 
 namespace vsa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Eight 16-bit elements (one MFMA operand per lane), held as bf16 bit
+// patterns and reinterpreted when the tensors are fp16.
+typedef __bf16 ev8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kUnits = 1024;  // 16-byte units in one 64 x 128 bf16 sub-tile (16 KB)
+constexpr int kUnits = 1024;  // 16-byte units in one 64 x 128 sub-tile of 16-bit elements (16 KB)
 
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ inline ev8 as_ev8(uint4 v) { return __builtin_bit_cast(ev8, v); }
+
+// D = A B + C on 32x32x16 tiles of bf16 (F16 = false) or fp16 operands.
+template <bool F16>
+__device__ inline f32x16 mfma_32x32x16(ev8 a, ev8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 values rounded to nearest-even in the element type, low half first.
+template <bool F16>
+__device__ inline uint32_t pack2(float a, float b) {
+  if constexpr (F16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 r = {_Float16(a), _Float16(b)};
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 r = {__bf16(a), __bf16(b)};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+}
 
 // Dispatch is round-robin over the 8 XCDs; give each XCD a contiguous run of rows.
 __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
@@ -124,7 +154,7 @@ __device__ inline float tile_max(const f32x16 (&st)[2]) {
   return mx;
 }
 
-template <int NW>
+template <int NW, bool F16>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ vt,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
@@ -174,11 +204,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int len = int(end - beg);
 
   const int64_t qk_row0 = bh * g.npad + int64_t(i) * g.vol;  // first token row of block i
-  bf16x8 qf[8];
+  ev8 qf[8];
   if (active) {
     const uint4* qsrc = q + (qk_row0 + qrow) * 16;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(qsrc[2 * s + half]);
+    for (int s = 0; s < 8; ++s) qf[s] = as_ev8(qsrc[2 * s + half]);
   }
 
   f32x16 oacc[4];
@@ -304,8 +334,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-          sa[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s], sa[mt], 0, 0, 0);
+          sa[mt] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s],
+                                      sa[mt]);
       mx_pre = tile_max(sa);
     }
     // the first step copies K_2 into kbuf0: every wave must be done with K_0
@@ -366,12 +396,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         // LDS operands are read in groups of 4, one group ahead of the slots
         // that consume them, so any wait for LDS data lands on reads issued
         // four slots (about 130 cycles) earlier.
-        bf16x8 opk[8], opv[8];
+        ev8 opk[8], opv[8];
         auto read_k = [&](int u) {  // operand of QK slot u
-          opk[u % 8] = as_bf16x8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
+          opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
         };
         auto read_v = [&](int w) {  // operand of PV slot w
-          opv[w % 8] = as_bf16x8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+          opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
         };
 #pragma unroll
         for (int u = 0; u < 4; ++u) read_k(u);
@@ -398,16 +428,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
                 else read_v(x);  // first V operands of the PV slots
               }
             }
-            nxt[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opk[u % 8], qf[s], nxt[mt], 0, 0, 0);
+            nxt[mt] = mfma_32x32x16<F16>(opk[u % 8], qf[s], nxt[mt]);
           } else {
             const int w = u - 16, cc = w / 4, dt = w % 4;
             if (w % 4 == 0 && w + 4 < 16) {
 #pragma unroll
               for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
             }
-            const bf16x8 pb = __builtin_bit_cast(
-                bf16x8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opv[w % 8], pb, oacc[dt], 0, 0, 0);
+            const ev8 pb = __builtin_bit_cast(
+                ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+            oacc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, oacc[dt]);
           }
           // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
           // in even slots 0..22, pairs 12..15 in slots 24..27
@@ -418,9 +448,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
             float p1 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -mb));
             rs0 += p0;
             rs1 += p1;
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const bf16x2 pr = {__bf16(p0), __bf16(p1)};
-            pw[cc][t / 2] = __builtin_bit_cast(uint32_t, pr);
+            pw[cc][t / 2] = pack2<F16>(p0, p1);
             pin(rs0);
             pin(rs1);
             pin(pw[cc][t / 2]);
@@ -465,7 +493,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
   const bool row_valid = active && qrow < cq;
   const float inv = (row_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   // staging area of 32 rows x 272 B per wave: two waves per buffer
   uint4* const sbase = wave < 2 ? kbuf0 : (wave < 4 ? kbuf1 : (wave < 6 ? vbuf0 : vbuf1));
   uint4* const srows = sbase + (wave % 2) * 32 * kORow;
@@ -475,10 +502,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       // registers 4jj..4jj+3 hold d = 32dt + 8jj + 4*half + 0..3
-      bf16x4 w;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) w[t] = __bf16(oacc[dt][4 * jj + t] * inv);
-      ostage[l32 * (kORow * 2) + (dt * 32 + 8 * jj + 4 * half) / 4] = __builtin_bit_cast(uint2, w);
+      const uint2 w = make_uint2(
+          pack2<F16>(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv),
+          pack2<F16>(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv));
+      ostage[l32 * (kORow * 2) + (dt * 32 + 8 * jj + 4 * half) / 4] = w;
     }
   // the staging area of wave w is only touched by wave w
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -496,14 +523,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
 }
 
-template <int NW>
+template <int NW, bool F16>
 hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* vt,
                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
                      void* o, float* lse, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attn_fwd_kernel<NW>, dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(q), static_cast<const uint4*>(k),
                      static_cast<const uint4*>(vt), row_ptr, col, uniform_k, nnz,
                      static_cast<uint4*>(o), lse, g, scale_log2, scale);
@@ -515,11 +542,17 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, hipStream_t s) {
+  auto launch = [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    return g.dtype == VSA_DTYPE_FP16
+               ? launch_nw<NW, true>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s)
+               : launch_nw<NW, false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
+  };
   switch (g.vol / 32) {
-    case 2: return launch_nw<2>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
-    case 4: return launch_nw<4>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
-    case 6: return launch_nw<6>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
-    case 8: return launch_nw<8>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
+    case 2: return launch(std::integral_constant<int, 2>());
+    case 4: return launch(std::integral_constant<int, 4>());
+    case 6: return launch(std::integral_constant<int, 6>());
+    case 8: return launch(std::integral_constant<int, 8>());
     default: return hipErrorInvalidValue;
   }
 }

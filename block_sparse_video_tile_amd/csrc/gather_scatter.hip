@@ -6,8 +6,9 @@
 // to the block volume with zero rows that the attention kernel masks.
 //
 // All three kernels are HBM-bound streams: one workgroup per (batch, head,
-// block), 16-byte loads and stores, one token row of one head (D = 128 bf16)
-// is 16 lanes x 16 bytes.
+// block), 16-byte loads and stores, one token row of one head (D = 128
+// 16-bit elements, bf16 or fp16: the guide's "Verify routing and fallback"
+// admits both) is 16 lanes x 16 bytes.
 
 #include "vsa_internal.h"
 
@@ -47,10 +48,22 @@ __device__ inline int64_t token_of(const VsaGeom& g, const BlockBox& b, int r) {
   return (int64_t(b.t0 + dt) * g.H + (b.h0 + dh)) * g.W + (b.w0 + dw);
 }
 
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// The two 16-bit elements of a 32-bit word as fp32 (low half first): bf16 is
+// the upper half of an fp32, fp16 converts exactly.
+template <bool F16>
+__device__ inline float elem_lo(uint32_t w) {
+  if constexpr (F16) return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xffffu)));
+  else return __uint_as_float(w << 16);
+}
+template <bool F16>
+__device__ inline float elem_hi(uint32_t w) {
+  if constexpr (F16) return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
+  else return __uint_as_float(w & 0xffff0000u);
+}
 
 // Q/K: raster [B,S,NH,D] -> blocked [B,NH,Npad,D], optional fp32 block means.
+// The copy moves raw 16-bit elements; only the means depend on the type.
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __restrict__ x,
                                                              uint4* __restrict__ xb,
                                                              float* __restrict__ pooled,
@@ -71,10 +84,10 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
     if (r < box.cnt) {
       const int64_t s = token_of(g, box, r);
       val = x[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit];
-      acc[0] += bf16_lo(val.x); acc[1] += bf16_hi(val.x);
-      acc[2] += bf16_lo(val.y); acc[3] += bf16_hi(val.y);
-      acc[4] += bf16_lo(val.z); acc[5] += bf16_hi(val.z);
-      acc[6] += bf16_lo(val.w); acc[7] += bf16_hi(val.w);
+      acc[0] += elem_lo<F16>(val.x); acc[1] += elem_hi<F16>(val.x);
+      acc[2] += elem_lo<F16>(val.y); acc[3] += elem_hi<F16>(val.y);
+      acc[4] += elem_lo<F16>(val.z); acc[5] += elem_hi<F16>(val.z);
+      acc[6] += elem_lo<F16>(val.w); acc[7] += elem_hi<F16>(val.w);
     }
     dst[int64_t(r) * kUnitsPerRow + unit] = val;
   }
@@ -167,8 +180,12 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restri
 hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* pooled,
                             hipStream_t s) {
   const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
-  hipLaunchKernelGGL(gather_qk_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
-                     static_cast<const uint4*>(x), static_cast<uint4*>(xb), pooled, g);
+  if (g.dtype == VSA_DTYPE_FP16)
+    hipLaunchKernelGGL(gather_qk_kernel<true>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(xb), pooled, g);
+  else
+    hipLaunchKernelGGL(gather_qk_kernel<false>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(xb), pooled, g);
   return hipGetLastError();
 }
 

@@ -101,8 +101,8 @@ vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
     return fail(VSA_ERR_INVALID_ARGUMENT,
                 "vsa_plan: topk %d outside [1, num_blocks=%lld] (0 selects map mode)", d->topk,
                 (long long)nb);
-  if (d->dtype != VSA_DTYPE_BF16)
-    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: dtype %d not implemented (bf16 only)", d->dtype);
+  if (d->dtype != VSA_DTYPE_BF16 && d->dtype != VSA_DTYPE_FP16)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: dtype %d not implemented (bf16 or fp16)", d->dtype);
   if (d->head_dim != vsa::kHeadDim)
     return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: head_dim %d not implemented (128 only)",
                 d->head_dim);
@@ -128,6 +128,7 @@ vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
   g.head_dim = d->head_dim;
   g.S = d->seq_len;
   g.npad = npad;
+  g.dtype = d->dtype;
   p->topk = d->topk;
   p->dtype = d->dtype;
   *out = p;

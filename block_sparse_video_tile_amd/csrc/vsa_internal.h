@@ -19,6 +19,7 @@ struct VsaGeom {
   int32_t head_dim;
   int64_t S;              // tokens
   int64_t npad;           // nb * vol
+  int32_t dtype;          // vsa_dtype of Q, K, V and O
 };
 
 struct vsa_plan_s {

@@ -24,8 +24,10 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device work is enqueued asynchronously on it; no call synchronises the
  *     host.  Device faults surface at the caller's next synchronisation.
- *   - Element types: bf16 tensors are 2-byte IEEE bfloat16, fp32 are IEEE
- *     binary32, indices are int32.
+ *   - Element types: the Q, K, V and O tensors ("elem" below) are all of the
+ *     plan's dtype, 2-byte bfloat16 or IEEE binary16 ("Verify routing and
+ *     fallback" admits FP16 or BF16); fp32 is IEEE binary32, indices are
+ *     int32.  Pooled means, scores and LSE are fp32 for either dtype.
  *   - Host-side argument checks happen before any HIP call, so every
  *     VSA_ERR_INVALID_ARGUMENT / VSA_ERR_UNSUPPORTED path works without a GPU.
  *
@@ -76,7 +78,7 @@ typedef struct vsa_plan_desc {
   int32_t head_dim;         /* D; 128 is implemented */
   int32_t topk;             /* key blocks kept per query block, 1..nb; 0 = the
                                caller supplies a block map (CSR) instead */
-  int32_t dtype;            /* vsa_dtype; VSA_DTYPE_BF16 is implemented */
+  int32_t dtype;            /* vsa_dtype of Q, K, V and O: BF16 or FP16 */
 } vsa_plan_desc;
 
 /* Derived sizes of a plan (host values). */
@@ -98,8 +100,8 @@ typedef struct vsa_plan_s* vsa_plan_t;
  * Errors: INVALID_ARGUMENT for null pointers, non-positive sizes,
  *   seq_len != T*H*W, topk < 0 or topk > nb ("Choose top-k": larger than
  *   num_blocks is invalid; "Enable the backend": it must be positive, with 0
- *   reserved here for map mode); UNSUPPORTED for head_dim != 128, dtype other
- *   than bf16, or V not in {64, 128, 192, 256}.
+ *   reserved here for map mode); UNSUPPORTED for head_dim != 128, a dtype
+ *   other than BF16 or FP16, or V not in {64, 128, 192, 256}.
  * Ownership: *out is owned by the caller and released with vsa_plan_destroy;
  * a plan may be shared across threads and streams. */
 vsa_status vsa_plan(const vsa_plan_desc* desc, vsa_plan_t* out);
@@ -130,13 +132,13 @@ vsa_status vsa_plan_block_counts(vsa_plan_t plan, int32_t* counts, int64_t n);
  * vector the block score is built from: the guide's intro has every key block
  * scored per query block, and the h3 FastH3 log entry pools per tile).
  * role V: writes x_blk in the blocked-V^T layout; `pooled` must be NULL.
- * x_raster: device, B*S*NH*D bf16.  x_blk: device, B*NH*Npad*D bf16.
+ * x_raster: device, B*S*NH*D elem.  x_blk: device, B*NH*Npad*D elem.
  * pooled: device, B*NH*nb*D fp32, or NULL. */
 vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void* x_blk,
                       float* pooled, void* stream);
 
 /* Blocked -> raster scatter of an output tensor (pad rows are dropped).
- * o_blk: device, blocked layout, bf16.  o_raster: device, raster layout, bf16. */
+ * o_blk: device, blocked layout, elem.  o_raster: device, raster layout, elem. */
 vsa_status vsa_scatter(vsa_plan_t plan, const void* o_blk, void* o_raster, void* stream);
 
 /* Block score and per-row top-k ("FastVideo VSA" guide, intro: every key
@@ -160,7 +162,9 @@ vsa_status vsa_score_topk(vsa_plan_t plan, const float* q_pooled, const float* k
  *   listed in row r,
  * padded keys masked; an empty row yields O = 0 and LSE = -inf; pad query
  * rows are written as 0 (LSE -inf).
- * q_blk, k_blk: device bf16 blocked layout.  v_blk: device bf16 blocked-V^T.
+ * q_blk, k_blk: device elem blocked layout.  v_blk: device elem blocked-V^T.
+ * Products and softmax run in fp32; P is rounded to elem for the PV product
+ * and O is rounded to elem.
  * row_ptr: device int32 [B*NH*nb + 1] CSR offsets into col_idx, or NULL for
  *   uniform rows of `uniform_k` entries each (row r uses entries
  *   r*uniform_k .. r*uniform_k + uniform_k - 1).
@@ -169,7 +173,7 @@ vsa_status vsa_score_topk(vsa_plan_t plan, const float* q_pooled, const float* k
  *   [0, nb) are skipped, so a malformed map cannot read out of bounds.  Ids in
  *   a row must be unique (a repeated id weighs that block twice); ascending
  *   order is recommended for cache reuse, the result does not depend on it.
- * o_blk: device bf16 blocked layout.  lse: device fp32 [B,NH,Npad] or NULL.
+ * o_blk: device elem blocked layout.  lse: device fp32 [B,NH,Npad] or NULL.
  * Errors: INVALID_ARGUMENT for null pointers, nnz < 0, uniform_k outside
  *   [0, nb] in uniform mode. */
 vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t plan, const void* q_blk, const void* k_blk,
@@ -183,7 +187,7 @@ vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path for a plan with topk >= 1, raster in and raster out:
  * gather Q, K (with pooling) and V; score and top-k; block-sparse attention;
- * scatter O.  q, k, v: device bf16 raster.  out: device bf16 raster.
+ * scatter O.  q, k, v: device elem raster.  out: device elem raster.
  * workspace: device buffer of at least vsa_forward_workspace_size bytes,
  * 256-byte aligned, not shared with a concurrently running call.
  * col_idx_out: optional device int32 copy target for the selected ids

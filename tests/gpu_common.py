@@ -1,0 +1,157 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest).
+
+Tolerances for floating-point outputs are the ones the problem statement
+fixes for 16-bit inputs with fp32 accumulation: attention output max-abs 2e-2
+and mean-abs 2e-3 against the fp64 oracle; LSE within 1e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_video_tile_amd as vsa
+import oracle
+from vsa_inputs import WORKLOADS, bf16_to_f64, make_qkv
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+MARGIN = 1e-3
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _say(f"[gpu] {request.node.name}")
+
+
+def _plan(wl, topk=None, dtype=vsa.VSA_DTYPE_BF16):
+    k = wl.topk if topk is None else topk
+    return vsa.vsa_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, batch=wl.batch,
+                        num_heads=wl.heads, head_dim=wl.head_dim, topk=k or 0, dtype=dtype)
+
+
+def _gather_all(plan, q, k, v):
+    """Device blocked Q/K/V^T and pooled Q/K through the C ABI."""
+    dq, dk, dv = (t.to(DEV) for t in (q, k, v))
+    qb = torch.empty(plan.blocked_shape(), dtype=plan.torch_dtype(), device=DEV)
+    kb = torch.empty_like(qb)
+    vb = torch.empty(plan.blocked_vt_shape(), dtype=plan.torch_dtype(), device=DEV)
+    qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=DEV)
+    kp = torch.empty_like(qp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, dq, qb, qp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dk, kb, kp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vb)
+    return qb, kb, vb, qp, kp
+
+
+def _attend(plan, qb, kb, vb, row_ptr, col_idx, uniform_k=0, with_lse=True):
+    ob = torch.empty(plan.blocked_shape(), dtype=plan.torch_dtype(), device=DEV)
+    lse = (torch.empty((plan.batch, plan.heads, plan.padded_len), dtype=torch.float32,
+                       device=DEV) if with_lse else None)
+    rp = None if row_ptr is None else torch.as_tensor(row_ptr, dtype=torch.int32).to(DEV)
+    ci = torch.as_tensor(col_idx, dtype=torch.int32).to(DEV).contiguous()
+    vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vb, rp, ci, uniform_k, ci.numel(), ob, lse)
+    return ob, lse
+
+
+def _compare_rows(oplan, ob_host, lse_host, ref_out, ref_lse, rows, heads, vol):
+    """Compare blocked GPU rows with oracle raster rows; return (max_abs, mean_abs, lse_max)."""
+    lists = oracle.block_token_lists(oplan)
+    nb = oplan.num_blocks
+    errs, n, lerr = [], 0, 0.0
+    for r in rows:
+        b, rem = divmod(int(r), heads * nb)
+        h, i = divmod(rem, nb)
+        toks = lists[i]
+        c = len(toks)
+        got = ob_host[b, h, i * vol:i * vol + c].astype(np.float64)
+        want = ref_out[b, toks, h]
+        errs.append(np.abs(got - want))
+        # pad query rows are written as zero
+        assert np.all(ob_host[b, h, i * vol + c:(i + 1) * vol] == 0)
+        if lse_host is not None:
+            gl = lse_host[b, h, i * vol:i * vol + c].astype(np.float64)
+            wl = ref_lse[b, toks, h]
+            assert np.array_equal(np.isinf(gl), np.isinf(wl))
+            fin = np.isfinite(wl)
+            if fin.any():
+                lerr = max(lerr, float(np.max(np.abs(gl[fin] - wl[fin]))))
+            assert np.all(np.isneginf(lse_host[b, h, i * vol + c:(i + 1) * vol]))
+    e = np.concatenate([x.reshape(-1) for x in errs])
+    return float(e.max()), float(e.mean()), lerr
+
+
+def _host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float16) else t.cpu().numpy()
+
+
+def _sample_rows(oplan, heads, batch, per_head=4, seed=0):
+    """Deterministic row sample: every distinct block count, first/last heads, random extras."""
+    nb = oplan.num_blocks
+    counts = oplan.block_counts()
+    rng = np.random.default_rng(seed)
+    picks = set()
+    firsts = {int(c): int(np.nonzero(counts == c)[0][0]) for c in np.unique(counts)}
+    for hh in (0, heads - 1):
+        for i in firsts.values():
+            picks.add(hh * nb + i)
+    for _ in range(per_head * 2):
+        picks.add(int(rng.integers(0, batch * heads)) * nb + int(rng.integers(0, nb)))
+    return sorted(picks)
+
+
+def _full_forward(name, k=None, dtype=vsa.VSA_DTYPE_BF16):
+    wl = WORKLOADS[name]
+    k = wl.topk if k is None else k
+    plan = _plan(wl, k, dtype)
+    q, kk, v = make_qkv(wl, dtype=plan.torch_dtype())
+    ws = torch.empty(vsa.vsa_forward_workspace_size(plan), dtype=torch.uint8, device=DEV)
+    out = torch.empty(plan.raster_shape(), dtype=plan.torch_dtype(), device=DEV)
+    col = torch.empty(plan.num_rows() * k, dtype=torch.int32, device=DEV)
+    lse = torch.empty((plan.batch, plan.heads, plan.padded_len), dtype=torch.float32, device=DEV)
+    vsa.vsa_forward(plan, q.to(DEV), kk.to(DEV), v.to(DEV), out, ws, col, lse)
+    torch.cuda.synchronize()
+    return wl, k, q, kk, v, plan, out.cpu(), col.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_full_forward_sampled(name, k=None, dtype=vsa.VSA_DTYPE_BF16):
+    """Whole path at full size: map rows exact outside near-ties, sampled rows
+    of O and LSE against the oracle run on the GPU's own map."""
+    wl, k, q, kk, v, plan, out, col, lse = _full_forward(name, k, dtype)
+    oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, k)
+    q64, k64, v64 = bf16_to_f64(q), bf16_to_f64(kk), bf16_to_f64(v)
+    ref_sc = oracle.block_scores(oracle.pool_blocks(q64, oplan), oracle.pool_blocks(k64, oplan))
+    sel, margin = oracle.select_topk(ref_sc, k)
+    gsel = col.reshape(sel.shape)
+    exact = margin >= MARGIN
+    assert np.array_equal(gsel[exact], sel[exact])
+    _say(f"    map rows exact {int(exact.sum())} / {exact.size}")
+    # near-tie rows: k distinct ascending ids, each scoring within 1e-3 of the k-th best
+    for idx in np.argwhere(~exact):
+        row_sc = ref_sc[tuple(idx)]
+        g = gsel[tuple(idx)]
+        assert len(set(g.tolist())) == k and np.all(np.diff(g) > 0)
+        assert np.all(row_sc[g] >= np.sort(row_sc)[::-1][k - 1] - MARGIN)
+    assert (~exact).sum() <= 0.10 * exact.size
+    # attention rows sampled, computed by the oracle on the GPU's own map
+    rows = [r for r in _sample_rows(oplan, wl.heads, wl.batch) if exact.reshape(-1)[r]]
+    rp, ci = oracle.selection_to_csr(gsel)
+    ref_o, ref_l = oracle.block_sparse_attention(q64, k64, v64, oplan, rp, ci, query_rows=rows)
+    lists = oracle.block_token_lists(oplan)
+    errs = []
+    nb = oplan.num_blocks
+    for r in rows:
+        b, rem = divmod(r, wl.heads * nb)
+        h, i = divmod(rem, nb)
+        toks = lists[i]
+        errs.append(np.abs(out[b, toks, h].double().numpy() - ref_o[b, toks, h]).reshape(-1))
+        gl = lse[b, h, i * oplan.block_volume: i * oplan.block_volume + len(toks)]
+        assert np.max(np.abs(gl - ref_l[b, toks, h])) <= 1e-3
+    e = np.concatenate(errs)
+    _say(f"    {len(rows)} rows: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS

@@ -82,7 +82,7 @@ def test_plan_geometry_agrees_with_oracle(shape, block):
     (dict(dit_seq_shape=(0, 22, 40), seq_len=0), vsa.VSA_ERR_INVALID_ARGUMENT),
     (dict(block_size=(4, 8, 0)), vsa.VSA_ERR_INVALID_ARGUMENT),
     (dict(head_dim=64), vsa.VSA_ERR_UNSUPPORTED),
-    (dict(dtype=vsa.VSA_DTYPE_FP16), vsa.VSA_ERR_UNSUPPORTED),
+    (dict(dtype=2), vsa.VSA_ERR_UNSUPPORTED),                        # neither bf16 nor fp16
     (dict(block_size=(2, 4, 4)), vsa.VSA_ERR_UNSUPPORTED),           # V = 32
     (dict(block_size=(4, 8, 16)), vsa.VSA_ERR_UNSUPPORTED),          # V = 512
 ])
@@ -145,3 +145,14 @@ def test_binding_rejects_host_tensors(plan):
     x = torch.zeros(plan.raster_shape(), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, x, x)
+
+
+def test_fp16_plan_is_accepted_and_sets_the_binding_dtype():
+    import torch
+    p16 = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), num_heads=24, topk=64,
+                       dtype=vsa.VSA_DTYPE_FP16)
+    assert p16.dtype == vsa.VSA_DTYPE_FP16 and p16.torch_dtype() == torch.float16
+    p16b = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), num_heads=24, topk=64)
+    assert p16b.torch_dtype() == torch.bfloat16
+    # geometry does not depend on the element type
+    assert p16.info == p16b.info
