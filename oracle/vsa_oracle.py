@@ -23,8 +23,11 @@ path computes, written from the pages:
   block map compacted into per-row index lists with NON-uniform per-row counts
   and zero-count rows; text-prefix query tiles dense, video tiles prefix +
   top-k.
-* same log, FastH3 example entry: the gate branch pools per tile (the block
-  score uses per-block pooled queries and keys).
+* same log, FastH3 example entry: the gate-compress branch pools per tile
+  (the block score uses per-block pooled queries and keys).
+* same guide, "Checkpoint behavior": checkpoints with learned
+  to_gate_compress weights use that projection to compensate the sparse
+  branch; without them VSA runs the sparse branch alone.
 
 Readings where the pages are silent (each also listed with the design notes):
   R1 tokens are in raster order s = (t*H + h)*W + w;
@@ -38,7 +41,16 @@ Readings where the pages are silent (each also listed with the design notes):
   R6 a selected row is reported sorted ascending by block index;
   R7 no block is forced into its own row (pure top-k);
   R8 an empty row gives O = 0 and LSE = -inf;
-  R9 padded tokens of edge blocks take no part in any softmax (masked).
+  R9 padded tokens of edge blocks take no part in any softmax (masked);
+  R10 the gate-compress (coarse) branch is attention among the per-tile pooled
+     tokens: block i's pooled query attends over every block's pooled key
+     with the standard head_size**-0.5 scale (its logits are the R4 block
+     scores, scaled) and returns the softmax-weighted mean of the pooled
+     values -- the pages give no formula, this is the plainest reading;
+  R11 the gated output is the sparse output plus the gate times the coarse
+     output of the token's block, elementwise; the gate is a tensor shaped
+     like Q (the projection's output, supplied by the caller); no gate means
+     the sparse output alone.
 
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
@@ -52,6 +64,7 @@ __all__ = [
     "Plan", "make_plan", "routing_line", "token_block_ids", "block_token_lists",
     "pool_blocks", "block_scores", "select_topk", "selection_to_csr",
     "map_to_csr", "block_sparse_attention", "vsa_reference", "valid_flops",
+    "compress_attention", "gated_combine", "vsa_gated_reference",
 ]
 
 
@@ -282,6 +295,49 @@ def vsa_reference(q, k, v, dit_seq_shape, block_size, topk):
     o, lse = block_sparse_attention(q, k, v, plan, row_ptr, col_idx)
     return dict(plan=plan, qbar=qbar, kbar=kbar, scores=sc, sel=sel, margin=margin,
                 row_ptr=row_ptr, col_idx=col_idx, out=o, lse=lse)
+
+
+def compress_attention(qbar, kbar, vbar, head_dim):
+    """Gate-compress (coarse) branch: attention among the per-tile pooled tokens (R10).
+
+    h3-perf-stack log, FastH3 example entry: the gate-compress branch pools
+    per tile.  For every (batch, head), block i's pooled query attends over
+    the pooled keys of all blocks with the standard head_size**-0.5 scale
+    ("Verify routing and fallback") and takes the softmax-weighted mean of
+    the pooled values.  qbar, kbar, vbar: [B, heads, nb, D] ->
+    [B, heads, nb, D] float64.
+    """
+    logits = block_scores(qbar, kbar) / math.sqrt(head_dim)
+    mx = logits.max(axis=-1, keepdims=True)
+    p = np.exp(logits - mx)
+    return np.matmul(p, np.asarray(vbar, np.float64)) / p.sum(axis=-1, keepdims=True)
+
+
+def gated_combine(o_sparse, o_coarse, gate, plan: Plan):
+    """Sparse output plus the gated coarse output of each token's block (R11).
+
+    "FastVideo VSA" guide, "Checkpoint behavior": a learned to_gate_compress
+    projection compensates the sparse branch; without it the sparse branch is
+    used alone (gate None).  out[b, s, h] = o_sparse[b, s, h] +
+    gate[b, s, h] * o_coarse[b, h, block(s)], all [.., D] elementwise.
+    o_sparse, gate: [B, S, heads, D]; o_coarse: [B, heads, nb, D].
+    """
+    o_sparse = np.asarray(o_sparse, np.float64)
+    if gate is None:
+        return o_sparse
+    beta = token_block_ids(plan)
+    per_token = np.asarray(o_coarse, np.float64)[:, :, beta, :]      # [B, heads, S, D]
+    return o_sparse + np.asarray(gate, np.float64) * np.swapaxes(per_token, 1, 2)
+
+
+def vsa_gated_reference(q, k, v, gate, dit_seq_shape, block_size, topk):
+    """Whole path with the gate-compress branch: vsa_reference, pooled values,
+    the coarse attention and the gated combination (R10, R11)."""
+    ref = vsa_reference(q, k, v, dit_seq_shape, block_size, topk)
+    vbar = pool_blocks(v, ref["plan"])
+    oc = compress_attention(ref["qbar"], ref["kbar"], vbar, np.asarray(q).shape[-1])
+    ref.update(vbar=vbar, o_coarse=oc, gated_out=gated_combine(ref["out"], oc, gate, ref["plan"]))
+    return ref
 
 
 def valid_flops(plan: Plan, row_ptr, col_idx, head_dim) -> int:

@@ -128,3 +128,41 @@ def test_floor_block_grid_is_caught(monkeypatch):
     _patch(monkeypatch, "make_plan", lambda *a, **kw: FloorPlan(*a, **kw))
     _fails(pins.test_routing_line_matches_page_worked_example, pins.os.path.join(
         pins.os.path.dirname(pins.__file__), "golden"))
+
+
+def test_coarse_without_scale_is_caught(monkeypatch):
+    def bad(qb, kb, vb, d):
+        lg = ov.block_scores(qb, kb)
+        p = np.exp(lg - lg.max(axis=-1, keepdims=True))
+        return np.matmul(p, vb) / p.sum(axis=-1, keepdims=True)
+    _patch(monkeypatch, "compress_attention", bad)
+    _fails(pins.test_compress_closed_form_two_blocks)
+
+
+def test_coarse_transposed_logits_are_caught(monkeypatch):
+    def bad(qb, kb, vb, d):
+        lg = np.swapaxes(ov.block_scores(qb, kb), -1, -2) / math.sqrt(d)
+        p = np.exp(lg - lg.max(axis=-1, keepdims=True))
+        return np.matmul(p, vb) / p.sum(axis=-1, keepdims=True)
+    _patch(monkeypatch, "compress_attention", bad)
+    _fails(pins.test_compress_one_token_blocks_equal_library_dense_attention)
+
+
+def test_coarse_softmax_over_queries_is_caught(monkeypatch):
+    def bad(qb, kb, vb, d):
+        lg = ov.block_scores(qb, kb) / math.sqrt(d)
+        p = np.exp(lg - lg.max(axis=-2, keepdims=True))
+        return np.matmul(p / p.sum(axis=-2, keepdims=True), vb)
+    _patch(monkeypatch, "compress_attention", bad)
+    _fails(pins.test_compress_one_token_blocks_equal_library_dense_attention)
+
+
+def test_gate_broadcast_by_token_index_is_caught(monkeypatch):
+    def bad(o_sparse, o_coarse, gate, plan):
+        o_sparse = np.asarray(o_sparse, np.float64)
+        if gate is None:
+            return o_sparse
+        beta = np.arange(o_sparse.shape[1]) % plan.num_blocks
+        return o_sparse + gate * np.swapaxes(np.asarray(o_coarse)[:, :, beta, :], 1, 2)
+    _patch(monkeypatch, "gated_combine", bad)
+    _fails(pins.test_gated_combine_special_cases)

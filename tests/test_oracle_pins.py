@@ -403,3 +403,85 @@ def test_valid_flops_hand_count():
     ci = np.array([0, 7, 5, 1])
     want = 4 * 128 * (counts[0] * (256 + 30) + counts[2] * 48 + counts[7] * 64)
     assert oracle.valid_flops(plan, rp, ci, 128) == want
+
+
+# ------------------------------------------------- f1: gate-compress (coarse) branch
+
+def test_compress_one_token_blocks_equal_library_dense_attention():
+    # With 1-token tiles the per-tile pooling is the identity, so the coarse
+    # branch is plain attention over the tokens: torch's fp64 SDPA.
+    shape, heads, d = (2, 3, 4), 2, 16
+    s = int(np.prod(shape))
+    plan = oracle.make_plan(s, shape, (1, 1, 1))
+    rng = np.random.default_rng(21)
+    q, k, v = (rng.standard_normal((1, s, heads, d)) for _ in range(3))
+    qb, kb, vb = (oracle.pool_blocks(x, plan) for x in (q, k, v))
+    assert np.array_equal(qb, np.swapaxes(q, 1, 2))
+    oc = oracle.compress_attention(qb, kb, vb, d)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    dense = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    np.testing.assert_allclose(oc, dense.numpy(), rtol=0, atol=1e-12)
+
+
+def test_compress_closed_form_two_blocks():
+    # D = 4: logits (2*1/2, 0) = (1, 0), weights e/(e+1) and 1/(e+1)
+    qb = np.array([[[[2.0, 0, 0, 0]]]])
+    kb = np.array([[[[1.0, 0, 0, 0], [0.0, 0, 0, 0]]]])
+    vb = np.array([[[[1.0, 2, 0, 0], [0.0, 0, 4, 0]]]])
+    e = math.e
+    want = np.array([e / (e + 1), 2 * e / (e + 1), 4 / (e + 1), 0.0])
+    np.testing.assert_allclose(oracle.compress_attention(qb, kb, vb, 4)[0, 0, 0], want,
+                               rtol=0, atol=1e-15)
+
+
+def test_compress_single_block_and_zero_queries():
+    rng = np.random.default_rng(22)
+    vb = rng.standard_normal((1, 2, 1, 8))
+    # one block: the softmax over one key is 1
+    out = oracle.compress_attention(rng.standard_normal((1, 2, 1, 8)),
+                                    rng.standard_normal((1, 2, 1, 8)), vb, 8)
+    np.testing.assert_allclose(out, vb, rtol=0, atol=1e-15)
+    # zero queries: every logit is 0, the output is the plain mean of the values
+    vb = rng.standard_normal((1, 2, 5, 8))
+    out = oracle.compress_attention(np.zeros((1, 2, 5, 8)), rng.standard_normal((1, 2, 5, 8)),
+                                    vb, 8)
+    np.testing.assert_allclose(out, np.broadcast_to(vb.mean(axis=2, keepdims=True), out.shape),
+                               rtol=0, atol=1e-14)
+
+
+def test_gated_combine_special_cases():
+    wl = WORKLOADS["padded_tiny"]
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
+    rng = np.random.default_rng(23)
+    o_sparse = rng.standard_normal((1, wl.seq_len, 2, 4))
+    o_coarse = rng.standard_normal((1, 2, plan.num_blocks, 4))
+    assert np.array_equal(oracle.gated_combine(o_sparse, o_coarse, None, plan), o_sparse)
+    assert np.array_equal(oracle.gated_combine(o_sparse, o_coarse, np.zeros_like(o_sparse), plan),
+                          o_sparse)
+    # sparse 0 and gate 1: every token carries its block's coarse output;
+    # token (t, h, w) = (5, 12, 9) is s = (5*13 + 12)*10 + 9 = 779, block
+    # (5//4, 12//8, 9//8) = (1, 1, 1) -> id (1*2 + 1)*2 + 1 = 7
+    out = oracle.gated_combine(np.zeros_like(o_sparse), o_coarse, np.ones_like(o_sparse), plan)
+    assert np.array_equal(out[0, 779], o_coarse[0, :, 7])
+    assert np.array_equal(out[0, 0], o_coarse[0, :, 0])
+    for b_id, toks in enumerate(oracle.block_token_lists(plan)):
+        for s in toks[:3]:
+            assert np.array_equal(out[0, s], o_coarse[0, :, b_id])
+
+
+def test_gated_reference_whole_path_by_loops():
+    wl = WORKLOADS["tiny"]
+    q, kk, v = (bf16_to_f64(t) for t in make_qkv(wl))
+    gate = np.random.default_rng(24).standard_normal(q.shape)
+    ref = oracle.vsa_gated_reference(q, kk, v, gate, wl.dit_seq_shape, wl.block_size, wl.topk)
+    plan, d = ref["plan"], wl.head_dim
+    lists = oracle.block_token_lists(plan)
+    for h in range(wl.heads):
+        for i, toks in enumerate(lists):
+            qb = q[0, toks, h].mean(axis=0)
+            logits = np.array([qb @ kk[0, lists[j], h].mean(axis=0) for j in range(len(lists))])
+            w = np.exp(logits / math.sqrt(d) - (logits / math.sqrt(d)).max())
+            oc = sum(w[j] * v[0, lists[j], h].mean(axis=0) for j in range(len(lists))) / w.sum()
+            for s in toks:
+                want = ref["out"][0, s, h] + gate[0, s, h] * oc
+                np.testing.assert_allclose(ref["gated_out"][0, s, h], want, rtol=0, atol=1e-12)
