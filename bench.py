@@ -56,6 +56,8 @@ MFMA_16BIT_PEAK_TFLOPS = 2500.0   # MI355X dense MFMA, bf16 and fp16 alike
 HBM_PEAK_GBS = 8000.0
 
 STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "scatter"]
+GATED_STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "coarse",
+                "scatter"]
 
 
 def log(msg):
@@ -187,6 +189,9 @@ def main():
     ap.add_argument("--workload", default="wan5b_k64", choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="element type of Q, K, V and O (the headline is bf16)")
+    ap.add_argument("--gated", action="store_true",
+                    help="also run the gate-compress branch (pooled V, coarse attention, "
+                         "gated scatter) with a synthetic gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--traffic-json",
@@ -227,6 +232,12 @@ def main():
     qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=dev)
     kp = torch.empty_like(qp)
     out = torch.empty(plan.raster_shape(), dtype=elem, device=dev)
+    stages = GATED_STAGES if args.gated else STAGES
+    if args.gated:
+        vp = torch.empty_like(qp)
+        oc = torch.empty_like(qp)
+        gen = torch.Generator("cpu").manual_seed(77)
+        gate = (torch.randn(plan.raster_shape(), generator=gen) * 0.5).to(elem).to(dev)
     if wl.topk:
         col = torch.empty(plan.num_rows() * wl.topk, dtype=torch.int32, device=dev)
         rp_dev, rp_host, uk = None, None, wl.topk
@@ -247,21 +258,27 @@ def main():
         mark(1)
         vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dk, kb, kp)
         mark(2)
-        vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vb)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vb, vp if args.gated else None)
         mark(3)
         if wl.topk:
             vsa.vsa_score_topk(plan, qp, kp, wl.topk, col)
         mark(4)
         vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vb, rp_dev, col, uk, nnz, ob)
         mark(5)
-        vsa.vsa_scatter(plan, ob, out)
-        mark(6)
+        if args.gated:
+            vsa.vsa_compress_attn(plan, qp, kp, vp, oc)
+            mark(6)
+            vsa.vsa_scatter_gated(plan, ob, oc, gate, out)
+        else:
+            vsa.vsa_scatter(plan, ob, out)
+        mark(len(stages))
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -269,11 +286,11 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {name: [] for name in STAGES}
+    stage_ms = {name: [] for name in stages}
     for ev in events:
-        for n, name in enumerate(STAGES):
+        for n, name in enumerate(stages):
             stage_ms[name].append(ev[n].elapsed_time(ev[n + 1]))
-    gpu_ms = events[0][0].elapsed_time(events[-1][6]) / args.steps
+    gpu_ms = events[0][0].elapsed_time(events[-1][len(stages)]) / args.steps
     ms_per_step = max(wall * 1e3 / args.steps, gpu_ms)
     col_host = col.cpu().numpy().astype(np.int64)
     f_valid, f_nominal = step_flops(plan, col_host, None if rp_host is None else rp_host.astype(np.int64), uk)
@@ -299,7 +316,7 @@ def main():
                    "block_size": list(wl.block_size), "seq_len": wl.seq_len,
                    "heads": wl.heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "topk": wl.topk, "num_blocks": plan.num_blocks,
-                   "parallelism": "single GPU"},
+                   "gate_compress": bool(args.gated), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_16BIT_PEAK_TFLOPS, 4),

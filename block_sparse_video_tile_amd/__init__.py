@@ -21,8 +21,8 @@ __all__ = [
     "VSA_DTYPE_BF16", "VSA_DTYPE_FP16", "VSA_ROLE_Q", "VSA_ROLE_K", "VSA_ROLE_V",
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_plan_describe",
     "vsa_plan_block_counts", "vsa_gather", "vsa_scatter", "vsa_score_topk",
-    "vsa_block_sparse_attn_fwd", "vsa_forward_workspace_size", "vsa_forward",
-    "vsa_status_string", "vsa_last_error",
+    "vsa_block_sparse_attn_fwd", "vsa_compress_attn", "vsa_scatter_gated",
+    "vsa_forward_workspace_size", "vsa_forward", "vsa_status_string", "vsa_last_error",
 ]
 
 VSA_OK, VSA_ERR_INVALID_ARGUMENT, VSA_ERR_UNSUPPORTED, VSA_ERR_HIP = 0, 1, 2, 3
@@ -70,7 +70,9 @@ _SIGS = {
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P,
                                    _P, _P], ctypes.c_int),
     "vsa_forward_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
-    "vsa_forward": ([_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
+    "vsa_compress_attn": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "vsa_scatter_gated": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "vsa_forward": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
     "vsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "vsa_last_error": ([], ctypes.c_char_p),
 }
@@ -316,7 +318,26 @@ def vsa_forward_workspace_size(plan: Plan) -> int:
     return n.value
 
 
-def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None, stream=None):
+def vsa_compress_attn(plan: Plan, q_pooled, k_pooled, v_pooled, o_coarse, stream=None):
+    pe = plan.info["pooled_elems"]
+    _check(load_library().vsa_compress_attn(
+        plan.handle, _ptr(q_pooled, pe, _f32(), "q_pooled"), _ptr(k_pooled, pe, _f32(), "k_pooled"),
+        _ptr(v_pooled, pe, _f32(), "v_pooled"), _ptr(o_coarse, pe, _f32(), "o_coarse"),
+        _stream(stream, q_pooled, o_coarse)))
+
+
+def vsa_scatter_gated(plan: Plan, o_blk, o_coarse, gate, o_raster, stream=None):
+    n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
+    et = plan.torch_dtype()
+    _check(load_library().vsa_scatter_gated(
+        plan.handle, _ptr(o_blk, plan.info["blocked_elems"], et, "o_blk"),
+        _ptr(o_coarse, plan.info["pooled_elems"], _f32(), "o_coarse"),
+        _ptr(gate, n_raster, et, "gate"), _ptr(o_raster, n_raster, et, "o_raster"),
+        _stream(stream, o_blk, o_raster)))
+
+
+def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None, stream=None,
+                gate=None):
     import torch
     n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
     ws_bytes = vsa_forward_workspace_size(plan)
@@ -329,7 +350,8 @@ def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
     et = plan.torch_dtype()
     _check(load_library().vsa_forward(
         plan.handle, _ptr(q, n_raster, et, "q"), _ptr(k, n_raster, et, "k"),
-        _ptr(v, n_raster, et, "v"), _ptr(out, n_raster, et, "out"), ws_ptr, ws_len,
+        _ptr(v, n_raster, et, "v"), _ptr(gate, n_raster, et, "gate"),
+        _ptr(out, n_raster, et, "out"), ws_ptr, ws_len,
         _ptr(col_idx_out, plan.num_rows() * max(plan.topk, 0), _i32(), "col_idx_out"),
         _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
         _stream(stream, q, out)))

@@ -104,12 +104,28 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
   }
 }
 
+// One 16-bit element (in the low half of `u`) as fp32.
+template <bool F16>
+__device__ inline float elem_f32(uint32_t u) {
+  if constexpr (F16) return float(__builtin_bit_cast(_Float16, uint16_t(u)));
+  else return __uint_as_float(u << 16);
+}
+
 // V: raster [B,S,NH,D] -> blocked-V^T [B,NH,Npad/64,D,64] (each 64-token
-// chunk stored d-major), transposed through LDS.
+// chunk stored d-major), transposed through LDS; optionally the fp32 mean of
+// each block's valid tokens (the gate-compress branch pools values per tile
+// as well).  Pad tokens are zero, so summing all 64 rows of a chunk and
+// dividing by the valid count gives the mean.
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restrict__ x,
-                                                            uint4* __restrict__ xbt, VsaGeom g) {
+                                                            uint4* __restrict__ xbt,
+                                                            float* __restrict__ pooled,
+                                                            VsaGeom g) {
+  static_assert(kThreads == 2 * kHeadDim, "two threads per d column");
   // [token][d]; the 16-byte row pad keeps the 16-byte row stores aligned.
   __shared__ __align__(16) uint16_t tile[kKvChunk][kHeadDim + 8];
+  __shared__ float red[2][kHeadDim];
+  float acc = 0.f;  // this thread's share of column d = threadIdx.x % D
   const int wg = blockIdx.x;
   const int beta = wg % g.nb;
   const int bh = wg / g.nb;
@@ -149,15 +165,50 @@ __global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restr
         const uint32_t lo = tile[ku * 8 + 2 * e][d];
         const uint32_t hi = tile[ku * 8 + 2 * e + 1][d];
         w[e] = lo | (hi << 16);
+        if (pooled != nullptr) acc += elem_f32<F16>(lo) + elem_f32<F16>(hi);
       }
       dst[int64_t(d) * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __syncthreads();
   }
+  if (pooled != nullptr) {
+    // column d was summed by threads d and d + D
+    red[threadIdx.x / kHeadDim][threadIdx.x % kHeadDim] = acc;
+    __syncthreads();
+    if (threadIdx.x < kHeadDim)
+      pooled[(int64_t(bh) * g.nb + beta) * kHeadDim + threadIdx.x] =
+          (red[0][threadIdx.x] + red[1][threadIdx.x]) / float(box.cnt);
+  }
+}
+
+// Eight fp32 values rounded to nearest-even in the element type, packed.
+template <bool F16>
+__device__ inline uint4 pack8(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (F16) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 r = {_Float16(f[2 * e]), _Float16(f[2 * e + 1])};
+      w[e] = __builtin_bit_cast(uint32_t, r);
+    } else {
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      const b2 r = {__bf16(f[2 * e]), __bf16(f[2 * e + 1])};
+      w[e] = __builtin_bit_cast(uint32_t, r);
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // O: blocked [B,NH,Npad,D] -> raster [B,S,NH,D]; pad rows are not read.
+// With `oc` (coarse output [B,NH,nb,D] fp32) and `gate` (raster, elem) the
+// token row written is O + gate * oc[block], in fp32, rounded once to elem:
+// the sparse output compensated by the gated coarse branch ("FastVideo VSA"
+// guide, "Checkpoint behavior").
+template <bool F16>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restrict__ ob,
+                                                           const float* __restrict__ oc,
+                                                           const uint4* __restrict__ gate,
                                                            uint4* __restrict__ o, VsaGeom g) {
   const int wg = blockIdx.x;
   const int beta = wg % g.nb;
@@ -168,10 +219,31 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restri
   const int unit = threadIdx.x % kUnitsPerRow;
   const int lt = threadIdx.x / kUnitsPerRow;
   const uint4* src = ob + (int64_t(bh) * g.npad + int64_t(beta) * g.vol) * kUnitsPerRow;
+  float c[8];
+  if (gate != nullptr) {
+    const float4* cp =
+        reinterpret_cast<const float4*>(oc + (int64_t(bh) * g.nb + beta) * kHeadDim + unit * 8);
+    const float4 c0 = cp[0], c1 = cp[1];
+    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+  }
   for (int r = lt; r < box.cnt; r += kThreads / kUnitsPerRow) {
     const int64_t s = token_of(g, box, r);
-    o[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit] =
-        src[int64_t(r) * kUnitsPerRow + unit];
+    const int64_t at = ((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit;
+    uint4 val = src[int64_t(r) * kUnitsPerRow + unit];
+    if (gate != nullptr) {
+      const uint4 gv = gate[at];
+      const uint32_t ow[4] = {val.x, val.y, val.z, val.w};
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = fmaf(elem_f32<F16>(gw[e] & 0xffffu), c[2 * e], elem_f32<F16>(ow[e] & 0xffffu));
+        f[2 * e + 1] = fmaf(elem_f32<F16>(gw[e] >> 16), c[2 * e + 1], elem_f32<F16>(ow[e] >> 16));
+      }
+      val = pack8<F16>(f);
+    }
+    o[at] = val;
   }
 }
 
@@ -189,17 +261,29 @@ hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* po
   return hipGetLastError();
 }
 
-hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, hipStream_t s) {
+hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, float* pooled,
+                           hipStream_t s) {
   const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
-  hipLaunchKernelGGL(gather_v_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
-                     static_cast<const uint4*>(x), static_cast<uint4*>(xbt), g);
+  if (g.dtype == VSA_DTYPE_FP16)
+    hipLaunchKernelGGL(gather_v_kernel<true>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(xbt), pooled, g);
+  else
+    hipLaunchKernelGGL(gather_v_kernel<false>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(xbt), pooled, g);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const VsaGeom& g, const void* ob, void* o, hipStream_t s) {
+hipError_t launch_scatter(const VsaGeom& g, const void* ob, const float* oc, const void* gate,
+                          void* o, hipStream_t s) {
   const int64_t grid = int64_t(g.batch) * g.heads * g.nb;
-  hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s,
-                     static_cast<const uint4*>(ob), static_cast<uint4*>(o), g);
+  if (g.dtype == VSA_DTYPE_FP16)
+    hipLaunchKernelGGL(scatter_kernel<true>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(ob), oc, static_cast<const uint4*>(gate),
+                       static_cast<uint4*>(o), g);
+  else
+    hipLaunchKernelGGL(scatter_kernel<false>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(ob), oc, static_cast<const uint4*>(gate),
+                       static_cast<uint4*>(o), g);
   return hipGetLastError();
 }
 

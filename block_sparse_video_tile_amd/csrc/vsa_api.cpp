@@ -38,7 +38,7 @@ vsa_status hip_status(hipError_t e, const char* what) {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t q, k, v, o, qp, kp, col, total;
+  size_t q, k, v, o, qp, kp, vp, oc, col, total;
 };
 
 Workspace workspace_layout(const vsa_plan_s& p) {
@@ -54,6 +54,8 @@ Workspace workspace_layout(const vsa_plan_s& p) {
   w.o = off; off += align256(blk);
   w.qp = off; off += align256(pooled);
   w.kp = off; off += align256(pooled);
+  w.vp = off; off += align256(pooled);
+  w.oc = off; off += align256(pooled);
   w.col = off; off += align256(col);
   w.total = off;
   return w;
@@ -189,17 +191,40 @@ vsa_status vsa_gather(vsa_plan_t p, int32_t role, const void* x, void* xb, float
   if (!p || !x || !xb) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: null argument");
   if (role != VSA_ROLE_Q && role != VSA_ROLE_K && role != VSA_ROLE_V)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: unknown role %d", role);
-  if (role == VSA_ROLE_V) {
-    if (pooled) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: pooled must be NULL for V");
-    return hip_status(vsa::launch_gather_v(p->g, x, xb, hipStream_t(stream)), "vsa_gather(V)");
-  }
+  if (role == VSA_ROLE_V)
+    return hip_status(vsa::launch_gather_v(p->g, x, xb, pooled, hipStream_t(stream)),
+                      "vsa_gather(V)");
   return hip_status(vsa::launch_gather_qk(p->g, x, xb, pooled, hipStream_t(stream)),
                     "vsa_gather(Q/K)");
 }
 
 vsa_status vsa_scatter(vsa_plan_t p, const void* ob, void* o, void* stream) {
   if (!p || !ob || !o) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter: null argument");
-  return hip_status(vsa::launch_scatter(p->g, ob, o, hipStream_t(stream)), "vsa_scatter");
+  return hip_status(vsa::launch_scatter(p->g, ob, nullptr, nullptr, o, hipStream_t(stream)),
+                    "vsa_scatter");
+}
+
+vsa_status vsa_compress_attn(vsa_plan_t p, const float* qp, const float* kp, const float* vp,
+                             float* oc, void* stream) {
+  if (!p || !qp || !kp || !vp || !oc)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_compress_attn: null argument");
+  if ((reinterpret_cast<uintptr_t>(kp) & 15) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_compress_attn: k_pooled not 16-byte aligned");
+  if (p->g.nb > 1024)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_compress_attn: num_blocks %d > 1024 not implemented",
+                p->g.nb);
+  return hip_status(vsa::launch_compress_attn(p->g, qp, kp, vp, oc, hipStream_t(stream)),
+                    "vsa_compress_attn");
+}
+
+vsa_status vsa_scatter_gated(vsa_plan_t p, const void* ob, const float* oc, const void* gate,
+                             void* o, void* stream) {
+  if (!p || !ob || !oc || !gate || !o)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter_gated: null argument");
+  if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter_gated: o_coarse not 16-byte aligned");
+  return hip_status(vsa::launch_scatter(p->g, ob, oc, gate, o, hipStream_t(stream)),
+                    "vsa_scatter_gated");
 }
 
 vsa_status vsa_score_topk(vsa_plan_t p, const float* qp, const float* kp, int32_t topk,
@@ -246,8 +271,9 @@ vsa_status vsa_forward_workspace_size(vsa_plan_t p, size_t* bytes) {
   return ok();
 }
 
-vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v, void* out,
-                       void* ws, size_t ws_bytes, int32_t* col_out, float* lse, void* stream) {
+vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v,
+                       const void* gate, void* out, void* ws, size_t ws_bytes, int32_t* col_out,
+                       float* lse, void* stream) {
   if (!p || !q || !k || !v || !out || !ws)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: null argument");
   if (p->topk < 1)
@@ -268,6 +294,8 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
   void* ob = base + w.o;
   float* qp = reinterpret_cast<float*>(base + w.qp);
   float* kp = reinterpret_cast<float*>(base + w.kp);
+  float* vp = reinterpret_cast<float*>(base + w.vp);
+  float* oc = reinterpret_cast<float*>(base + w.oc);
   int32_t* col = col_out ? col_out : reinterpret_cast<int32_t*>(base + w.col);
   hipStream_t s = hipStream_t(stream);
   const VsaGeom& g = p->g;
@@ -275,12 +303,16 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
   hipError_t e;
   if ((e = vsa::launch_gather_qk(g, q, qb, qp, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather Q");
   if ((e = vsa::launch_gather_qk(g, k, kb, kp, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather K");
-  if ((e = vsa::launch_gather_v(g, v, vb, s)) != hipSuccess) return hip_status(e, "vsa_forward: gather V");
+  if ((e = vsa::launch_gather_v(g, v, vb, gate ? vp : nullptr, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward: gather V");
   if ((e = vsa::launch_score_topk(g, qp, kp, p->topk, col, nullptr, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: score/top-k");
   if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: attention");
-  if ((e = vsa::launch_scatter(g, ob, out, s)) != hipSuccess) return hip_status(e, "vsa_forward: scatter");
+  if (gate && (e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward: coarse attention");
+  if ((e = vsa::launch_scatter(g, ob, gate ? oc : nullptr, gate, out, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward: scatter");
   return ok();
 }
 

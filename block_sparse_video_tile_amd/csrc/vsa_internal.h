@@ -48,8 +48,13 @@ __host__ __device__ inline int block_count(const VsaGeom& g, int beta) {
 
 hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* pooled,
                             hipStream_t s);
-hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, hipStream_t s);
-hipError_t launch_scatter(const VsaGeom& g, const void* ob, void* o, hipStream_t s);
+hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, float* pooled,
+                           hipStream_t s);
+// gate == nullptr: plain scatter; otherwise O + gate * oc[block] (oc fp32 [B,NH,nb,D])
+hipError_t launch_scatter(const VsaGeom& g, const void* ob, const float* oc, const void* gate,
+                          void* o, hipStream_t s);
+hipError_t launch_compress_attn(const VsaGeom& g, const float* qp, const float* kp,
+                                const float* vp, float* oc, hipStream_t s);
 hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp, int topk,
                              int32_t* col, float* scores, hipStream_t s);
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,

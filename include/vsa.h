@@ -131,7 +131,9 @@ vsa_status vsa_plan_block_counts(vsa_plan_t plan, int32_t* counts, int64_t n);
  * NULL, the fp32 mean of each block's valid tokens (the per-block pooled
  * vector the block score is built from: the guide's intro has every key block
  * scored per query block, and the h3 FastH3 log entry pools per tile).
- * role V: writes x_blk in the blocked-V^T layout; `pooled` must be NULL.
+ * role V: writes x_blk in the blocked-V^T layout and, if `pooled` is not
+ * NULL, the fp32 mean of each block's valid values (the gate-compress
+ * branch's pooled values; h3 FastH3 log entry: that branch pools per tile).
  * x_raster: device, B*S*NH*D elem.  x_blk: device, B*NH*Npad*D elem.
  * pooled: device, B*NH*nb*D fp32, or NULL. */
 vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void* x_blk,
@@ -140,6 +142,31 @@ vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void*
 /* Blocked -> raster scatter of an output tensor (pad rows are dropped).
  * o_blk: device, blocked layout, elem.  o_raster: device, raster layout, elem. */
 vsa_status vsa_scatter(vsa_plan_t plan, const void* o_blk, void* o_raster, void* stream);
+
+/* Gate-compress (coarse) branch ("FastVideo VSA" guide, "Checkpoint
+ * behavior": a learned to_gate_compress projection compensates the sparse
+ * branch; h3 FastH3 log entry: the branch pools per tile).  The pages give
+ * no formula; this computes attention among the per-tile pooled tokens:
+ *   o_coarse[b,h,i] = sum_j softmax_j(q_pooled[b,h,i] . k_pooled[b,h,j] / sqrt(D))
+ *                     * v_pooled[b,h,j]
+ * over all nb blocks, in fp32.
+ * q_pooled, k_pooled, v_pooled: device fp32 pooled layout (vsa_gather with
+ * `pooled`), k_pooled 16-byte aligned.  o_coarse: device fp32, pooled layout.
+ * Errors: INVALID_ARGUMENT for null or misaligned pointers; UNSUPPORTED for
+ *   nb > 1024. */
+vsa_status vsa_compress_attn(vsa_plan_t plan, const float* q_pooled, const float* k_pooled,
+                             const float* v_pooled, float* o_coarse, void* stream);
+
+/* Blocked -> raster scatter of the sparse output combined with the gated
+ * coarse output: for every valid token s of block i,
+ *   o_raster[b,s,h,:] = o_blk[b,h,row(s),:] + gate[b,s,h,:] * o_coarse[b,h,i,:]
+ * elementwise in fp32, rounded once to elem.  gate: device elem raster
+ * [B,S,NH,D] (the output of the caller's to_gate_compress projection).
+ * o_coarse: device fp32 pooled layout, 16-byte aligned.  o_blk, o_raster as
+ * for vsa_scatter.
+ * Errors: INVALID_ARGUMENT for null or misaligned pointers. */
+vsa_status vsa_scatter_gated(vsa_plan_t plan, const void* o_blk, const float* o_coarse,
+                             const void* gate, void* o_raster, void* stream);
 
 /* Block score and per-row top-k ("FastVideo VSA" guide, intro: every key
  * block is scored for every query block and the top-k are kept).
@@ -182,20 +209,26 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t plan, const void* q_blk, const v
                                      void* o_blk, float* lse, void* stream);
 
 /* Bytes of device workspace vsa_forward needs for this plan (blocked Q, K,
- * V, O, pooled Q and K, and the selected block ids, each 256-byte aligned). */
+ * V, O, pooled Q, K and V, the coarse output, and the selected block ids,
+ * each 256-byte aligned). */
 vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path for a plan with topk >= 1, raster in and raster out:
  * gather Q, K (with pooling) and V; score and top-k; block-sparse attention;
  * scatter O.  q, k, v: device elem raster.  out: device elem raster.
+ * gate: device elem raster [B,S,NH,D] or NULL.  NULL runs the sparse branch
+ * alone (the guide's "Checkpoint behavior": without to_gate_compress
+ * weights there is no compensation); otherwise V is pooled too, the coarse
+ * branch runs (vsa_compress_attn) and the output is written as by
+ * vsa_scatter_gated.
  * workspace: device buffer of at least vsa_forward_workspace_size bytes,
  * 256-byte aligned, not shared with a concurrently running call.
  * col_idx_out: optional device int32 copy target for the selected ids
  * (B*NH*nb*topk) or NULL.  lse: optional device fp32 [B,NH,Npad] or NULL.
  * Errors: INVALID_ARGUMENT for null pointers or a map-mode plan (topk == 0). */
-vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void* v, void* out,
-                       void* workspace, size_t workspace_bytes, int32_t* col_idx_out,
-                       float* lse, void* stream);
+vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void* v,
+                       const void* gate, void* out, void* workspace, size_t workspace_bytes,
+                       int32_t* col_idx_out, float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* vsa_status_string(vsa_status status);

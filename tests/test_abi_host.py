@@ -111,7 +111,6 @@ def test_null_and_range_checks_before_any_device_call(plan):
     assert _raw("vsa_gather", h, 0, None, FAKE, None, None) == bad
     assert _raw("vsa_gather", h, 0, FAKE, None, None, None) == bad
     assert _raw("vsa_gather", h, 7, FAKE, FAKE, None, None) == bad          # unknown role
-    assert _raw("vsa_gather", h, 2, FAKE, FAKE, FAKE, None) == bad          # pooled with V
     assert _raw("vsa_scatter", h, None, FAKE, None) == bad
     assert _raw("vsa_score_topk", h, FAKE, FAKE, 0, FAKE, None, None) == bad   # topk < 1
     assert _raw("vsa_score_topk", h, FAKE, FAKE, 9, FAKE, None, None) == bad   # topk > nb
@@ -131,12 +130,12 @@ def test_forward_checks(plan):
     bad = vsa.VSA_ERR_INVALID_ARGUMENT
     need = vsa.vsa_forward_workspace_size(plan)
     assert need > 0 and need % 256 == 0
-    f = "vsa_forward"
-    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None, None, None) == bad
-    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, None, None, None) == bad  # alignment
-    assert _raw(f, h, FAKE, None, FAKE, FAKE, FAKE, need, None, None, None) == bad
+    f = "vsa_forward"   # (plan, q, k, v, gate, out, ws, ws_bytes, col_out, lse, stream)
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, FAKE + 16, need, None, None, None) == bad
+    assert _raw(f, h, FAKE, None, FAKE, None, FAKE, FAKE, need, None, None, None) == bad
     mp = vsa.vsa_plan(2048, (8, 16, 16), (4, 8, 8), topk=0)
-    assert _raw(f, mp.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None, None) == bad
+    assert _raw(f, mp.handle, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None, None, None) == bad
     assert "map mode" in vsa.vsa_last_error()
 
 
@@ -156,3 +155,22 @@ def test_fp16_plan_is_accepted_and_sets_the_binding_dtype():
     assert p16b.torch_dtype() == torch.bfloat16
     # geometry does not depend on the element type
     assert p16.info == p16b.info
+
+
+def test_coarse_branch_checks(plan):
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    f = "vsa_compress_attn"   # (plan, q_pooled, k_pooled, v_pooled, o_coarse, stream)
+    assert _raw(f, h, None, FAKE, FAKE, FAKE, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE + 4, FAKE, FAKE, None) == bad          # k_pooled alignment
+    big = vsa.vsa_plan(1025 * 64, (1, 1, 1025 * 64), (1, 1, 64), topk=1)
+    assert _raw(f, big.handle, FAKE, FAKE, FAKE, FAKE, None) == vsa.VSA_ERR_UNSUPPORTED
+    g = "vsa_scatter_gated"   # (plan, o_blk, o_coarse, gate, o_raster, stream)
+    assert _raw(g, h, FAKE, FAKE, None, FAKE, None) == bad
+    assert _raw(g, h, FAKE, None, FAKE, FAKE, None) == bad
+    assert _raw(g, h, FAKE, FAKE + 8, FAKE, FAKE, None) == bad          # o_coarse alignment
+    # the workspace of vsa_forward holds pooled V and the coarse output too
+    info = plan.info
+    assert vsa.vsa_forward_workspace_size(plan) >= (4 * info["blocked_elems"] * 2
+                                                    + 4 * info["pooled_elems"] * 4)
