@@ -42,12 +42,12 @@ Readings where the pages are silent (each also listed with the design notes):
   R7 no block is forced into its own row (pure top-k);
   R8 an empty row gives O = 0 and LSE = -inf;
   R9 padded tokens of edge blocks take no part in any softmax (masked);
-  R10 the gate-compress (coarse) branch is attention among the per-tile pooled
+  R15 the gate-compress (coarse) branch is attention among the per-tile pooled
      tokens: block i's pooled query attends over every block's pooled key
      with the standard head_size**-0.5 scale (its logits are the R4 block
      scores, scaled) and returns the softmax-weighted mean of the pooled
      values -- the pages give no formula, this is the plainest reading;
-  R11 the gated output is the sparse output plus the gate times the coarse
+  R16 the gated output is the sparse output plus the gate times the coarse
      output of the token's block, elementwise; the gate is a tensor shaped
      like Q (the projection's output, supplied by the caller); no gate means
      the sparse output alone.
@@ -298,7 +298,7 @@ def vsa_reference(q, k, v, dit_seq_shape, block_size, topk):
 
 
 def compress_attention(qbar, kbar, vbar, head_dim):
-    """Gate-compress (coarse) branch: attention among the per-tile pooled tokens (R10).
+    """Gate-compress (coarse) branch: attention among the per-tile pooled tokens (R15).
 
     h3-perf-stack log, FastH3 example entry: the gate-compress branch pools
     per tile.  For every (batch, head), block i's pooled query attends over
@@ -314,7 +314,7 @@ def compress_attention(qbar, kbar, vbar, head_dim):
 
 
 def gated_combine(o_sparse, o_coarse, gate, plan: Plan):
-    """Sparse output plus the gated coarse output of each token's block (R11).
+    """Sparse output plus the gated coarse output of each token's block (R16).
 
     "FastVideo VSA" guide, "Checkpoint behavior": a learned to_gate_compress
     projection compensates the sparse branch; without it the sparse branch is
@@ -332,7 +332,7 @@ def gated_combine(o_sparse, o_coarse, gate, plan: Plan):
 
 def vsa_gated_reference(q, k, v, gate, dit_seq_shape, block_size, topk):
     """Whole path with the gate-compress branch: vsa_reference, pooled values,
-    the coarse attention and the gated combination (R10, R11)."""
+    the coarse attention and the gated combination (R15, R16)."""
     ref = vsa_reference(q, k, v, dit_seq_shape, block_size, topk)
     vbar = pool_blocks(v, ref["plan"])
     oc = compress_attention(ref["qbar"], ref["kbar"], vbar, np.asarray(q).shape[-1])

@@ -2,7 +2,7 @@
 
 The branch pools values per tile, attends among the pooled tokens and adds
 the gated coarse output of each token's block to the sparse output (the
-oracle's readings R10 and R11).  The gate is a synthetic seeded tensor shaped
+oracle's readings R15 and R16).  The gate is a synthetic seeded tensor shaped
 like Q: the learned to_gate_compress weights are not available.
 """
 import numpy as np
@@ -83,7 +83,7 @@ def test_scatter_gated_matches_oracle(name, dtype):
     gate = _gate(wl, dtype)
     out = torch.full(plan.raster_shape(), 7.0, dtype=dtype, device=DEV)
     vsa.vsa_scatter_gated(plan, ob.to(DEV), oc.to(DEV), gate.to(DEV), out)
-    # oracle: the blocked sparse output back in raster order, then R11
+    # oracle: the blocked sparse output back in raster order, then R16
     vol = oplan.block_volume
     o_sparse = np.zeros((wl.batch, wl.seq_len, wl.heads, wl.head_dim))
     obh = ob.double().numpy()
