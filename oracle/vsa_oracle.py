@@ -65,6 +65,7 @@ __all__ = [
     "pool_blocks", "block_scores", "select_topk", "selection_to_csr",
     "map_to_csr", "block_sparse_attention", "vsa_reference", "valid_flops",
     "compress_attention", "gated_combine", "vsa_gated_reference",
+    "block_sparse_attention_bwd",
 ]
 
 
@@ -338,6 +339,49 @@ def vsa_gated_reference(q, k, v, gate, dit_seq_shape, block_size, topk):
     oc = compress_attention(ref["qbar"], ref["kbar"], vbar, np.asarray(q).shape[-1])
     ref.update(vbar=vbar, o_coarse=oc, gated_out=gated_combine(ref["out"], oc, gate, ref["plan"]))
     return ref
+
+
+def block_sparse_attention_bwd(q, k, v, do, plan: Plan, row_ptr, col_idx):
+    """Gradients of block_sparse_attention with respect to q, k and v.
+
+    h3-perf-stack log, sm_100a route entry: the forward-only route falls back
+    to the Triton tile-64 kernels, which keep the entire gradient path; this
+    is that gradient.  The forward is, per query token,
+    O = softmax(l) V over the valid tokens of the row's blocks with
+    l = q K^T / sqrt(D); its exact gradients (the softmax Jacobian written
+    out) are, with P the softmax probabilities and dO the output gradient:
+      dV_j += P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+      dQ = dS K / sqrt(D),  dK_j += dS^T Q / sqrt(D),
+    summed over every row that selected block j (a block listed twice in a
+    row counts twice, as in the forward).  Empty rows contribute nothing.
+    q, k, v, do: [B, S, heads, D].  Returns (dq, dk, dv) float64, same shape.
+    """
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    bsz, s, nh, d = q.shape
+    nb = plan.num_blocks
+    lists = block_token_lists(plan)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for r in range(bsz * nh * nb):
+        b, rem = divmod(r, nh * nb)
+        h, i = divmod(rem, nb)
+        cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        if len(cols) == 0:
+            continue
+        qtok = lists[i]
+        ktok = np.concatenate([lists[j] for j in cols])
+        qi, kj, vj, doi = q[b, qtok, h], k[b, ktok, h], v[b, ktok, h], do[b, qtok, h]
+        logits = (qi @ kj.T) * scale
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ vj
+        dp = doi @ vj.T
+        ds = p * (dp - (doi * o).sum(axis=1, keepdims=True))
+        dq[b, qtok, h] += (ds @ kj) * scale
+        # keys may repeat within a row: accumulate per occurrence
+        np.add.at(dk[:, :, h], (b, ktok), (ds.T @ qi) * scale)
+        np.add.at(dv[:, :, h], (b, ktok), p.T @ doi)
+    return dq, dk, dv
 
 
 def valid_flops(plan: Plan, row_ptr, col_idx, head_dim) -> int:

@@ -166,3 +166,59 @@ def test_gate_broadcast_by_token_index_is_caught(monkeypatch):
         return o_sparse + gate * np.swapaxes(np.asarray(o_coarse)[:, :, beta, :], 1, 2)
     _patch(monkeypatch, "gated_combine", bad)
     _fails(pins.test_gated_combine_special_cases)
+
+
+def _bwd_variant(drop_d_term=False, unscaled_dk=False, plain_assign=False):
+    def bwd(q, k, v, do, plan, row_ptr, col_idx):
+        q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+        bsz, s, nh, d = q.shape
+        nb = plan.num_blocks
+        lists = ov.block_token_lists(plan)
+        sc = 1.0 / math.sqrt(d)
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for r in range(bsz * nh * nb):
+            b, rem = divmod(r, nh * nb)
+            h, i = divmod(rem, nb)
+            cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+            if len(cols) == 0:
+                continue
+            qt, kt = lists[i], np.concatenate([lists[j] for j in cols])
+            lg = q[b, qt, h] @ k[b, kt, h].T * sc
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = do[b, qt, h] @ v[b, kt, h].T
+            corr = 0.0 if drop_d_term else (do[b, qt, h] * (p @ v[b, kt, h])).sum(axis=1, keepdims=True)
+            ds = p * (dp - corr)
+            dq[b, qt, h] += ds @ k[b, kt, h] * sc
+            gk = ds.T @ q[b, qt, h] * (1.0 if unscaled_dk else sc)
+            gv = p.T @ do[b, qt, h]
+            if plain_assign:
+                dk[b, kt, h] += gk
+                dv[b, kt, h] += gv
+            else:
+                np.add.at(dk[:, :, h], (b, kt), gk)
+                np.add.at(dv[:, :, h], (b, kt), gv)
+        return dq, dk, dv
+    return bwd
+
+
+def test_backward_without_rowsum_term_is_caught(monkeypatch):
+    _patch(monkeypatch, "block_sparse_attention_bwd", _bwd_variant(drop_d_term=True))
+    _fails(pins.test_backward_matches_torch_autograd_masked, 4)
+
+
+def test_backward_unscaled_dk_is_caught(monkeypatch):
+    _patch(monkeypatch, "block_sparse_attention_bwd", _bwd_variant(unscaled_dk=True))
+    _fails(pins.test_backward_all_blocks_equals_sdpa_autograd)
+
+
+def test_backward_dropping_repeated_keys_is_caught(monkeypatch):
+    _patch(monkeypatch, "block_sparse_attention_bwd", _bwd_variant(plain_assign=True))
+    _fails(pins.test_backward_repeated_block_counts_twice)
+
+
+def test_backward_mutation_harness_is_faithful(monkeypatch):
+    # the unmutated copy passes the pins the mutations fail
+    _patch(monkeypatch, "block_sparse_attention_bwd", _bwd_variant())
+    pins.test_backward_matches_torch_autograd_masked(4)
+    pins.test_backward_repeated_block_counts_twice()

@@ -485,3 +485,121 @@ def test_gated_reference_whole_path_by_loops():
             for s in toks:
                 want = ref["out"][0, s, h] + gate[0, s, h] * oc
                 np.testing.assert_allclose(ref["gated_out"][0, s, h], want, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- f2: backward of the attention
+
+def _torch_masked_grads(q, k, v, do, keep):
+    """fp64 autograd of a dense S x S attention under a token keep-mask; fully
+    masked query rows output 0 (and so get no gradient)."""
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    d = q.shape[-1]
+    logits = torch.einsum("bshd,bthd->bhst", tq, tk) / math.sqrt(d)
+    km = torch.from_numpy(keep)
+    anyk = km.any(dim=-1, keepdim=True)
+    logits = torch.where(km, logits, torch.full_like(logits, -1e300))
+    p = torch.softmax(torch.where(anyk, logits, torch.zeros_like(logits)), dim=-1) * anyk
+    o = torch.einsum("bhst,bthd->bshd", p, tv)
+    (o * torch.from_numpy(do)).sum().backward()
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("k", [1, 4])
+def test_backward_matches_torch_autograd_masked(k):
+    wl = WORKLOADS["padded_tiny"]
+    q, kk, v = (bf16_to_f64(t) for t in make_qkv(wl))
+    do = np.random.default_rng(31).standard_normal(q.shape)
+    ref = oracle.vsa_reference(q, kk, v, wl.dit_seq_shape, wl.block_size, k)
+    keep = _token_keep(ref["plan"], ref["row_ptr"], ref["col_idx"], 1, 2)
+    got = oracle.block_sparse_attention_bwd(q, kk, v, do, ref["plan"], ref["row_ptr"],
+                                            ref["col_idx"])
+    for g, w in zip(got, _torch_masked_grads(q, kk, v, do, keep)):
+        np.testing.assert_allclose(g, w, rtol=0, atol=1e-11)
+
+
+def test_backward_csr_with_zero_rows_matches_torch_autograd():
+    wl = WORKLOADS["tile64_tiny"]
+    q, kk, v = (bf16_to_f64(t) for t in make_qkv(wl))
+    rp, ci, _ = make_tile64_map(wl)
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
+    do = np.random.default_rng(32).standard_normal(q.shape)
+    keep = _token_keep(plan, rp, ci, 1, 2)
+    got = oracle.block_sparse_attention_bwd(q, kk, v, do, plan, rp, ci)
+    for g, w in zip(got, _torch_masked_grads(q, kk, v, do, keep)):
+        np.testing.assert_allclose(g, w, rtol=0, atol=1e-11)
+    # query tokens of empty rows get no gradient
+    nb = plan.num_blocks
+    for r in np.nonzero(np.diff(rp) == 0)[0]:
+        h, i = divmod(int(r), nb)
+        assert np.all(got[0][0, oracle.block_token_lists(plan)[i], h] == 0)
+
+
+def test_backward_all_blocks_equals_sdpa_autograd():
+    wl = WORKLOADS["tiny"]
+    q, kk, v = (bf16_to_f64(t) for t in make_qkv(wl))
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
+    nb = plan.num_blocks
+    rp, ci = oracle.selection_to_csr(np.tile(np.arange(nb), (1, wl.heads, nb, 1)))
+    do = np.random.default_rng(33).standard_normal(q.shape)
+    got = oracle.block_sparse_attention_bwd(q, kk, v, do, plan, rp, ci)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).requires_grad_(True) for x in (q, kk, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    (o * torch.from_numpy(do).permute(0, 2, 1, 3)).sum().backward()
+    for g, t in zip(got, (tq, tk, tv)):
+        np.testing.assert_allclose(g, t.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_constant_values_give_zero_qk_gradients():
+    # if every value row is the same vector the output does not depend on the
+    # logits, so dQ = dK = 0 and dV of each key is the probability-weighted dO
+    wl = WORKLOADS["padded_tiny"]
+    q, kk, _ = (bf16_to_f64(t) for t in make_qkv(wl))
+    v = np.broadcast_to(np.linspace(-1, 1, wl.head_dim), q.shape).copy()
+    do = np.random.default_rng(34).standard_normal(q.shape)
+    ref = oracle.vsa_reference(q, kk, v, wl.dit_seq_shape, wl.block_size, 3)
+    dq, dk, dv = oracle.block_sparse_attention_bwd(q, kk, v, do, ref["plan"], ref["row_ptr"],
+                                                   ref["col_idx"])
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    # sum of dV over keys = sum of dO over queries with a non-empty row
+    np.testing.assert_allclose(dv.sum(axis=1), do.sum(axis=1), rtol=0, atol=1e-10)
+
+
+def test_backward_repeated_block_counts_twice():
+    # a row listing block 1 twice is attention over block 1's keys duplicated
+    shape, block = (2, 8, 8), (1, 8, 8)
+    plan = oracle.make_plan(128, shape, block)
+    rng = np.random.default_rng(35)
+    q, k, v, do = (rng.standard_normal((1, 128, 1, 16)) for _ in range(4))
+    rp, ci = np.array([0, 2, 3]), np.array([1, 1, 0])
+    dq, dk, dv = oracle.block_sparse_attention_bwd(q, k, v, do, plan, rp, ci)
+    toks0, toks1 = oracle.block_token_lists(plan)
+    tq = torch.from_numpy(q[0, toks0, 0]).requires_grad_(True)
+    tk = torch.from_numpy(k[0, toks1, 0]).requires_grad_(True)
+    tv = torch.from_numpy(v[0, toks1, 0]).requires_grad_(True)
+    kk2, vv2 = torch.cat([tk, tk]), torch.cat([tv, tv])
+    o = torch.softmax(tq @ kk2.T / 4.0, dim=-1) @ vv2
+    (o * torch.from_numpy(do[0, toks0, 0])).sum().backward()
+    np.testing.assert_allclose(dq[0, toks0, 0], tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk[0, toks1, 0], tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv[0, toks1, 0], tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_finite_differences():
+    wl = WORKLOADS["padded_tiny"]
+    q, kk, v = (bf16_to_f64(t) for t in make_qkv(wl))
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, 2)
+    ref = oracle.vsa_reference(q, kk, v, wl.dit_seq_shape, wl.block_size, 2)
+    rp, ci = ref["row_ptr"], ref["col_idx"]
+    do = np.random.default_rng(36).standard_normal(q.shape)
+    grads = oracle.block_sparse_attention_bwd(q, kk, v, do, plan, rp, ci)
+
+    def loss(qq, kk_, vv):
+        return float((oracle.block_sparse_attention(qq, kk_, vv, plan, rp, ci)[0] * do).sum())
+    eps = 1e-5
+    for which, idx in ((0, (0, 5, 1, 3)), (1, (0, 700, 0, 17)), (2, (0, 130, 1, 64))):
+        args = [q.copy(), kk.copy(), v.copy()]
+        args[which][idx] += eps
+        up = loss(*args)
+        args[which][idx] -= 2 * eps
+        dn = loss(*args)
+        assert abs((up - dn) / (2 * eps) - grads[which][idx]) < 1e-6
