@@ -21,7 +21,8 @@ __all__ = [
     "VSA_DTYPE_BF16", "VSA_DTYPE_FP16", "VSA_ROLE_Q", "VSA_ROLE_K", "VSA_ROLE_V",
     "vsa_plan", "vsa_plan_destroy", "vsa_plan_get_info", "vsa_plan_describe",
     "vsa_plan_block_counts", "vsa_gather", "vsa_scatter", "vsa_score_topk",
-    "vsa_block_sparse_attn_fwd", "vsa_compress_attn", "vsa_scatter_gated",
+    "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_bwd_workspace_size",
+    "vsa_block_sparse_attn_bwd", "vsa_compress_attn", "vsa_scatter_gated",
     "vsa_forward_workspace_size", "vsa_forward", "vsa_status_string", "vsa_last_error",
 ]
 
@@ -70,6 +71,11 @@ _SIGS = {
     "vsa_block_sparse_attn_fwd": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P,
                                    _P, _P], ctypes.c_int),
     "vsa_forward_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "vsa_block_sparse_attn_bwd_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)],
+                                                 ctypes.c_int),
+    "vsa_block_sparse_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                   ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P],
+                                  ctypes.c_int),
     "vsa_compress_attn": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
     "vsa_scatter_gated": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
     "vsa_forward": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
@@ -316,6 +322,32 @@ def vsa_forward_workspace_size(plan: Plan) -> int:
     n = ctypes.c_size_t()
     _check(load_library().vsa_forward_workspace_size(plan.handle, ctypes.byref(n)))
     return n.value
+
+
+def vsa_block_sparse_attn_bwd_workspace_size(plan: Plan) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().vsa_block_sparse_attn_bwd_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def vsa_block_sparse_attn_bwd(plan: Plan, q_blk, k_blk, v_blk, o_blk, do_blk, lse, row_ptr,
+                              col_idx, uniform_k: int, nnz: int, dq_blk, dk_blk, dv_blk, workspace,
+                              stream=None):
+    """Gradients of the block-sparse forward; v_blk is token-major (gathered with role K)."""
+    be = plan.info["blocked_elems"]
+    rows = plan.num_rows()
+    et = plan.torch_dtype()
+    ws_bytes = vsa_block_sparse_attn_bwd_workspace_size(plan)
+    if workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError(f"workspace: fewer than {ws_bytes} bytes")
+    _check(load_library().vsa_block_sparse_attn_bwd(
+        plan.handle, _ptr(q_blk, be, et, "q_blk"), _ptr(k_blk, be, et, "k_blk"),
+        _ptr(v_blk, be, et, "v_blk"), _ptr(o_blk, be, et, "o_blk"), _ptr(do_blk, be, et, "do_blk"),
+        _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
+        _ptr(row_ptr, rows + 1, _i32(), "row_ptr"), _ptr(col_idx, int(nnz), _i32(), "col_idx"),
+        int(uniform_k), int(nnz), _ptr(dq_blk, be, et, "dq_blk"), _ptr(dk_blk, be, et, "dk_blk"),
+        _ptr(dv_blk, be, et, "dv_blk"), _ptr(workspace, name="workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream, q_blk, dq_blk)))
 
 
 def vsa_compress_attn(plan: Plan, q_pooled, k_pooled, v_pooled, o_coarse, stream=None):

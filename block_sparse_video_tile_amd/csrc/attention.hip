@@ -54,69 +54,14 @@
 
 #include <type_traits>
 
+#include "attn_common.h"
 #include "vsa_internal.h"
 
 namespace vsa {
 namespace {
 
-// Eight 16-bit elements (one MFMA operand per lane), held as bf16 bit
-// patterns and reinterpreted when the tensors are fp16.
-typedef __bf16 ev8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace tile;
 
-constexpr int kUnits = 1024;  // 16-byte units in one 64 x 128 sub-tile of 16-bit elements (16 KB)
-
-__device__ inline ev8 as_ev8(uint4 v) { return __builtin_bit_cast(ev8, v); }
-
-// D = A B + C on 32x32x16 tiles of bf16 (F16 = false) or fp16 operands.
-template <bool F16>
-__device__ inline f32x16 mfma_32x32x16(ev8 a, ev8 b, f32x16 c) {
-  if constexpr (F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Two fp32 values rounded to nearest-even in the element type, low half first.
-template <bool F16>
-__device__ inline uint32_t pack2(float a, float b) {
-  if constexpr (F16) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 r = {_Float16(a), _Float16(b)};
-    return __builtin_bit_cast(uint32_t, r);
-  } else {
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    const b2 r = {__bf16(a), __bf16(b)};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-}
-
-// Dispatch is round-robin over the 8 XCDs; give each XCD a contiguous run of rows.
-__device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
-  const int64_t per = n / 8, rem = n % 8;
-  const int64_t x = wg % 8, loc = wg / 8;
-  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
-}
-
-// LDS row holding key `key` of a K sub-tile: swap bits 2 and 3.
-__device__ inline int kappa(int key) {
-  return (key & ~0xc) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
-
-// LDS tiles use padded rows so that every MFMA operand read is one base
-// register plus an immediate offset and the 16-byte reads of 8 (or 16)
-// consecutive lanes fall on distinct banks:
-//   K   : 64 rows (keys, kappa-permuted) x (16 + 1) 16-byte units = 17 KB
-//   V^T : 128 rows (d) x (8 + 1) units = 18 KB
-// The pad unit of each row is filled with a copy of the row's first unit.
-constexpr int kKRow = 17, kVRow = 9;
-constexpr int kKUnits = 64 * kKRow;    // 1088
-constexpr int kVUnits = 128 * kVRow;   // 1152
-constexpr int kKChunks = kKUnits / 64;  // 17 wave-loads of 1 KB
-constexpr int kVChunks = kVUnits / 64;  // 18
-constexpr int kORow = 17;               // epilogue O staging row: 272 B
 
 // A row's CSR entries are flattened, up to kListEntries at a time, into a list
 // of 64-key sub-tile descriptors in LDS:
@@ -124,15 +69,6 @@ constexpr int kORow = 17;               // epilogue O staging row: 272 B
 // K rows of chunk c start at token row 64c of the head and V^T chunk c is the
 // c-th 64-token chunk, so the chunk index addresses both.
 constexpr int kListEntries = 1024;
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// One wave copies 64 x 16 bytes from global memory straight into LDS: lane l
-// reads `src + off` and its 16 bytes land at `dst + 16*l`.
-__device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* dst) {
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + off),
-                                   (lds_ptr_t)(dst), 16, 0, 0);
-}
 
 // Keep the scheduler from moving work across this point: the main loop is
 // laid out slot by slot (one MFMA, its operand prefetch and a share of the

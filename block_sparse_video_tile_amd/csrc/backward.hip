@@ -1,0 +1,485 @@
+// Block-sparse attention backward (dQ, dK, dV) for the VSA path on gfx950.
+//
+// h3-perf-stack commit log, sm_100a route entry: the forward-only route falls
+// back to the tile-64 kernels, which keep the entire gradient path; this is
+// that gradient for the block-sparse forward of attention.hip.  With the
+// forward's LSE the probabilities are recomputed exactly,
+//   P = exp(q.k/sqrt(D) - LSE_q),  D_q = sum_d dO_q O_q,
+//   dP = dO V^T,  dS = P (dP - D_q),
+//   dQ = dS K / sqrt(D),  dK_j += dS^T Q / sqrt(D),  dV_j += P^T dO,
+// over the valid tokens of the selected blocks (a block listed m times in a
+// row counts m times, as in the forward).
+//
+// Kernels
+//   rowdot    D_q for every blocked row.
+//   transpose blocked token-major -> d-major 64-token chunks (the layout the
+//             forward uses for V^T), for K, Q and dO.
+//   tmap      per key block j, the query blocks i whose row lists j, with the
+//             multiplicity, ascending i (one thread per column, no atomics).
+//   dq        one workgroup per query block, wave w owns 32 query rows:
+//             S^T = K Q^T and dP^T = V dO^T with the key rows of K and V
+//             staged kappa-permuted, so dS^T comes out in exactly the register
+//             layout of the B operand of dQ^T += K^T dS^T (the forward's PV
+//             arrangement with K^T in place of V^T).
+//   dv, dk    one workgroup per key block, wave w owns 32 keys, streaming the
+//             64-query sub-tiles of the query blocks that selected the block:
+//             S = Q K^T and dP = dO V^T with the query rows staged
+//             kappa-permuted, so P and dS feed dV^T += dO^T P and
+//             dK^T += Q^T dS as B operands.  dV and dK are separate kernels so
+//             that each stays within 256 VGPRs per lane.
+// The loops are plain (copy, barrier, compute, barrier): correctness and a
+// measured baseline first; the forward's software pipeline is not applied
+// here.
+
+#include "attn_common.h"
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+using namespace tile;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ helpers
+
+// D[row] = sum_d dO[row, d] * O[row, d] over all B*NH*Npad blocked rows.
+template <bool F16>
+__global__ __launch_bounds__(256) void rowdot_kernel(const uint4* __restrict__ o,
+                                                     const uint4* __restrict__ dout,
+                                                     float* __restrict__ dsum, int64_t rows) {
+  const int64_t row = int64_t(blockIdx.x) * 16 + threadIdx.x / 16;
+  const int unit = threadIdx.x % 16;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint4 a = o[row * 16 + unit], b = dout[row * 16 + unit];
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float alo, ahi, blo, bhi;
+      if constexpr (F16) {
+        alo = float(__builtin_bit_cast(_Float16, uint16_t(aw[e] & 0xffffu)));
+        ahi = float(__builtin_bit_cast(_Float16, uint16_t(aw[e] >> 16)));
+        blo = float(__builtin_bit_cast(_Float16, uint16_t(bw[e] & 0xffffu)));
+        bhi = float(__builtin_bit_cast(_Float16, uint16_t(bw[e] >> 16)));
+      } else {
+        alo = __uint_as_float(aw[e] << 16);
+        ahi = __uint_as_float(aw[e] & 0xffff0000u);
+        blo = __uint_as_float(bw[e] << 16);
+        bhi = __uint_as_float(bw[e] & 0xffff0000u);
+      }
+      acc = fmaf(alo, blo, fmaf(ahi, bhi, acc));
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && unit == 0) dsum[row] = acc;
+}
+
+// Blocked token-major [B,NH,Npad,D] -> [B,NH,Npad/64,D,64]: one workgroup per
+// 64-token chunk, transposed through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint4* __restrict__ x,
+                                                        uint4* __restrict__ xt) {
+  __shared__ __align__(16) uint16_t t[64][kHeadDim + 8];
+  const int64_t c = blockIdx.x;  // chunk over B*NH*Npad/64
+  const uint4* src = x + c * 64 * 16;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int idx = threadIdx.x + p * 256;
+    *reinterpret_cast<uint4*>(&t[idx / 16][(idx % 16) * 8]) = src[idx];
+  }
+  __syncthreads();
+  uint4* dst = xt + c * kHeadDim * 8;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int idx = threadIdx.x + p * 256;
+    const int d = idx % kHeadDim, ku = idx / kHeadDim;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(t[ku * 8 + 2 * e][d]) | (uint32_t(t[ku * 8 + 2 * e + 1][d]) << 16);
+    dst[d * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Bounds of CSR row r, sanitised exactly as the forward does.
+__device__ inline void row_bounds(const int32_t* row_ptr, int uniform_k, int64_t nnz, int64_t r,
+                                  int64_t& beg, int64_t& end) {
+  if (row_ptr != nullptr) {
+    beg = min(max(int64_t(row_ptr[r]), int64_t(0)), nnz);
+    end = min(max(int64_t(row_ptr[r + 1]), beg), nnz);
+  } else {
+    beg = r * uniform_k;
+    end = beg + uniform_k;
+  }
+}
+
+// Transposed block map: for (bh, j), the ascending query blocks i whose row
+// lists j, packed as i | min(multiplicity, 65535) << 16, and their count.
+// One workgroup per (b, h); thread t handles columns t, t + 256, ...
+__global__ __launch_bounds__(256) void tmap_kernel(const int32_t* __restrict__ row_ptr,
+                                                   const int32_t* __restrict__ col,
+                                                   int uniform_k, int64_t nnz,
+                                                   int32_t* __restrict__ tlist,
+                                                   int32_t* __restrict__ tcount, VsaGeom g) {
+  const int nb = g.nb;
+  const int64_t bh = blockIdx.x;
+  for (int j = threadIdx.x; j < nb; j += 256) {
+    int cnt = 0;
+    int32_t* out = tlist + (bh * nb + j) * int64_t(nb);
+    for (int i = 0; i < nb; ++i) {
+      int64_t beg, end;
+      row_bounds(row_ptr, uniform_k, nnz, bh * nb + i, beg, end);
+      int m = 0;
+      for (int64_t e = beg; e < end; ++e) m += col[e] == j ? 1 : 0;
+      if (m > 0) out[cnt++] = i | (min(m, 65535) << 16);
+    }
+    tcount[bh * nb + j] = cnt;
+  }
+}
+
+// Per-lane copy offsets (16-byte units inside one 64-token sub-tile) of the
+// padded LDS layouts: "row" tiles (64 token rows, kappa-permuted, 17 units
+// per row) and "column" tiles (128 d rows of 64 tokens, 9 units per row).
+// Positions past the buffer are clamped; their copies are not issued.
+__device__ inline uint32_t row_tile_off(int pos) {
+  pos = min(pos, kKUnits - 1);
+  const int row = pos / kKRow, unit = pos % kKRow;
+  return kappa(row) * 16 + (unit < 16 ? unit : 0);
+}
+__device__ inline uint32_t col_tile_off(int pos) {
+  pos = min(pos, kVUnits - 1);
+  const int row = pos / kVRow, unit = pos % kVRow;
+  return row * 8 + (unit < 8 ? unit : 0);
+}
+
+// Copy one sub-tile with all NW waves of the workgroup.
+template <int NW, int CHUNKS>
+__device__ inline void copy_tile(const uint4* src, uint4* dst, int wave, int lane, bool row_tile) {
+#pragma unroll
+  for (int x = 0; x < (CHUNKS + NW - 1) / NW; ++x) {
+    const int c = wave + x * NW;
+    if (c < CHUNKS) {
+      const int pos = c * 64 + lane;
+      wave_copy_to_lds(src, row_tile ? row_tile_off(pos) : col_tile_off(pos), dst + c * 64);
+    }
+  }
+}
+
+__device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Store one wave's 32 x 128 accumulator tile (acc[dt] register j holds row
+// l%32, column 32dt + 8(j/4) + 4(l/32) + j%4) times `mul` as element rows.
+template <bool F16>
+__device__ inline void store_rows(const f32x16 (&acc)[4], float mul, uint4* rows_base, int l32,
+                                  int half) {
+  uint2* dst = reinterpret_cast<uint2*>(rows_base + int64_t(l32) * 16);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      dst[(dt * 32 + 8 * jj + 4 * half) / 4] =
+          make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
+                     pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <int NW, bool F16>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ kt, const uint4* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ col, int uniform_k, int64_t nnz, uint4* __restrict__ dq,
+    VsaGeom g, float scale_log2, float scale) {
+  __shared__ __align__(16) uint4 ks[kKUnits];
+  __shared__ __align__(16) uint4 vs[kKUnits];
+  __shared__ __align__(16) uint4 kts[kVUnits];
+  const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
+  const int64_t r = xcd_remap(blockIdx.x, nrows);
+  const int i = int(r % g.nb);
+  const int64_t bh = r / g.nb;
+  const int cq = block_count(g, i);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, half = lane / 32, l32 = lane & 31;
+  const int qrow = wave * 32 + l32;
+  const bool active = wave * 32 < cq;
+  const bool row_valid = qrow < cq;
+  const int64_t row0 = bh * g.npad + int64_t(i) * g.vol;
+
+  ev8 qf[8], df[8];
+  float lse_l2 = INFINITY, dq_row = 0.f;
+  if (active) {
+    const uint4* qs = q + (row0 + qrow) * 16;
+    const uint4* ds = dout + (row0 + qrow) * 16;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      qf[s] = as_ev8(qs[2 * s + half]);
+      df[s] = as_ev8(ds[2 * s + half]);
+    }
+    if (row_valid) {
+      lse_l2 = lse[row0 + qrow] * kLog2e;
+      dq_row = dsum[row0 + qrow];
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[dt][j] = 0.f;
+
+  const uint4* const kbase = k + bh * g.npad * 16;
+  const uint4* const vbase = v + bh * g.npad * 16;
+  const uint4* const ktbase = kt + bh * (g.npad / kKvChunk) * kUnits;
+  const int cpb = g.vol / kKvChunk;
+  const int kread = l32 * kKRow + half, ktread = l32 * kVRow + half;
+  int64_t beg, end;
+  row_bounds(row_ptr, uniform_k, nnz, r, beg, end);
+  for (int64_t e = beg; e < end; ++e) {
+    const int j = col[e];
+    if (j < 0 || j >= g.nb) continue;
+    const int cj = block_count(g, j);
+    for (int sub = 0; sub * kKvChunk < cj; ++sub) {
+      const int64_t chunk = int64_t(j) * cpb + sub;
+      __syncthreads();  // every wave is done with the previous sub-tile
+      copy_tile<NW, kKChunks>(kbase + chunk * kUnits, ks, wave, lane, true);
+      copy_tile<NW, kKChunks>(vbase + chunk * kUnits, vs, wave, lane, true);
+      copy_tile<NW, kVChunks>(ktbase + chunk * kUnits, kts, wave, lane, false);
+      wait_copies();
+      __syncthreads();
+      if (!active) continue;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j2 = 0; j2 < 16; ++j2) s[mt][j2] = dp[mt][j2] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          s[mt] = mfma_32x32x16<F16>(as_ev8(ks[kread + mt * 32 * kKRow + 2 * st]), qf[st], s[mt]);
+          dp[mt] = mfma_32x32x16<F16>(as_ev8(vs[kread + mt * 32 * kKRow + 2 * st]), df[st], dp[mt]);
+        }
+      const int valid = min(kKvChunk, cj - sub * kKvChunk);
+      // dS^T pairs, grouped by 16-key step cc (keys 16cc + 8*half + 0..7)
+      uint32_t dsw[4][4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          float d2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * (cc % 2) + t + u;
+            const int key = 16 * cc + 8 * half + t + u;
+            const float p = key < valid
+                                ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2, -lse_l2))
+                                : 0.f;
+            d2[u] = p * (dp[cc / 2][jj] - dq_row);
+          }
+          dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
+        }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
+                                                         dsw[cc][3]));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          acc[dt] = mfma_32x32x16<F16>(as_ev8(kts[ktread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+      }
+    }
+  }
+  // dQ rows; pad query rows are written as zero
+  store_rows<F16>(acc, row_valid ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32, half);
+}
+
+// ------------------------------------------------------------------ dV, dK
+
+// Per 64-query sub-tile the workgroup stages lse (log2 units, +inf for pad
+// query rows) and D; register jj of query tile mt holds query
+// 32mt + 16(jj/8) + 8*half + jj%8 (query rows staged kappa-permuted).
+__device__ inline int query_of(int mt, int jj, int half) {
+  return 32 * mt + 16 * (jj / 8) + 8 * half + jj % 8;
+}
+
+template <int NW, bool F16, bool DK>
+__global__ __launch_bounds__(NW * 64) void dkv_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ qt, const uint4* __restrict__ dout, const uint4* __restrict__ dot,
+    const float* __restrict__ lse, const float* __restrict__ dsum,
+    const int32_t* __restrict__ tlist, const int32_t* __restrict__ tcount,
+    uint4* __restrict__ grad, VsaGeom g, float scale_log2, float scale) {
+  // A operand of the first product(s): query rows (Q, and dO for dK); A of the
+  // accumulation: d rows (dO^T for dV, Q^T for dK)
+  __shared__ __align__(16) uint4 qsh[kKUnits];
+  __shared__ __align__(16) uint4 dsh[DK ? kKUnits : 1];
+  __shared__ __align__(16) uint4 tsh[kVUnits];
+  __shared__ float lse_sh[kKvChunk], d_sh[kKvChunk];
+  const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
+  const int64_t c = xcd_remap(blockIdx.x, ncols);
+  const int j = int(c % g.nb);
+  const int64_t bh = c / g.nb;
+  const int cj = block_count(g, j);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, half = lane / 32, l32 = lane & 31;
+  const int key = wave * 32 + l32;
+  const bool active = wave * 32 < cj;
+  const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
+
+  ev8 kf[8], vf[8];
+  if (active) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      kf[s] = as_ev8(k[(key0 + key) * 16 + 2 * s + half]);
+      if constexpr (DK) vf[s] = as_ev8(v[(key0 + key) * 16 + 2 * s + half]);
+    }
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+
+  const uint4* const qbase = q + bh * g.npad * 16;
+  const uint4* const dbase = dout + bh * g.npad * 16;
+  const uint4* const tbase = (DK ? qt : dot) + bh * (g.npad / kKvChunk) * kUnits;
+  const int cpb = g.vol / kKvChunk;
+  const int qread = l32 * kKRow + half, tread = l32 * kVRow + half;
+  const int n = tcount[c];
+  const int32_t* list = tlist + c * int64_t(g.nb);
+  for (int e = 0; e < n; ++e) {
+    const int32_t ent = list[e];
+    const int i = ent & 0xffff;
+    const float mult = float(uint32_t(ent) >> 16);
+    const int cq = block_count(g, i);
+    for (int sub = 0; sub * kKvChunk < cq; ++sub) {
+      const int64_t chunk = int64_t(i) * cpb + sub;
+      const int nq = min(kKvChunk, cq - sub * kKvChunk);
+      __syncthreads();
+      copy_tile<NW, kKChunks>(qbase + chunk * kUnits, qsh, wave, lane, true);
+      if constexpr (DK) copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsh, wave, lane, true);
+      copy_tile<NW, kVChunks>(tbase + chunk * kUnits, tsh, wave, lane, false);
+      if (threadIdx.x < kKvChunk) {
+        const int64_t row = bh * g.npad + chunk * kKvChunk + threadIdx.x;
+        const bool ok = int(threadIdx.x) < nq;
+        lse_sh[threadIdx.x] = ok ? lse[row] * kLog2e : INFINITY;
+        d_sh[threadIdx.x] = ok ? dsum[row] : 0.f;
+      }
+      wait_copies();
+      __syncthreads();
+      if (!active) continue;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) s[mt][jj] = dp[mt][jj] = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          s[mt] = mfma_32x32x16<F16>(as_ev8(qsh[qread + mt * 32 * kKRow + 2 * st]), kf[st], s[mt]);
+          if constexpr (DK)
+            dp[mt] = mfma_32x32x16<F16>(as_ev8(dsh[qread + mt * 32 * kKRow + 2 * st]), vf[st],
+                                        dp[mt]);
+        }
+      // B operand of the accumulation, by 16-query step cc
+      uint32_t bw[4][4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          float x2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * (cc % 2) + t + u;
+            const int qi = query_of(cc / 2, jj, half);
+            // pad keys of this block take no part (their rows are also stored as 0)
+            const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
+                                                                   -lse_sh[qi])) * mult
+                                     : 0.f;
+            x2[u] = DK ? p * (dp[cc / 2][jj] - d_sh[qi]) : p;
+          }
+          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
+        }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
+                                                         bw[cc][3]));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          acc[dt] = mfma_32x32x16<F16>(as_ev8(tsh[tread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+      }
+    }
+  }
+  // rows of this wave's keys; pad key rows are written as zero
+  store_rows<F16>(acc, key < cj ? (DK ? scale : 1.f) : 0.f, grad + (key0 + wave * 32) * 16,
+                  l32, half);
+}
+
+template <int NW, bool F16>
+hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
+  const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
+  const float scale = 1.0f / sqrtf(float(g.head_dim));
+  const float scale_log2 = scale * kLog2e;
+  hipLaunchKernelGGL((dq_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
+                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.kt),
+                     static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.row_ptr, a.col,
+                     a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), g, scale_log2, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkv_kernel<NW, F16, false>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
+                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
+                     static_cast<const uint4*>(a.dout), static_cast<const uint4*>(a.dot), a.lse,
+                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dv), g, scale_log2, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dkv_kernel<NW, F16, true>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
+                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
+                     static_cast<const uint4*>(a.dout), static_cast<const uint4*>(a.dot), a.lse,
+                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk), g, scale_log2, scale);
+  return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_bwd_typed(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
+  return g.dtype == VSA_DTYPE_FP16 ? launch_bwd_nw<NW, true>(g, a, s)
+                                   : launch_bwd_nw<NW, false>(g, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
+  const int64_t blocked_rows = int64_t(g.batch) * g.heads * g.npad;
+  hipError_t e;
+  if (g.dtype == VSA_DTYPE_FP16)
+    hipLaunchKernelGGL(rowdot_kernel<true>, dim3(unsigned((blocked_rows + 15) / 16)), dim3(256),
+                       0, s, static_cast<const uint4*>(a.o), static_cast<const uint4*>(a.dout),
+                       a.dsum, blocked_rows);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<false>, dim3(unsigned((blocked_rows + 15) / 16)), dim3(256),
+                       0, s, static_cast<const uint4*>(a.o), static_cast<const uint4*>(a.dout),
+                       a.dsum, blocked_rows);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned chunks = unsigned(blocked_rows / kKvChunk);
+  const void* srcs[3] = {a.k, a.q, a.dout};
+  void* dsts[3] = {a.kt, a.qt, a.dot};
+  for (int t = 0; t < 3; ++t) {
+    hipLaunchKernelGGL(transpose_kernel, dim3(chunks), dim3(256), 0, s,
+                       static_cast<const uint4*>(srcs[t]), static_cast<uint4*>(dsts[t]));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(tmap_kernel, dim3(unsigned(int64_t(g.batch) * g.heads)), dim3(256), 0, s,
+                     a.row_ptr, a.col, a.uniform_k, a.nnz, a.tlist, a.tcount, g);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  switch (g.vol / 32) {
+    case 2: return launch_bwd_typed<2>(g, a, s);
+    case 4: return launch_bwd_typed<4>(g, a, s);
+    case 6: return launch_bwd_typed<6>(g, a, s);
+    case 8: return launch_bwd_typed<8>(g, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace vsa

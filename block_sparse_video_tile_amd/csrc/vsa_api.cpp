@@ -61,6 +61,25 @@ Workspace workspace_layout(const vsa_plan_s& p) {
   return w;
 }
 
+struct BwdWorkspace {
+  size_t dsum, kt, qt, dot, tlist, tcount, total;
+};
+BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
+  const VsaGeom& g = p.g;
+  const size_t heads = size_t(g.batch) * g.heads;
+  const size_t blk = heads * g.npad * g.head_dim * 2;
+  BwdWorkspace w;
+  size_t off = 0;
+  w.dsum = off; off += align256(heads * g.npad * 4);
+  w.kt = off; off += align256(blk);
+  w.qt = off; off += align256(blk);
+  w.dot = off; off += align256(blk);
+  w.tlist = off; off += align256(heads * g.nb * size_t(g.nb) * 4);
+  w.tcount = off; off += align256(heads * g.nb * 4);
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +282,57 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k,
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
                                          hipStream_t(stream)),
                     "vsa_block_sparse_attn_fwd");
+}
+
+
+vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t p, size_t* bytes) {
+  if (!p || !bytes)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_bwd_workspace_size: null");
+  *bytes = bwd_workspace_layout(*p).total;
+  return ok();
+}
+
+vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t p, const void* q, const void* k, const void* v,
+                                     const void* o, const void* dout, const float* lse,
+                                     const int32_t* row_ptr, const int32_t* col,
+                                     int32_t uniform_k, int64_t nnz, void* dq, void* dk, void* dv,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  if (!p || !q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_bwd: null argument");
+  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_bwd: nnz < 0");
+  if (nnz > 0 && !col)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_bwd: null col_idx with nnz > 0");
+  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
+  if (!row_ptr) {
+    if (uniform_k < 0 || uniform_k > p->g.nb)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_bwd: uniform_k %d outside [0, %d]", uniform_k, p->g.nb);
+    if (nnz < rows * uniform_k)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_bwd: nnz %lld < rows*uniform_k = %lld", (long long)nnz,
+                  (long long)(rows * uniform_k));
+  }
+  if (p->g.nb > 4096)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "vsa_block_sparse_attn_bwd: num_blocks %d > 4096 not implemented", p->g.nb);
+  const BwdWorkspace w = bwd_workspace_layout(*p);
+  if (ws_bytes < w.total)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_bwd: workspace %zu bytes < %zu",
+                ws_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_bwd: workspace not 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  vsa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+  a.row_ptr = row_ptr; a.col = col; a.uniform_k = row_ptr ? 0 : uniform_k; a.nnz = nnz;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsum = reinterpret_cast<float*>(base + w.dsum);
+  a.kt = base + w.kt; a.qt = base + w.qt; a.dot = base + w.dot;
+  a.tlist = reinterpret_cast<int32_t*>(base + w.tlist);
+  a.tcount = reinterpret_cast<int32_t*>(base + w.tcount);
+  return hip_status(vsa::launch_attn_bwd(p->g, a, hipStream_t(stream)),
+                    "vsa_block_sparse_attn_bwd");
 }
 
 vsa_status vsa_forward_workspace_size(vsa_plan_t p, size_t* bytes) {

@@ -53,6 +53,23 @@ hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, float* po
 // gate == nullptr: plain scatter; otherwise O + gate * oc[block] (oc fp32 [B,NH,nb,D])
 hipError_t launch_scatter(const VsaGeom& g, const void* ob, const float* oc, const void* gate,
                           void* o, hipStream_t s);
+// Device buffers of one backward call (blocked layouts; see vsa.h).
+struct BwdArgs {
+  const void *q, *k, *v, *o, *dout;   // token-major blocked inputs
+  const float* lse;                   // forward LSE [B,NH,Npad]
+  const int32_t* row_ptr;             // CSR (nullptr = uniform rows)
+  const int32_t* col;
+  int uniform_k;
+  int64_t nnz;
+  void *dq, *dk, *dv;                 // token-major blocked outputs
+  // workspace
+  float* dsum;                        // rowsum(dO * O) [B,NH,Npad]
+  void *kt, *qt, *dot;                // d-major 64-token chunks of K, Q, dO
+  int32_t* tlist;                     // [B*NH*nb][nb] transposed block map
+  int32_t* tcount;                    // [B*NH*nb]
+};
+hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s);
+
 hipError_t launch_compress_attn(const VsaGeom& g, const float* qp, const float* kp,
                                 const float* vp, float* oc, hipStream_t s);
 hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp, int topk,

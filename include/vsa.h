@@ -208,6 +208,36 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t plan, const void* q_blk, const v
                                      const int32_t* col_idx, int32_t uniform_k, int64_t nnz,
                                      void* o_blk, float* lse, void* stream);
 
+/* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
+ * rowsum(dO*O) [B,NH,Npad] fp32, d-major copies of K, Q and dO, and the
+ * transposed block map (B*NH*nb*nb + B*NH*nb int32), each 256-byte aligned. */
+vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t plan, size_t* bytes);
+
+/* Gradients of vsa_block_sparse_attn_fwd (h3-perf-stack log, sm_100a route
+ * entry: the route's fallback kernels keep the entire gradient path).  With
+ * the forward's LSE the probabilities are recomputed exactly:
+ *   P = exp(q.k/sqrt(D) - LSE_q), D_q = sum_d dO_q*O_q, dS = P (dO V^T - D_q),
+ *   dQ = dS K / sqrt(D),  dK_j += dS^T Q / sqrt(D),  dV_j += P^T dO
+ * over the valid tokens of the blocks of each row; a block listed m times in
+ * a row counts m times, as in the forward.  Products and softmax in fp32, P
+ * and dS rounded to elem for the matrix products, gradients rounded to elem.
+ * q_blk, k_blk, o_blk, do_blk: device elem blocked layout (do_blk is the
+ *   output gradient gathered like Q).  v_blk: device elem blocked layout --
+ *   token-major, i.e. V gathered with role Q or K, NOT the V^T layout.
+ * lse: device fp32 [B,NH,Npad], as written by the forward on the same map.
+ * row_ptr, col_idx, uniform_k, nnz: the forward's map, same rules.
+ * dq_blk, dk_blk, dv_blk: device elem blocked layout; pad rows are written 0.
+ * workspace: device buffer of vsa_block_sparse_attn_bwd_workspace_size bytes,
+ *   256-byte aligned, not shared with a concurrently running call.
+ * Errors: INVALID_ARGUMENT for null pointers, nnz < 0, uniform_k outside
+ *   [0, nb], a short or misaligned workspace; UNSUPPORTED for nb > 4096. */
+vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t plan, const void* q_blk, const void* k_blk,
+                                     const void* v_blk, const void* o_blk, const void* do_blk,
+                                     const float* lse, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t uniform_k, int64_t nnz,
+                                     void* dq_blk, void* dk_blk, void* dv_blk, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace vsa_forward needs for this plan (blocked Q, K,
  * V, O, pooled Q, K and V, the coarse output, and the selected block ids,
  * each 256-byte aligned). */

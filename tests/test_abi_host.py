@@ -174,3 +174,32 @@ def test_coarse_branch_checks(plan):
     info = plan.info
     assert vsa.vsa_forward_workspace_size(plan) >= (4 * info["blocked_elems"] * 2
                                                     + 4 * info["pooled_elems"] * 4)
+
+
+def test_backward_checks(plan):
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    need = vsa.vsa_block_sparse_attn_bwd_workspace_size(plan)
+    info = plan.info
+    # rowsum, three d-major copies and the transposed map (nb x nb per head)
+    assert need >= (info["num_rows"] // info["num_blocks"]) * (
+        info["padded_len"] * 4 + info["num_blocks"] ** 2 * 4) + 3 * info["blocked_elems"] * 2
+    f = "vsa_block_sparse_attn_bwd"
+    # (plan, q, k, v, o, do, lse, row_ptr, col, uniform_k, nnz, dq, dk, dv, ws, ws_bytes, stream)
+    args = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE,
+            need, None]
+    for idx in (1, 5, 6, 11, 14):                      # null inputs, outputs, workspace
+        a = list(args)
+        a[idx] = None
+        assert _raw(f, *a) == bad
+    a = list(args); a[9] = 9                            # uniform_k > nb
+    assert _raw(f, *a) == bad
+    a = list(args); a[10] = 63                          # nnz short for uniform rows
+    assert _raw(f, *a) == bad
+    a = list(args); a[15] = need - 1                    # short workspace
+    assert _raw(f, *a) == bad
+    a = list(args); a[14] = FAKE + 64                   # misaligned workspace
+    assert _raw(f, *a) == bad
+    big = vsa.vsa_plan(4097 * 64, (1, 1, 4097 * 64), (1, 1, 64), topk=1)
+    a = list(args); a[0] = big.handle; a[9] = 1; a[10] = 4097; a[15] = 1 << 40
+    assert _raw(f, *a) == vsa.VSA_ERR_UNSUPPORTED
