@@ -181,6 +181,69 @@ def cpu_baseline(wl, q, k, v, budget_s):
                       f"nproc={os.cpu_count()}"}
 
 
+def bench_backward(args, wl, plan, elem, dq, dk, dv):
+    """Time vsa_block_sparse_attn_bwd on the workload (the forward runs once for O and LSE).
+
+    Work counted: the five products of the attention backward (S recompute,
+    dP, dV, dK, dQ) on valid (query, key) pairs of the selected blocks, i.e.
+    2.5 x the forward's F_valid.
+    """
+    dev = dq.device
+    bs = plan.blocked_shape()
+    qb, kb, vb, ob, dob = (torch.empty(bs, dtype=elem, device=dev) for _ in range(5))
+    vtb = torch.empty(plan.blocked_vt_shape(), dtype=elem, device=dev)
+    qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=dev)
+    kp = torch.empty_like(qp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, dq, qb, qp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dk, kb, kp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dv, vb)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vtb)
+    gen = torch.Generator("cpu").manual_seed(41)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_Q,
+                   torch.randn(plan.raster_shape(), generator=gen).to(elem).to(dev), dob)
+    col = torch.empty(plan.num_rows() * wl.topk, dtype=torch.int32, device=dev)
+    vsa.vsa_score_topk(plan, qp, kp, wl.topk, col)
+    lse = torch.empty((plan.batch, plan.heads, plan.padded_len), dtype=torch.float32, device=dev)
+    vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vtb, None, col, wl.topk, col.numel(), ob, lse)
+    grads = [torch.empty(bs, dtype=elem, device=dev) for _ in range(3)]
+    ws = torch.empty(vsa.vsa_block_sparse_attn_bwd_workspace_size(plan), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        vsa.vsa_block_sparse_attn_bwd(plan, qb, kb, vb, ob, dob, lse, None, col, wl.topk,
+                                      col.numel(), *grads, ws)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(args.steps):
+        step()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    ms = max(float(np.mean(per)), wall * 1e3 / args.steps)
+    f_valid, _ = step_flops(plan, col.cpu().numpy().astype(np.int64), None, wl.topk)
+    f_bwd = 2.5 * f_valid
+    tf = f_bwd / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "attention backward effective TFLOP/s (5 products on selected valid pairs)",
+        "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic: seeded inputs and output gradient, " + args.dtype,
+        "config": {"workload": wl.name, "topk": wl.topk, "heads": wl.heads,
+                   "seq_len": wl.seq_len, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_16BIT_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_16BIT_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "flops_backward": f_bwd,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +252,8 @@ def main():
     ap.add_argument("--workload", default="wan5b_k64", choices=sorted(WORKLOADS))
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "fp16"],
                     help="element type of Q, K, V and O (the headline is bf16)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the attention backward (dQ, dK, dV) instead of the forward layer")
     ap.add_argument("--gated", action="store_true",
                     help="also run the gate-compress branch (pooled V, coarse attention, "
                          "gated scatter) with a synthetic gate")
@@ -224,6 +289,11 @@ def main():
     plan = vsa.vsa_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, batch=wl.batch,
                         num_heads=wl.heads, head_dim=wl.head_dim, topk=wl.topk or 0,
                         dtype=vsa.VSA_DTYPE_FP16 if args.dtype == "fp16" else vsa.VSA_DTYPE_BF16)
+    if args.backward:
+        if not wl.topk:
+            sys.exit("--backward runs on a top-k workload")
+        bench_backward(args, wl, plan, elem, dq, dk, dv)
+        return
     log(f"[bench] {vsa.vsa_plan_describe(plan)}")
     qb = torch.empty(plan.blocked_shape(), dtype=elem, device=dev)
     kb = torch.empty_like(qb)
