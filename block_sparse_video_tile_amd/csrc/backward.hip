@@ -27,8 +27,8 @@
 //             kappa-permuted, so P and dS feed dV^T += dO^T P and
 //             dK^T += Q^T dS as B operands.  dV and dK are separate kernels so
 //             that each stays within 256 VGPRs per lane.
-// The loops are plain (copy, barrier, compute, barrier): correctness and a
-// measured baseline first; the forward's software pipeline is not applied
+// Sub-tiles are double-buffered (copies of the next one in flight while the
+// current one is computed); the forward's slot-level schedule is not applied
 // here.
 
 #include "attn_common.h"
@@ -183,6 +183,44 @@ __device__ inline void store_rows(const f32x16 (&acc)[4], float mul, uint4* rows
                      pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
 }
 
+// ------------------------------------------------------------------ work lists
+
+// Each workgroup flattens its work (the CSR row for dQ, the key block's list
+// of query blocks for dK/dV) into a list of 64-token sub-tile descriptors in
+// LDS, kPassEntries entries at a time:
+//   (64-token chunk index within the head) << 7 | (valid tokens - 1)
+// and then streams the sub-tiles double-buffered: the copies of sub-tile n+1
+// are in flight while sub-tile n is computed, one wait and one barrier per
+// sub-tile.
+constexpr int kPassEntries = 1024;
+
+// Exclusive scan of cnt[0..m) in place by wave 0; *total receives the sum.
+__device__ inline void scan_counts(int* cnt, int m, int* total, int wave, int lane) {
+  if (wave != 0) return;
+  constexpr int kPer = kPassEntries / 64;
+  int loc[kPer];
+  int sum = 0;
+#pragma unroll
+  for (int x = 0; x < kPer; ++x) {
+    const int e = lane * kPer + x;
+    loc[x] = sum;
+    sum += e < m ? cnt[e] : 0;
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int up = __shfl_up(incl, d);
+    if (lane >= d) incl += up;
+  }
+  const int base = incl - sum;
+#pragma unroll
+  for (int x = 0; x < kPer; ++x) {
+    const int e = lane * kPer + x;
+    if (e < m) cnt[e] = base + loc[x];
+  }
+  if (lane == 63) *total = incl;
+}
+
 // ------------------------------------------------------------------ dQ
 
 template <int NW, bool F16>
@@ -192,16 +230,26 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, int uniform_k, int64_t nnz, uint4* __restrict__ dq,
     VsaGeom g, float scale_log2, float scale) {
-  __shared__ __align__(16) uint4 ks[kKUnits];
-  __shared__ __align__(16) uint4 vs[kKUnits];
-  __shared__ __align__(16) uint4 kts[kVUnits];
+  constexpr int kThreads = NW * 64;
+  constexpr int kPassTiles = kPassEntries * (NW / 2);  // <= vol/64 sub-tiles per block
+  // two buffer sets: K rows, V rows (kappa, padded), K^T (d-major, padded)
+  __shared__ __align__(16) uint4 ks0[kKUnits];
+  __shared__ __align__(16) uint4 vs0[kKUnits];
+  __shared__ __align__(16) uint4 kts0[kVUnits];
+  __shared__ __align__(16) uint4 ks1[kKUnits];
+  __shared__ __align__(16) uint4 vs1[kKUnits];
+  __shared__ __align__(16) uint4 kts1[kVUnits];
+  __shared__ int tl[kPassTiles];
+  __shared__ int esc[kPassEntries];
+  __shared__ int ntl;
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   const int64_t r = xcd_remap(blockIdx.x, nrows);
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int lane = threadIdx.x % 64, half = lane / 32, l32 = lane & 31;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
   const int qrow = wave * 32 + l32;
   const bool active = wave * 32 < cq;
   const bool row_valid = qrow < cq;
@@ -233,60 +281,93 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   const uint4* const ktbase = kt + bh * (g.npad / kKvChunk) * kUnits;
   const int cpb = g.vol / kKvChunk;
   const int kread = l32 * kKRow + half, ktread = l32 * kVRow + half;
+
+  auto issue = [&](int d, uint4* ksb, uint4* vsb, uint4* ktsb) {
+    const int64_t chunk = d >> 7;
+    copy_tile<NW, kKChunks>(kbase + chunk * kUnits, ksb, wave, lane, true);
+    copy_tile<NW, kKChunks>(vbase + chunk * kUnits, vsb, wave, lane, true);
+    copy_tile<NW, kVChunks>(ktbase + chunk * kUnits, ktsb, wave, lane, false);
+  };
+  auto compute = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
+    if (!active) return;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int j2 = 0; j2 < 16; ++j2) s[mt][j2] = dp[mt][j2] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt] = mfma_32x32x16<F16>(as_ev8(ksb[kread + mt * 32 * kKRow + 2 * st]), qf[st], s[mt]);
+        dp[mt] = mfma_32x32x16<F16>(as_ev8(vsb[kread + mt * 32 * kKRow + 2 * st]), df[st], dp[mt]);
+      }
+    const int valid = (d & 127) + 1;
+    // dS^T pairs, grouped by 16-key step cc (keys 16cc + 8*half + 0..7)
+    uint32_t dsw[4][4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        float d2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = 8 * (cc % 2) + t + u;
+          const int key = 16 * cc + 8 * half + t + u;
+          const float p = key < valid
+                              ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2, -lse_l2))
+                              : 0.f;
+          d2[u] = p * (dp[cc / 2][jj] - dq_row);
+        }
+        dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
+      }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
+                                                       dsw[cc][3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma_32x32x16<F16>(as_ev8(ktsb[ktread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+    }
+  };
+
   int64_t beg, end;
   row_bounds(row_ptr, uniform_k, nnz, r, beg, end);
-  for (int64_t e = beg; e < end; ++e) {
-    const int j = col[e];
-    if (j < 0 || j >= g.nb) continue;
-    const int cj = block_count(g, j);
-    for (int sub = 0; sub * kKvChunk < cj; ++sub) {
-      const int64_t chunk = int64_t(j) * cpb + sub;
-      __syncthreads();  // every wave is done with the previous sub-tile
-      copy_tile<NW, kKChunks>(kbase + chunk * kUnits, ks, wave, lane, true);
-      copy_tile<NW, kKChunks>(vbase + chunk * kUnits, vs, wave, lane, true);
-      copy_tile<NW, kVChunks>(ktbase + chunk * kUnits, kts, wave, lane, false);
+  for (int64_t e0 = beg; e0 < end; e0 += kPassEntries) {
+    const int m = int(min(int64_t(kPassEntries), end - e0));
+    for (int x = tid; x < m; x += kThreads) {
+      const int j = col[e0 + x];
+      esc[x] = (j >= 0 && j < g.nb) ? (block_count(g, j) + kKvChunk - 1) / kKvChunk : 0;
+    }
+    __syncthreads();
+    scan_counts(esc, m, &ntl, wave, lane);
+    __syncthreads();
+    for (int x = tid; x < m; x += kThreads) {
+      const int j = col[e0 + x];
+      if (j >= 0 && j < g.nb) {
+        const int cj = block_count(g, j);
+        for (int sub = 0; sub * kKvChunk < cj; ++sub)
+          tl[esc[x] + sub] = ((j * cpb + sub) << 7) | (min(kKvChunk, cj - sub * kKvChunk) - 1);
+      }
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(ntl);
+    if (T == 0) continue;
+    issue(__builtin_amdgcn_readfirstlane(tl[0]), ks0, vs0, kts0);
+    wait_copies();
+    __syncthreads();
+    for (int n = 0; n < T; n += 2) {
+      const int d0 = __builtin_amdgcn_readfirstlane(tl[n]);
+      const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
+      if (n + 1 < T) issue(d1, ks1, vs1, kts1);
+      compute(d0, ks0, vs0, kts0);
       wait_copies();
       __syncthreads();
-      if (!active) continue;
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int j2 = 0; j2 < 16; ++j2) s[mt][j2] = dp[mt][j2] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = mfma_32x32x16<F16>(as_ev8(ks[kread + mt * 32 * kKRow + 2 * st]), qf[st], s[mt]);
-          dp[mt] = mfma_32x32x16<F16>(as_ev8(vs[kread + mt * 32 * kKRow + 2 * st]), df[st], dp[mt]);
-        }
-      const int valid = min(kKvChunk, cj - sub * kKvChunk);
-      // dS^T pairs, grouped by 16-key step cc (keys 16cc + 8*half + 0..7)
-      uint32_t dsw[4][4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float d2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jj = 8 * (cc % 2) + t + u;
-            const int key = 16 * cc + 8 * half + t + u;
-            const float p = key < valid
-                                ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2, -lse_l2))
-                                : 0.f;
-            d2[u] = p * (dp[cc / 2][jj] - dq_row);
-          }
-          dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
-        }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
-                                                         dsw[cc][3]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          acc[dt] = mfma_32x32x16<F16>(as_ev8(kts[ktread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
-      }
+      if (n + 1 >= T) break;
+      if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), ks0, vs0, kts0);
+      compute(d1, ks1, vs1, kts1);
+      wait_copies();
+      __syncthreads();
     }
   }
   // dQ rows; pad query rows are written as zero
@@ -309,19 +390,29 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ tlist, const int32_t* __restrict__ tcount,
     uint4* __restrict__ grad, VsaGeom g, float scale_log2, float scale) {
-  // A operand of the first product(s): query rows (Q, and dO for dK); A of the
-  // accumulation: d rows (dO^T for dV, Q^T for dK)
-  __shared__ __align__(16) uint4 qsh[kKUnits];
-  __shared__ __align__(16) uint4 dsh[DK ? kKUnits : 1];
-  __shared__ __align__(16) uint4 tsh[kVUnits];
-  __shared__ float lse_sh[kKvChunk], d_sh[kKvChunk];
+  constexpr int kThreads = NW * 64;
+  constexpr int kPassTiles = kPassEntries * (NW / 2);
+  // two buffer sets.  A operand of the first product(s): query rows (Q, and
+  // dO for dK); A of the accumulation: d rows (dO^T for dV, Q^T for dK)
+  __shared__ __align__(16) uint4 qs0[kKUnits];
+  __shared__ __align__(16) uint4 ds0[DK ? kKUnits : 1];
+  __shared__ __align__(16) uint4 ts0[kVUnits];
+  __shared__ __align__(16) uint4 qs1[kKUnits];
+  __shared__ __align__(16) uint4 ds1[DK ? kKUnits : 1];
+  __shared__ __align__(16) uint4 ts1[kVUnits];
+  __shared__ float lse_sh[2][kKvChunk], d_sh[2][kKvChunk];
+  __shared__ int tl[kPassTiles];
+  __shared__ float tm[kPassTiles];  // multiplicity of each sub-tile's query block
+  __shared__ int esc[kPassEntries];
+  __shared__ int ntl;
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
   const int64_t c = xcd_remap(blockIdx.x, ncols);
   const int j = int(c % g.nb);
   const int64_t bh = c / g.nb;
   const int cj = block_count(g, j);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  const int lane = threadIdx.x % 64, half = lane / 32, l32 = lane & 31;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
   const int key = wave * 32 + l32;
   const bool active = wave * 32 < cj;
   const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
@@ -345,70 +436,103 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   const uint4* const tbase = (DK ? qt : dot) + bh * (g.npad / kKvChunk) * kUnits;
   const int cpb = g.vol / kKvChunk;
   const int qread = l32 * kKRow + half, tread = l32 * kVRow + half;
-  const int n = tcount[c];
-  const int32_t* list = tlist + c * int64_t(g.nb);
-  for (int e = 0; e < n; ++e) {
-    const int32_t ent = list[e];
-    const int i = ent & 0xffff;
-    const float mult = float(uint32_t(ent) >> 16);
-    const int cq = block_count(g, i);
-    for (int sub = 0; sub * kKvChunk < cq; ++sub) {
-      const int64_t chunk = int64_t(i) * cpb + sub;
-      const int nq = min(kKvChunk, cq - sub * kKvChunk);
-      __syncthreads();
-      copy_tile<NW, kKChunks>(qbase + chunk * kUnits, qsh, wave, lane, true);
-      if constexpr (DK) copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsh, wave, lane, true);
-      copy_tile<NW, kVChunks>(tbase + chunk * kUnits, tsh, wave, lane, false);
-      if (threadIdx.x < kKvChunk) {
-        const int64_t row = bh * g.npad + chunk * kKvChunk + threadIdx.x;
-        const bool ok = int(threadIdx.x) < nq;
-        lse_sh[threadIdx.x] = ok ? lse[row] * kLog2e : INFINITY;
-        d_sh[threadIdx.x] = ok ? dsum[row] : 0.f;
+
+  // copies of one query sub-tile and its lse / D (threads 0..63, plain loads)
+  auto issue = [&](int d, uint4* qsb, uint4* dsb, uint4* tsb, int set) {
+    const int64_t chunk = d >> 7;
+    copy_tile<NW, kKChunks>(qbase + chunk * kUnits, qsb, wave, lane, true);
+    if constexpr (DK) copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsb, wave, lane, true);
+    copy_tile<NW, kVChunks>(tbase + chunk * kUnits, tsb, wave, lane, false);
+    if (tid < kKvChunk) {
+      const int64_t row = bh * g.npad + chunk * kKvChunk + tid;
+      const bool ok = tid <= (d & 127);
+      lse_sh[set][tid] = ok ? lse[row] * kLog2e : INFINITY;
+      d_sh[set][tid] = ok ? dsum[row] : 0.f;
+    }
+  };
+  auto compute = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
+    if (!active) return;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) s[mt][jj] = dp[mt][jj] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        s[mt] = mfma_32x32x16<F16>(as_ev8(qsb[qread + mt * 32 * kKRow + 2 * st]), kf[st], s[mt]);
+        if constexpr (DK)
+          dp[mt] = mfma_32x32x16<F16>(as_ev8(dsb[qread + mt * 32 * kKRow + 2 * st]), vf[st],
+                                      dp[mt]);
       }
+    // B operand of the accumulation, by 16-query step cc
+    uint32_t bw[4][4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        float x2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = 8 * (cc % 2) + t + u;
+          const int qi = query_of(cc / 2, jj, half);
+          // pad keys of this block take no part (their rows are also stored as 0)
+          const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
+                                                                 -lse_sh[set][qi])) * mult
+                                   : 0.f;
+          x2[u] = DK ? p * (dp[cc / 2][jj] - d_sh[set][qi]) : p;
+        }
+        bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
+      }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
+                                                       bw[cc][3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma_32x32x16<F16>(as_ev8(tsb[tread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+    }
+  };
+
+  const int nent = tcount[c];
+  const int32_t* list = tlist + c * int64_t(g.nb);
+  for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
+    const int m = min(kPassEntries, nent - e0);
+    for (int x = tid; x < m; x += kThreads)
+      esc[x] = (block_count(g, list[e0 + x] & 0xffff) + kKvChunk - 1) / kKvChunk;
+    __syncthreads();
+    scan_counts(esc, m, &ntl, wave, lane);
+    __syncthreads();
+    for (int x = tid; x < m; x += kThreads) {
+      const int32_t ent = list[e0 + x];
+      const int qi = ent & 0xffff;
+      const float mult = float(uint32_t(ent) >> 16);
+      const int cq = block_count(g, qi);
+      for (int sub = 0; sub * kKvChunk < cq; ++sub) {
+        tl[esc[x] + sub] = ((qi * cpb + sub) << 7) | (min(kKvChunk, cq - sub * kKvChunk) - 1);
+        tm[esc[x] + sub] = mult;
+      }
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(ntl);
+    if (T == 0) continue;
+    issue(__builtin_amdgcn_readfirstlane(tl[0]), qs0, ds0, ts0, 0);
+    wait_copies();
+    __syncthreads();
+    for (int n = 0; n < T; n += 2) {
+      const float m0 = tm[n];
+      const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
+      const float m1 = tm[min(n + 1, T - 1)];
+      if (n + 1 < T) issue(d1, qs1, ds1, ts1, 1);
+      compute(m0, qs0, ds0, ts0, 0);
       wait_copies();
       __syncthreads();
-      if (!active) continue;
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) s[mt][jj] = dp[mt][jj] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          s[mt] = mfma_32x32x16<F16>(as_ev8(qsh[qread + mt * 32 * kKRow + 2 * st]), kf[st], s[mt]);
-          if constexpr (DK)
-            dp[mt] = mfma_32x32x16<F16>(as_ev8(dsh[qread + mt * 32 * kKRow + 2 * st]), vf[st],
-                                        dp[mt]);
-        }
-      // B operand of the accumulation, by 16-query step cc
-      uint32_t bw[4][4];
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float x2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jj = 8 * (cc % 2) + t + u;
-            const int qi = query_of(cc / 2, jj, half);
-            // pad keys of this block take no part (their rows are also stored as 0)
-            const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
-                                                                   -lse_sh[qi])) * mult
-                                     : 0.f;
-            x2[u] = DK ? p * (dp[cc / 2][jj] - d_sh[qi]) : p;
-          }
-          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
-        }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
-                                                         bw[cc][3]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          acc[dt] = mfma_32x32x16<F16>(as_ev8(tsh[tread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
-      }
+      if (n + 1 >= T) break;
+      if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), qs0, ds0, ts0, 0);
+      compute(m1, qs1, ds1, ts1, 1);
+      wait_copies();
+      __syncthreads();
     }
   }
   // rows of this wave's keys; pad key rows are written as zero
