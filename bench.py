@@ -85,9 +85,12 @@ def step_flops(plan, col_host, row_ptr_host, uniform_k):
 
 
 def attention_source_digest():
-    path = os.path.join(ROOT, "block_sparse_video_tile_amd", "csrc", "attention.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the sources the forward attention kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in ("attention.hip", "attn_common.h"):
+        with open(os.path.join(ROOT, "block_sparse_video_tile_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(path, workload, dtype):
