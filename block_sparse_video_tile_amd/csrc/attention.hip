@@ -163,6 +163,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // inside the sub-tile, the same for every sub-tile.  Chunk positions past
   // the buffer belong to copies that the lane predicate switches off.
   constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
+  // With 8 or 6 waves each issues at most 3 + 3 copies per sub-tile and they
+  // are placed inside the MFMA slots; with fewer waves (up to 9 + 9 copies
+  // each) predicated copies inside the slots make the compiler duplicate the
+  // slot code many times over, so those copies go at the top of the step.
+  constexpr bool kSlotCopies = kMaxK + kMaxV <= 6;
   uint32_t koff[kMaxK], voff[kMaxV];
 #pragma unroll
   for (int x = 0; x < kMaxK; ++x) {
@@ -285,6 +290,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       const uint4* const sk = src_of(kbase, d2);
       const uint4* const sv = src_of(vbase, d1);
       const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
+      if constexpr (!kSlotCopies) {
+        load_k(d2, kw);
+        load_v(d1, vw);
+      }
       if (active) {
         float mx = mx_pre;
         // mask keys past the block's valid count (only in its last sub-tile)
@@ -349,12 +358,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 #pragma unroll
         for (int u = 0; u < 32; ++u) {
           // this sub-tile's copies, K in the QK^T half and V in the PV half
+          if constexpr (kSlotCopies) {
 #pragma unroll
-          for (int x = 0; x < kMaxK; ++x)
-            if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
+            for (int x = 0; x < kMaxK; ++x)
+              if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
 #pragma unroll
-          for (int x = 0; x < kMaxV; ++x)
-            if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
+            for (int x = 0; x < kMaxV; ++x)
+              if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
+          }
           if (u < 16) {
             const int s = u / 2, mt = u % 2;
             if (u % 4 == 0) {
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         }
         l_run += rs0 + rs1;
         mx_pre = mxn;
-      } else {
+      } else if constexpr (kSlotCopies) {
         load_k(d2, kw);
         load_v(d1, vw);
       }
