@@ -76,6 +76,11 @@ WORKLOADS = {
     "tile64_tiny": Workload("tile64_tiny", (1, 1, 640), (1, 1, 64), 1, 2, 128, None,
                             seed=8, map_seed=1008, prefix_tiles=2, max_video_k=4,
                             zero_row_every=3),
+    # the other block volumes the kernels implement (128, 192, 3-D 64), one
+    # with two batches
+    "vol128_b2": Workload("vol128_b2", (8, 16, 16), (2, 8, 8), 2, 2, 128, 5, seed=9),
+    "vol192_padded": Workload("vol192_padded", (7, 13, 10), (3, 8, 8), 1, 2, 128, 5, seed=10),
+    "vol64_3d": Workload("vol64_3d", (4, 16, 16), (1, 8, 8), 1, 2, 128, 6, seed=11),
 }
 
 
