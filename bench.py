@@ -58,6 +58,9 @@ HBM_PEAK_GBS = 8000.0
 STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "scatter"]
 GATED_STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "coarse",
                 "scatter"]
+# gather-free path: block means read from the raster tensors, raster attention
+FUSED_STAGES = ["pool_q", "pool_k", "score_topk", "attention"]
+FUSED_GATED_STAGES = ["pool_q", "pool_k", "score_topk", "pool_v", "coarse", "attention"]
 
 
 def log(msg):
@@ -93,7 +96,7 @@ def attention_source_digest():
     return h.hexdigest()
 
 
-def recorded_traffic(path, workload, dtype):
+def recorded_traffic(path, workload, dtype, variant="blocked"):
     """HBM bytes per attention launch from the committed PMC record, or None.
 
     The record is only used when it was taken on this workload and on the
@@ -105,6 +108,7 @@ def recorded_traffic(path, workload, dtype):
     with open(path) as f:
         rec = json.load(f)
     if (rec.get("workload") != workload or rec.get("dtype", "bf16") != dtype
+            or rec.get("variant", "blocked") != variant
             or rec.get("kernel_source_sha256") != attention_source_digest()):
         return None
     return rec.get("bytes_per_launch")
@@ -146,6 +150,7 @@ def record_traffic(args):
                       "calibration_kib": cal, "calibration_dispatches": n_cal,
                       "calibration_factor": factor, "bytes_per_launch": att * 1024.0 * factor}
     rec = {"workload": args.workload, "dtype": args.dtype,
+           "variant": "raster" if args.fused else "blocked",
            "kernel_source_sha256": attention_source_digest(),
            "bytes_per_launch": out["fetch"]["bytes_per_launch"] + out["write"]["bytes_per_launch"],
            "fetch": out["fetch"], "write": out["write"], "calibration_copy_bytes": cal_bytes}
@@ -260,14 +265,22 @@ def main():
     ap.add_argument("--gated", action="store_true",
                     help="also run the gate-compress branch (pooled V, coarse attention, "
                          "gated scatter) with a synthetic gate")
+    ap.add_argument("--fused", action="store_true",
+                    help="gather-free path: pool Q and K from the raster tensors, score/top-k, "
+                         "raster attention writing the raster output (no gather or scatter)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--traffic-json",
-                    default=os.path.join(ROOT, "profiles", "attention_wan5b_k64_traffic.json"))
+    ap.add_argument("--traffic-json", default=None,
+                    help="PMC traffic record of the attention kernel (default: the one in "
+                         "profiles/ for the blocked or, with --fused, the raster kernel)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB")
     ap.add_argument("--record-traffic", nargs=4, metavar="CSV")
     ap.add_argument("--cal-mib", type=int, default=1024)
     args = ap.parse_args()
+    if args.traffic_json is None:
+        args.traffic_json = os.path.join(
+            ROOT, "profiles", "attention_raster_wan5b_k64_traffic.json" if args.fused
+            else "attention_wan5b_k64_traffic.json")
 
     if args.record_traffic:
         record_traffic(args)
@@ -298,14 +311,18 @@ def main():
         bench_backward(args, wl, plan, elem, dq, dk, dv)
         return
     log(f"[bench] {vsa.vsa_plan_describe(plan)}")
-    qb = torch.empty(plan.blocked_shape(), dtype=elem, device=dev)
-    kb = torch.empty_like(qb)
-    ob = torch.empty_like(qb)
-    vb = torch.empty(plan.blocked_vt_shape(), dtype=elem, device=dev)
+    if not args.fused:   # the gather-free path keeps no blocked copies
+        qb = torch.empty(plan.blocked_shape(), dtype=elem, device=dev)
+        kb = torch.empty_like(qb)
+        ob = torch.empty_like(qb)
+        vb = torch.empty(plan.blocked_vt_shape(), dtype=elem, device=dev)
     qp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=dev)
     kp = torch.empty_like(qp)
     out = torch.empty(plan.raster_shape(), dtype=elem, device=dev)
-    stages = GATED_STAGES if args.gated else STAGES
+    if args.fused:
+        stages = FUSED_GATED_STAGES if args.gated else FUSED_STAGES
+    else:
+        stages = GATED_STAGES if args.gated else STAGES
     if args.gated:
         vp = torch.empty_like(qp)
         oc = torch.empty_like(qp)
@@ -322,7 +339,33 @@ def main():
         uk, nnz = 0, col.numel()
     stream = torch.cuda.current_stream(dev)
 
+    def fused_step(ev=None):
+        def mark(n):
+            if ev is not None:
+                ev[n].record(stream)
+        mark(0)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_Q, dq, None, qp)
+        mark(1)
+        vsa.vsa_gather(plan, vsa.VSA_ROLE_K, dk, None, kp)
+        mark(2)
+        if wl.topk:
+            vsa.vsa_score_topk(plan, qp, kp, wl.topk, col)
+        mark(3)
+        if args.gated:
+            vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, None, vp)
+            mark(4)
+            vsa.vsa_compress_attn(plan, qp, kp, vp, oc)
+            mark(5)
+            vsa.vsa_block_sparse_attn_fwd_raster(plan, dq, dk, dv, rp_dev, col, uk, nnz, out,
+                                                 gate=gate, o_coarse=oc)
+        else:
+            vsa.vsa_block_sparse_attn_fwd_raster(plan, dq, dk, dv, rp_dev, col, uk, nnz, out)
+        mark(len(stages))
+
     def step(ev=None):
+        if args.fused:
+            return fused_step(ev)
+
         def mark(n):
             if ev is not None:
                 ev[n].record(stream)
@@ -370,7 +413,8 @@ def main():
     t_attn = float(np.mean(stage_ms["attention"]))
     attn_tflops = f_valid / (t_attn * 1e-3) / 1e12
     value = f_valid / (ms_per_step * 1e-3) / 1e12
-    traffic = recorded_traffic(args.traffic_json, wl.name, args.dtype)
+    traffic = recorded_traffic(args.traffic_json, wl.name, args.dtype,
+                               "raster" if args.fused else "blocked")
     result = {
         "metric": "effective TFLOP/s (selected blocks) + ms/layer, 27280 tok, topk=64, 1 GPU",
         "value": round(value, 3),
@@ -389,7 +433,8 @@ def main():
                    "block_size": list(wl.block_size), "seq_len": wl.seq_len,
                    "heads": wl.heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "topk": wl.topk, "num_blocks": plan.num_blocks,
-                   "gate_compress": bool(args.gated), "parallelism": "single GPU"},
+                   "gate_compress": bool(args.gated), "gather_free": bool(args.fused),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_16BIT_PEAK_TFLOPS, 4),

@@ -23,7 +23,9 @@ __all__ = [
     "vsa_plan_block_counts", "vsa_gather", "vsa_scatter", "vsa_score_topk",
     "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_bwd_workspace_size",
     "vsa_block_sparse_attn_bwd", "vsa_compress_attn", "vsa_scatter_gated",
-    "vsa_forward_workspace_size", "vsa_forward", "vsa_status_string", "vsa_last_error",
+    "vsa_forward_workspace_size", "vsa_forward", "vsa_block_sparse_attn_fwd_raster",
+    "vsa_forward_fused_workspace_size", "vsa_forward_fused", "vsa_status_string",
+    "vsa_last_error",
 ]
 
 VSA_OK, VSA_ERR_INVALID_ARGUMENT, VSA_ERR_UNSUPPORTED, VSA_ERR_HIP = 0, 1, 2, 3
@@ -79,6 +81,11 @@ _SIGS = {
     "vsa_compress_attn": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
     "vsa_scatter_gated": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
     "vsa_forward": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P], ctypes.c_int),
+    "vsa_block_sparse_attn_fwd_raster": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
+                                          _P, _P, _P, _P, _P], ctypes.c_int),
+    "vsa_forward_fused_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "vsa_forward_fused": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
+                          ctypes.c_int),
     "vsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "vsa_last_error": ([], ctypes.c_char_p),
 }
@@ -318,6 +325,37 @@ def vsa_block_sparse_attn_fwd(plan: Plan, q_blk, k_blk, v_blk, row_ptr, col_idx,
         _stream(stream, q_blk, o_blk)))
 
 
+def vsa_block_sparse_attn_fwd_raster(plan: Plan, q, k, v, row_ptr, col_idx, uniform_k: int,
+                                     nnz: int, o_raster, lse=None, stream=None, gate=None,
+                                     o_coarse=None):
+    """Block-sparse attention on raster [B,S,NH,D] tensors (no gather/scatter);
+    with gate and o_coarse the rows are written as vsa_scatter_gated writes them."""
+    n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
+    rows = plan.num_rows()
+    et = plan.torch_dtype()
+    _check(load_library().vsa_block_sparse_attn_fwd_raster(
+        plan.handle, _ptr(q, n_raster, et, "q"), _ptr(k, n_raster, et, "k"),
+        _ptr(v, n_raster, et, "v"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
+        _ptr(col_idx, int(nnz), _i32(), "col_idx"), int(uniform_k), int(nnz),
+        _ptr(gate, n_raster, et, "gate"),
+        _ptr(o_coarse, plan.info["pooled_elems"], _f32(), "o_coarse"),
+        _ptr(o_raster, n_raster, et, "o_raster"),
+        _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
+        _stream(stream, q, o_raster)))
+
+
+def vsa_forward_fused_workspace_size(plan: Plan) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().vsa_forward_fused_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def vsa_forward_fused(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
+                      stream=None, gate=None):
+    """vsa_forward_fused: the gather-free hot path (raster in, raster out)."""
+    vsa_forward(plan, q, k, v, out, workspace, col_idx_out, lse, stream, gate, fused=True)
+
+
 def vsa_forward_workspace_size(plan: Plan) -> int:
     n = ctypes.c_size_t()
     _check(load_library().vsa_forward_workspace_size(plan.handle, ctypes.byref(n)))
@@ -369,10 +407,12 @@ def vsa_scatter_gated(plan: Plan, o_blk, o_coarse, gate, o_raster, stream=None):
 
 
 def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None, stream=None,
-                gate=None):
+                gate=None, fused=False):
+    """The whole hot path, raster in and out; fused=True calls vsa_forward_fused
+    (no gather or scatter passes) with its own, smaller workspace."""
     import torch
     n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
-    ws_bytes = vsa_forward_workspace_size(plan)
+    ws_bytes = (vsa_forward_fused_workspace_size if fused else vsa_forward_workspace_size)(plan)
     if isinstance(workspace, torch.Tensor):
         if workspace.numel() * workspace.element_size() < ws_bytes:
             raise ValueError(f"workspace: fewer than {ws_bytes} bytes")
@@ -380,7 +420,8 @@ def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
     else:
         ws_ptr, ws_len = int(workspace), ws_bytes
     et = plan.torch_dtype()
-    _check(load_library().vsa_forward(
+    lib = load_library()
+    _check((lib.vsa_forward_fused if fused else lib.vsa_forward)(
         plan.handle, _ptr(q, n_raster, et, "q"), _ptr(k, n_raster, et, "k"),
         _ptr(v, n_raster, et, "v"), _ptr(gate, n_raster, et, "gate"),
         _ptr(out, n_raster, et, "out"), ws_ptr, ws_len,

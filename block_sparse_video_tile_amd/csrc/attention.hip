@@ -45,6 +45,26 @@
 //   the keys of PV step c are the contiguous run 16c + 8*(l/32) + 0..7 and the
 //   matching V^T operand is one 16-byte LDS read.
 //
+// Raster variant (no gather or scatter passes): Q, K, V are read and O is
+// written in the raster layout [B,S,NH,D] by block index arithmetic.  A
+// block's valid tokens, taken in raster order inside its box, lie at token
+// offsets from the box origin that depend only on which of the box's three
+// extents the grid edge cuts, so each workgroup first tabulates those offsets
+// for the 8 possible edge classes in LDS; a sub-tile descriptor then carries
+// the block's origin token, class and sub-tile index, and each lane's source
+// offset for a copy is one LDS table read.  Pad rows of a partial sub-tile
+// re-read a valid row (masked as before).  V stays token-major in LDS (64 key
+// rows of 256 B plus a 32-byte pad) and the PV operands are read with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes,
+// lane i receives element i%4 of the 8-byte rows addressed by lanes
+// 4e + i/4 (e = 0..3), so two such reads give a lane the 8 consecutive keys of
+// one d column that the V^T layout holds as one 16-byte read.  A 32-lane
+// half of such a read covers 4 key rows; so that it touches 8 distinct
+// 32-byte bank groups, the MFMA row m of O^T tile dt holds
+// d = 64*(m/16) + 16*dt + m%16 (lanes 16..31 read 128 bytes further along
+// the row) instead of 32*dt + m.  Rounding and product order are those of the
+// blocked kernel: both write identical O.
+//
 // Online softmax (exact up to rounding): running reference max m and sum l per
 // query in fp32, p = exp2(s*log2(e)/sqrt(D) - m*log2(e)/sqrt(D)) on the
 // transcendental unit, l summed from the fp32 p, P rounded to bf16 (fp16 for
@@ -70,6 +90,51 @@ using namespace tile;
 // c-th 64-token chunk, so the chunk index addresses both.
 constexpr int kListEntries = 1024;
 
+// Raster sub-tile descriptor:
+//   origin token of the block << 11 | edge class << 8 | sub-tile << 6 | (valid keys - 1)
+// (origin < 2^21 tokens; the host checks it).
+constexpr int kRasterVRow = 18;  // raster V tile row: 16 units of data + 2 pad units (288 B)
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (see the header comment for its lane layout).
+__device__ inline v4i16 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+}
+
+// Origin token (raster index of the box corner) and edge class of block j:
+// bit 2 / 1 / 0 set when the block is the last one along T / H / W.
+__device__ inline void block_origin_class(const VsaGeom& g, int j, int& origin, int& cls) {
+  const int plane = g.nbh * g.nbw;
+  const int it = j / plane;
+  const int rem = j - it * plane;
+  const int ih = rem / g.nbw;
+  const int iw = rem - ih * g.nbw;
+  origin = (it * g.bt * g.H + ih * g.bh) * g.W + iw * g.bw;
+  cls = (it == g.nbt - 1 ? 4 : 0) | (ih == g.nbh - 1 ? 2 : 0) | (iw == g.nbw - 1 ? 1 : 0);
+}
+
+// soff[c*VOL + s]: offset, in 16-byte units of the raster tensor, of the s-th
+// valid token of a block of edge class c from its origin token (slots past
+// the valid count repeat the last valid token).
+template <int VOL>
+__device__ inline void build_slot_table(const VsaGeom& g, uint32_t* soff, int tid, int nthreads) {
+  for (int idx = tid; idx < 8 * VOL; idx += nthreads) {
+    const int c = idx / VOL, s = idx % VOL;
+    const int ct = (c & 4) ? g.T - (g.nbt - 1) * g.bt : g.bt;
+    const int ch = (c & 2) ? g.H - (g.nbh - 1) * g.bh : g.bh;
+    const int cw = (c & 1) ? g.W - (g.nbw - 1) * g.bw : g.bw;
+    const int sc = min(s, ct * ch * cw - 1);
+    const int dw = sc % cw;
+    const int r2 = sc / cw;
+    const int dh = r2 % ch;
+    const int dt = r2 / ch;
+    soff[idx] = ((uint32_t(dt) * uint32_t(g.H) + uint32_t(dh)) * uint32_t(g.W) + uint32_t(dw)) *
+                uint32_t(g.heads) * 16u;
+  }
+}
+
 // Keep the scheduler from moving work across this point: the main loop is
 // laid out slot by slot (one MFMA, its operand prefetch and a share of the
 // softmax VALU work per slot) and each slot is fenced.
@@ -90,12 +155,15 @@ __device__ inline float tile_max(const f32x16 (&st)[2]) {
   return mx;
 }
 
-template <int NW, bool F16>
+// RASTER = false: q, k, o blocked [B,NH,Npad,D], v blocked-V^T.
+// RASTER = true: q, k, v, o raster [B,S,NH,D]; with `gate` (raster) the
+// output is O + gate * oc[block] (oc fp32 [B,NH,nb,D]), as the gated scatter.
+template <int NW, bool F16, bool RASTER>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ vt,
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
-    int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, VsaGeom g, float scale_log2,
-    float scale) {
+    int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, const uint4* __restrict__ gate,
+    const float* __restrict__ oc, VsaGeom g, float scale_log2, float scale) {
   static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits), "O staging must fit in LDS");
   const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
   // Sub-tile buffers.  K runs one sub-tile ahead of V: while sub-tile n is
@@ -114,6 +182,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   __shared__ int tlist[kListTiles];
   __shared__ int escan[kListEntries];
   __shared__ int ntiles_sh;
+  constexpr int kVol = 32 * NW;
+  __shared__ uint32_t soff[RASTER ? 8 * kVol : 1];
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   const int64_t r = xcd_remap(blockIdx.x, nrows);
@@ -140,9 +210,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int len = int(end - beg);
 
   const int64_t qk_row0 = bh * g.npad + int64_t(i) * g.vol;  // first token row of block i
+  // raster: first unit of head h in batch b, the token stride, block i's origin and class
+  int64_t head0 = 0, rs = 0;
+  int origin_i = 0, cls_i = 0;
+  if constexpr (RASTER) {
+    head0 = ((bh / g.heads) * g.S * g.heads + bh % g.heads) * 16;
+    rs = int64_t(g.heads) * 16;
+    block_origin_class(g, i, origin_i, cls_i);
+    build_slot_table<kVol>(g, soff, tid, kThreads);
+    __syncthreads();
+  }
   ev8 qf[8];
   if (active) {
-    const uint4* qsrc = q + (qk_row0 + qrow) * 16;
+    const uint4* qsrc;
+    if constexpr (RASTER)
+      qsrc = q + head0 + origin_i * rs + soff[cls_i * kVol + min(qrow, cq - 1)];
+    else
+      qsrc = q + (qk_row0 + qrow) * 16;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = as_ev8(qsrc[2 * s + half]);
   }
@@ -155,8 +239,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const uint4* const kbase = k + bh * g.npad * 16;
-  const uint4* const vbase = vt + bh * (g.npad / kKvChunk) * kUnits;
+  const uint4* const kbase = RASTER ? k + head0 : k + bh * g.npad * 16;
+  const uint4* const vbase = RASTER ? v + head0 : v + bh * (g.npad / kKvChunk) * kUnits;
   const int chunks_per_block = g.vol / kKvChunk;
   // Copy x of a sub-tile moves LDS chunk wave + x*NW (64 consecutive 16-byte
   // units of the padded buffer); koff/voff are this lane's source offsets
@@ -168,41 +252,72 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // each) predicated copies inside the slots make the compiler duplicate the
   // slot code many times over, so those copies go at the top of the step.
   constexpr bool kSlotCopies = kMaxK + kMaxV <= 6;
+  // Blocked: koff/voff are the lane's source offsets inside a sub-tile.
+  // Raster: krow/vrow are the sub-tile rows (keys) the lane copies and
+  // kun/vun the 16-byte units inside the token row; the row's offset comes
+  // from the slot table.  The pad units of a row re-read units of that row.
+  constexpr int kVRowX = RASTER ? kRasterVRow : kVRow;
   uint32_t koff[kMaxK], voff[kMaxV];
+  int krow[kMaxK], vrow[kMaxV];
 #pragma unroll
   for (int x = 0; x < kMaxK; ++x) {
     const int pos = min((wave + x * NW) * 64 + lane, kKUnits - 1);
     const int row = pos / kKRow, unit = pos % kKRow;
-    koff[x] = kappa(row) * 16 + (unit < 16 ? unit : 0);
+    koff[x] = RASTER ? (unit < 16 ? unit : 0) : kappa(row) * 16 + (unit < 16 ? unit : 0);
+    krow[x] = kappa(row);
   }
 #pragma unroll
   for (int x = 0; x < kMaxV; ++x) {
     const int pos = min((wave + x * NW) * 64 + lane, kVUnits - 1);
-    const int row = pos / kVRow, unit = pos % kVRow;
-    voff[x] = row * 8 + (unit < 8 ? unit : 0);
+    const int row = pos / kVRowX, unit = pos % kVRowX;
+    if constexpr (RASTER) voff[x] = unit < 16 ? unit : unit - 16;
+    else voff[x] = row * 8 + (unit < 8 ? unit : 0);
+    vrow[x] = row;
   }
-  auto src_of = [](const uint4* base, int desc) { return base + int64_t(desc >> 7) * kUnits; };
+  auto src_of = [&](const uint4* base, int desc) {
+    if constexpr (RASTER) return base + int64_t(uint32_t(desc) >> 11) * rs;
+    else return base + int64_t(desc >> 7) * kUnits;
+  };
+  // source offsets of this lane's copies of the sub-tile `desc`
+  auto k_offsets = [&](int desc, uint32_t (&ko)[kMaxK]) {
+    const int tb = ((desc >> 8) & 7) * kVol + ((desc >> 6) & 3) * 64;
+#pragma unroll
+    for (int x = 0; x < kMaxK; ++x) ko[x] = RASTER ? soff[tb + krow[x]] + koff[x] : koff[x];
+  };
+  auto v_offsets = [&](int desc, uint32_t (&vo)[kMaxV]) {
+    const int tb = ((desc >> 8) & 7) * kVol + ((desc >> 6) & 3) * 64;
+#pragma unroll
+    for (int x = 0; x < kMaxV; ++x) vo[x] = RASTER ? soff[tb + vrow[x]] + voff[x] : voff[x];
+  };
   // The predicate is evaluated per lane (exec mask) rather than as a branch,
   // so copies can sit inside the scheduled slots without splitting them.
-  auto copy_k = [&](const uint4* src, int x, uint4* dst) {
-    if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, koff[x], dst + (wave + x * NW) * 64);
+  auto copy_k = [&](const uint4* src, uint32_t off, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, off, dst + (wave + x * NW) * 64);
   };
-  auto copy_v = [&](const uint4* src, int x, uint4* dst) {
-    if (tid / 64 + x * NW < kVChunks) wave_copy_to_lds(src, voff[x], dst + (wave + x * NW) * 64);
+  auto copy_v = [&](const uint4* src, uint32_t off, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kVChunks) wave_copy_to_lds(src, off, dst + (wave + x * NW) * 64);
   };
   auto load_k = [&](int desc, uint4* dst) {
+    uint32_t ko[kMaxK];
+    k_offsets(desc, ko);
 #pragma unroll
-    for (int x = 0; x < kMaxK; ++x) copy_k(src_of(kbase, desc), x, dst);
+    for (int x = 0; x < kMaxK; ++x) copy_k(src_of(kbase, desc), ko[x], x, dst);
   };
   auto load_v = [&](int desc, uint4* dst) {
+    uint32_t vo[kMaxV];
+    v_offsets(desc, vo);
 #pragma unroll
-    for (int x = 0; x < kMaxV; ++x) copy_v(src_of(vbase, desc), x, dst);
+    for (int x = 0; x < kMaxV; ++x) copy_v(src_of(vbase, desc), vo[x], x, dst);
   };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // per-lane operand bases: K row l32 (+ half unit), V^T row l32 (+ half unit)
   const int kread = l32 * kKRow + half;
   const int vread = l32 * kVRow + half;
+  // raster: byte offset of this lane's transposing V read: key row
+  // 8*half + e (e = (lane%16)/4), d column 64*((lane/16)%2) + 4*(lane%4)
+  const int vtr = (8 * half + (lane & 15) / 4) * (kRasterVRow * 16) +
+                  (64 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   f32x16 sa[2], sb[2];
   float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
 
@@ -245,9 +360,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       if (j >= 0 && j < g.nb) {
         const int cj = block_count(g, j);
         const int off = escan[e];
-        for (int sub = 0; sub * kKvChunk < cj; ++sub)
-          tlist[off + sub] =
-              ((j * chunks_per_block + sub) << 7) | (min(kKvChunk, cj - sub * kKvChunk) - 1);
+        if constexpr (RASTER) {
+          int origin, cls;
+          block_origin_class(g, j, origin, cls);
+          for (int sub = 0; sub * kKvChunk < cj; ++sub)
+            tlist[off + sub] = int((uint32_t(origin) << 11) | uint32_t(cls << 8) |
+                                   uint32_t(sub << 6) |
+                                   uint32_t(min(kKvChunk, cj - sub * kKvChunk) - 1));
+        } else {
+          for (int sub = 0; sub * kKvChunk < cj; ++sub)
+            tlist[off + sub] =
+                ((j * chunks_per_block + sub) << 7) | (min(kKvChunk, cj - sub * kKvChunk) - 1);
+        }
       }
     }
     __syncthreads();
@@ -290,14 +414,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       const uint4* const sk = src_of(kbase, d2);
       const uint4* const sv = src_of(vbase, d1);
       const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
+      uint32_t ko[kMaxK], vo[kMaxV];
       if constexpr (!kSlotCopies) {
         load_k(d2, kw);
         load_v(d1, vw);
+      } else {
+        k_offsets(d2, ko);
+        v_offsets(d1, vo);
       }
       if (active) {
         float mx = mx_pre;
         // mask keys past the block's valid count (only in its last sub-tile)
-        const int valid = (d0 & 127) + 1;
+        const int valid = (d0 & (RASTER ? 63 : 127)) + 1;
         if (valid < kKvChunk) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
@@ -346,7 +474,17 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
         };
         auto read_v = [&](int w) {  // operand of PV slot w
-          opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+          if constexpr (RASTER) {
+            // keys 16*(w/4) + 8*half + 0..7 of d column
+            // 64*(l32/16) + 16*(w%4) + l32%16
+            const char* bp = reinterpret_cast<const char*>(vn) + vtr +
+                             (16 * (w / 4)) * (kRasterVRow * 16) + 32 * (w % 4);
+            const v4i16 lo = lds_read_tr16(bp);
+            const v4i16 hi = lds_read_tr16(bp + 4 * (kRasterVRow * 16));
+            opv[w % 8] = __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          } else {
+            opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+          }
         };
 #pragma unroll
         for (int u = 0; u < 4; ++u) read_k(u);
@@ -361,10 +499,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           if constexpr (kSlotCopies) {
 #pragma unroll
             for (int x = 0; x < kMaxK; ++x)
-              if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
+              if (u == 1 + (x * 16) / kMaxK) copy_k(sk, ko[x], x, kw);
 #pragma unroll
             for (int x = 0; x < kMaxV; ++x)
-              if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
+              if (u == 17 + (x * 16) / kMaxV) copy_v(sv, vo[x], x, vw);
           }
           if (u < 16) {
             const int s = u / 2, mt = u % 2;
@@ -412,8 +550,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         l_run += rs0 + rs1;
         mx_pre = mxn;
       } else if constexpr (kSlotCopies) {
-        load_k(d2, kw);
-        load_v(d1, vw);
+#pragma unroll
+        for (int x = 0; x < kMaxK; ++x) copy_k(sk, ko[x], x, kw);
+#pragma unroll
+        for (int x = 0; x < kMaxV; ++x) copy_v(sv, vo[x], x, vw);
       }
       wait_loads();
       __syncthreads();
@@ -448,21 +588,61 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      // registers 4jj..4jj+3 hold d = 32dt + 8jj + 4*half + 0..3
+      // registers 4jj..4jj+3 hold O^T rows m = 8jj + 4*half + 0..3, i.e.
+      // d = 32dt + m (blocked) or 64*(m/16) + 16dt + m%16 (raster)
+      const int d0 = RASTER ? 64 * (jj / 2) + 16 * dt + 8 * (jj % 2) + 4 * half
+                            : dt * 32 + 8 * jj + 4 * half;
       const uint2 w = make_uint2(
           pack2<F16>(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv),
           pack2<F16>(oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv));
-      ostage[l32 * (kORow * 2) + (dt * 32 + 8 * jj + 4 * half) / 4] = w;
+      ostage[l32 * (kORow * 2) + d0 / 4] = w;
     }
   // the staging area of wave w is only touched by wave w
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint4* const odst = o + (qk_row0 + wave * 32) * 16;
+  if constexpr (RASTER) {
+    // rows go to their raster tokens; pad rows are dropped.  With a gate the
+    // row is O + gate * oc[block i] in fp32, rounded once (as the gated scatter).
+    const int unit = lane & 15;
+    float c[8];
+    if (gate != nullptr) {
+      const float4* cp = reinterpret_cast<const float4*>(oc + (bh * g.nb + i) * kHeadDim + unit * 8);
+      const float4 c0 = cp[0], c1 = cp[1];
+      c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+      c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+    }
+    const int64_t obase = head0 + origin_i * rs + unit;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int rr = p * 4 + lane / 16;
-    odst[rr * 16 + (lane & 15)] = srows[rr * kORow + (lane & 15)];
+    for (int p = 0; p < 8; ++p) {
+      const int rr = p * 4 + lane / 16;
+      const int slot = wave * 32 + rr;
+      if (slot < cq) {
+        const int64_t at = obase + soff[cls_i * kVol + slot];
+        uint4 val = srows[rr * kORow + unit];
+        if (gate != nullptr) {
+          const uint4 gv = gate[at];
+          const uint32_t ow[4] = {val.x, val.y, val.z, val.w};
+          const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = pack2<F16>(fmaf(elem_to_f32<F16>(gw[e] & 0xffffu), c[2 * e],
+                                   elem_to_f32<F16>(ow[e] & 0xffffu)),
+                              fmaf(elem_to_f32<F16>(gw[e] >> 16), c[2 * e + 1],
+                                   elem_to_f32<F16>(ow[e] >> 16)));
+          val = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        o[at] = val;
+      }
+    }
+  } else {
+    uint4* const odst = o + (qk_row0 + wave * 32) * 16;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const int rr = p * 4 + lane / 16;
+      odst[rr * 16 + (lane & 15)] = srows[rr * kORow + (lane & 15)];
+    }
   }
   if (lse != nullptr && half == 0) {
     lse[qk_row0 + qrow] =
@@ -470,30 +650,32 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
 }
 
-template <int NW, bool F16>
-hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* vt,
+template <int NW, bool F16, bool RASTER>
+hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
-                     void* o, float* lse, hipStream_t s) {
+                     void* o, float* lse, const void* gate, const float* oc, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
-                     static_cast<const uint4*>(q), static_cast<const uint4*>(k),
-                     static_cast<const uint4*>(vt), row_ptr, col, uniform_k, nnz,
-                     static_cast<uint4*>(o), lse, g, scale_log2, scale);
+  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16, RASTER>), dim3(unsigned(rows)), dim3(NW * 64), 0,
+                     s, static_cast<const uint4*>(q), static_cast<const uint4*>(k),
+                     static_cast<const uint4*>(v), row_ptr, col, uniform_k, nnz,
+                     static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, g,
+                     scale_log2, scale);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
-                           const int32_t* row_ptr, const int32_t* col, int uniform_k,
-                           int64_t nnz, void* o, float* lse, hipStream_t s) {
+template <bool RASTER>
+hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void* v,
+                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
+                      void* o, float* lse, const void* gate, const float* oc, hipStream_t s) {
   auto launch = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
     return g.dtype == VSA_DTYPE_FP16
-               ? launch_nw<NW, true>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s)
-               : launch_nw<NW, false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, s);
+               ? launch_nw<NW, true, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                             gate, oc, s)
+               : launch_nw<NW, false, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                              gate, oc, s);
   };
   switch (g.vol / 32) {
     case 2: return launch(std::integral_constant<int, 2>());
@@ -502,6 +684,22 @@ hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const
     case 8: return launch(std::integral_constant<int, 8>());
     default: return hipErrorInvalidValue;
   }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
+                           const int32_t* row_ptr, const int32_t* col, int uniform_k,
+                           int64_t nnz, void* o, float* lse, hipStream_t s) {
+  return launch_any<false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, nullptr, nullptr,
+                           s);
+}
+
+hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
+                                  const int32_t* row_ptr, const int32_t* col, int uniform_k,
+                                  int64_t nnz, void* o, float* lse, const void* gate,
+                                  const float* oc, hipStream_t s) {
+  return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, s);
 }
 
 }  // namespace vsa

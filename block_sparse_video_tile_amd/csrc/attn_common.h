@@ -44,6 +44,14 @@ __device__ inline uint32_t pack2(float a, float b) {
   }
 }
 
+// One 16-bit element (the low half of `u`) as fp32: bf16 is the upper half
+// of an fp32, fp16 converts exactly.
+template <bool F16>
+__device__ inline float elem_to_f32(uint32_t u) {
+  if constexpr (F16) return float(__builtin_bit_cast(_Float16, uint16_t(u)));
+  else return __uint_as_float(u << 16);
+}
+
 // Dispatch is round-robin over the 8 XCDs; give each XCD a contiguous run of rows.
 __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
   const int64_t per = n / 8, rem = n % 8;
@@ -72,10 +80,13 @@ constexpr int kORow = 17;               // epilogue O staging row: 272 B
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One wave copies 64 x 16 bytes from global memory straight into LDS: lane l
-// reads `src + off` and its 16 bytes land at `dst + 16*l`.
+// reads `src + off` and its 16 bytes land at `dst + 16*l`.  `src` is uniform
+// and the byte offset 16*off is formed in 32 bits (callers keep it below
+// 2^32), so the copy takes the scalar-base + 32-bit vector-offset form.
 __device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* dst) {
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + off),
-                                   (lds_ptr_t)(dst), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(
+      static_cast<const void*>(reinterpret_cast<const char*>(src) + off * 16u), (lds_ptr_t)(dst),
+      16, 0, 0);
 }
 
 }  // namespace tile

@@ -10,6 +10,7 @@
 // 16-bit elements, bf16 or fp16: the guide's "Verify routing and fallback"
 // admits both) is 16 lanes x 16 bytes.
 
+#include "attn_common.h"
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -61,7 +62,8 @@ __device__ inline float elem_hi(uint32_t w) {
   else return __uint_as_float(w & 0xffff0000u);
 }
 
-// Q/K: raster [B,S,NH,D] -> blocked [B,NH,Npad,D], optional fp32 block means.
+// Q/K: raster [B,S,NH,D] -> blocked [B,NH,Npad,D], optional fp32 block means
+// (or the means alone, for any of Q, K, V, when xb is null).
 // The copy moves raw 16-bit elements; only the means depend on the type.
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __restrict__ x,
@@ -78,8 +80,10 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
   const int unit = threadIdx.x % kUnitsPerRow;
   const int lt = threadIdx.x / kUnitsPerRow;  // token lane, 16 tokens per pass
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  uint4* dst = xb + (int64_t(bh) * g.npad + int64_t(beta) * g.vol) * kUnitsPerRow;
-  for (int r = lt; r < g.vol; r += kThreads / kUnitsPerRow) {
+  const int64_t dst0 = (int64_t(bh) * g.npad + int64_t(beta) * g.vol) * kUnitsPerRow;
+  // xb == nullptr: pooling only (reads the valid tokens, writes the means)
+  const int rows = xb != nullptr ? g.vol : box.cnt;
+  for (int r = lt; r < rows; r += kThreads / kUnitsPerRow) {
     uint4 val = make_uint4(0u, 0u, 0u, 0u);
     if (r < box.cnt) {
       const int64_t s = token_of(g, box, r);
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
       acc[4] += elem_lo<F16>(val.z); acc[5] += elem_hi<F16>(val.z);
       acc[6] += elem_lo<F16>(val.w); acc[7] += elem_hi<F16>(val.w);
     }
-    dst[int64_t(r) * kUnitsPerRow + unit] = val;
+    if (xb != nullptr) xb[dst0 + int64_t(r) * kUnitsPerRow + unit] = val;
   }
   if (pooled != nullptr) {
 #pragma unroll
@@ -102,13 +106,6 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
       pooled[(int64_t(bh) * g.nb + beta) * kHeadDim + threadIdx.x] = s / float(box.cnt);
     }
   }
-}
-
-// One 16-bit element (in the low half of `u`) as fp32.
-template <bool F16>
-__device__ inline float elem_f32(uint32_t u) {
-  if constexpr (F16) return float(__builtin_bit_cast(_Float16, uint16_t(u)));
-  else return __uint_as_float(u << 16);
 }
 
 // V: raster [B,S,NH,D] -> blocked-V^T [B,NH,Npad/64,D,64] (each 64-token
@@ -165,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restr
         const uint32_t lo = tile[ku * 8 + 2 * e][d];
         const uint32_t hi = tile[ku * 8 + 2 * e + 1][d];
         w[e] = lo | (hi << 16);
-        if (pooled != nullptr) acc += elem_f32<F16>(lo) + elem_f32<F16>(hi);
+        if (pooled != nullptr) acc += tile::elem_to_f32<F16>(lo) + tile::elem_to_f32<F16>(hi);
       }
       dst[int64_t(d) * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
     }
@@ -238,8 +235,8 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restri
       float f[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        f[2 * e] = fmaf(elem_f32<F16>(gw[e] & 0xffffu), c[2 * e], elem_f32<F16>(ow[e] & 0xffffu));
-        f[2 * e + 1] = fmaf(elem_f32<F16>(gw[e] >> 16), c[2 * e + 1], elem_f32<F16>(ow[e] >> 16));
+        f[2 * e] = fmaf(tile::elem_to_f32<F16>(gw[e] & 0xffffu), c[2 * e], tile::elem_to_f32<F16>(ow[e] & 0xffffu));
+        f[2 * e + 1] = fmaf(tile::elem_to_f32<F16>(gw[e] >> 16), c[2 * e + 1], tile::elem_to_f32<F16>(ow[e] >> 16));
       }
       val = pack8<F16>(f);
     }

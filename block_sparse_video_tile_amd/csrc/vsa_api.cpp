@@ -61,6 +61,36 @@ Workspace workspace_layout(const vsa_plan_s& p) {
   return w;
 }
 
+// Workspace of the raster (gather-free) forward: pooled Q, K (and V and the
+// coarse output for the gated branch) and the selected block ids.
+struct FusedWorkspace {
+  size_t qp, kp, vp, oc, col, total;
+};
+FusedWorkspace fused_workspace_layout(const vsa_plan_s& p) {
+  const VsaGeom& g = p.g;
+  const size_t pooled = size_t(g.batch) * g.heads * g.nb * g.head_dim * 4;
+  const size_t col = size_t(g.batch) * g.heads * g.nb * (p.topk > 0 ? p.topk : 0) * 4;
+  FusedWorkspace w;
+  size_t off = 0;
+  w.qp = off; off += align256(pooled);
+  w.kp = off; off += align256(pooled);
+  w.vp = off; off += align256(pooled);
+  w.oc = off; off += align256(pooled);
+  w.col = off; off += align256(col);
+  w.total = off;
+  return w;
+}
+
+// Limits of the raster attention kernel: sub-tile descriptors hold the
+// block's origin token in 21 bits, and a token's byte offset from its block
+// origin in the raster tensor is a 32-bit value.
+const char* raster_unsupported(const VsaGeom& g) {
+  if (g.S >= (int64_t(1) << 21)) return "seq_len >= 2^21";
+  const int64_t span = (int64_t(g.bt - 1) * g.H + (g.bh - 1)) * g.W + g.bw;
+  if (span * g.heads * 256 >= (int64_t(1) << 32)) return "block span * num_heads too large";
+  return nullptr;
+}
+
 struct BwdWorkspace {
   size_t dsum, kt, qt, dot, tlist, tcount, total;
 };
@@ -207,9 +237,13 @@ vsa_status vsa_plan_block_counts(vsa_plan_t p, int32_t* counts, int64_t n) {
 
 vsa_status vsa_gather(vsa_plan_t p, int32_t role, const void* x, void* xb, float* pooled,
                       void* stream) {
-  if (!p || !x || !xb) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: null argument");
+  if (!p || !x || (!xb && !pooled))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: null argument");
   if (role != VSA_ROLE_Q && role != VSA_ROLE_K && role != VSA_ROLE_V)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: unknown role %d", role);
+  if (!xb)  // block means only, for any role
+    return hip_status(vsa::launch_gather_qk(p->g, x, nullptr, pooled, hipStream_t(stream)),
+                      "vsa_gather(pooling)");
   if (role == VSA_ROLE_V)
     return hip_status(vsa::launch_gather_v(p->g, x, xb, pooled, hipStream_t(stream)),
                       "vsa_gather(V)");
@@ -284,6 +318,41 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k,
                     "vsa_block_sparse_attn_fwd");
 }
 
+
+vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const void* k,
+                                            const void* v, const int32_t* row_ptr,
+                                            const int32_t* col, int32_t uniform_k, int64_t nnz,
+                                            const void* gate, const float* oc, void* o,
+                                            float* lse, void* stream) {
+  if (!p || !q || !k || !v || !o)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd_raster: null argument");
+  if ((gate == nullptr) != (oc == nullptr))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_fwd_raster: gate and o_coarse must both be given or both NULL");
+  if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_fwd_raster: o_coarse not 16-byte aligned");
+  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd_raster: nnz < 0");
+  if (nnz > 0 && !col)
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_fwd_raster: null col_idx with nnz > 0");
+  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
+  if (!row_ptr) {
+    if (uniform_k < 0 || uniform_k > p->g.nb)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_fwd_raster: uniform_k %d outside [0, %d]", uniform_k,
+                  p->g.nb);
+    if (nnz < rows * uniform_k)
+      return fail(VSA_ERR_INVALID_ARGUMENT,
+                  "vsa_block_sparse_attn_fwd_raster: nnz %lld < rows*uniform_k = %lld",
+                  (long long)nnz, (long long)(rows * uniform_k));
+  }
+  if (const char* why = raster_unsupported(p->g))
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd_raster: %s", why);
+  return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
+                                                lse, gate, oc, hipStream_t(stream)),
+                    "vsa_block_sparse_attn_fwd_raster");
+}
 
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t p, size_t* bytes) {
   if (!p || !bytes)
@@ -383,6 +452,59 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
     return hip_status(e, "vsa_forward: coarse attention");
   if ((e = vsa::launch_scatter(g, ob, gate ? oc : nullptr, gate, out, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: scatter");
+  return ok();
+}
+
+vsa_status vsa_forward_fused_workspace_size(vsa_plan_t p, size_t* bytes) {
+  if (!p || !bytes)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused_workspace_size: null");
+  *bytes = fused_workspace_layout(*p).total;
+  return ok();
+}
+
+vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const void* v,
+                             const void* gate, void* out, void* ws, size_t ws_bytes,
+                             int32_t* col_out, float* lse, void* stream) {
+  if (!p || !q || !k || !v || !out || !ws)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: null argument");
+  if (p->topk < 1)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: plan is in map mode (topk == 0)");
+  if (p->g.nb > 1024)
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_forward_fused: num_blocks %d > 1024 not implemented",
+                p->g.nb);
+  if (const char* why = raster_unsupported(p->g))
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_forward_fused: %s", why);
+  const FusedWorkspace w = fused_workspace_layout(*p);
+  if (ws_bytes < w.total)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: workspace %zu bytes < %zu needed",
+                ws_bytes, w.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: workspace not 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  float* qp = reinterpret_cast<float*>(base + w.qp);
+  float* kp = reinterpret_cast<float*>(base + w.kp);
+  float* vp = reinterpret_cast<float*>(base + w.vp);
+  float* oc = reinterpret_cast<float*>(base + w.oc);
+  int32_t* col = col_out ? col_out : reinterpret_cast<int32_t*>(base + w.col);
+  hipStream_t s = hipStream_t(stream);
+  const VsaGeom& g = p->g;
+  const int64_t nnz = int64_t(g.batch) * g.heads * g.nb * p->topk;
+  hipError_t e;
+  if ((e = vsa::launch_gather_qk(g, q, nullptr, qp, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward_fused: pool Q");
+  if ((e = vsa::launch_gather_qk(g, k, nullptr, kp, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward_fused: pool K");
+  if ((e = vsa::launch_score_topk(g, qp, kp, p->topk, col, nullptr, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward_fused: score/top-k");
+  if (gate) {
+    if ((e = vsa::launch_gather_qk(g, v, nullptr, vp, s)) != hipSuccess)
+      return hip_status(e, "vsa_forward_fused: pool V");
+    if ((e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
+      return hip_status(e, "vsa_forward_fused: coarse attention");
+  }
+  if ((e = vsa::launch_attn_fwd_raster(g, q, k, v, nullptr, col, p->topk, nnz, out, lse, gate,
+                                       gate ? oc : nullptr, s)) != hipSuccess)
+    return hip_status(e, "vsa_forward_fused: attention");
   return ok();
 }
 

@@ -46,6 +46,7 @@ __host__ __device__ inline int block_count(const VsaGeom& g, int beta) {
   return ct * ch * cw;
 }
 
+// xb == nullptr: block means only (any role)
 hipError_t launch_gather_qk(const VsaGeom& g, const void* x, void* xb, float* pooled,
                             hipStream_t s);
 hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, float* pooled,
@@ -77,5 +78,11 @@ hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp,
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, hipStream_t s);
+// Raster [B,S,NH,D] q, k, v and o; gate (raster) and oc (fp32 [B,NH,nb,D])
+// optional: o = attention + gate * oc[block].
+hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
+                                  const int32_t* row_ptr, const int32_t* col, int uniform_k,
+                                  int64_t nnz, void* o, float* lse, const void* gate,
+                                  const float* oc, hipStream_t s);
 
 }  // namespace vsa

@@ -134,8 +134,13 @@ vsa_status vsa_plan_block_counts(vsa_plan_t plan, int32_t* counts, int64_t n);
  * role V: writes x_blk in the blocked-V^T layout and, if `pooled` is not
  * NULL, the fp32 mean of each block's valid values (the gate-compress
  * branch's pooled values; h3 FastH3 log entry: that branch pools per tile).
- * x_raster: device, B*S*NH*D elem.  x_blk: device, B*NH*Npad*D elem.
- * pooled: device, B*NH*nb*D fp32, or NULL. */
+ * x_blk == NULL (any role, `pooled` required): the block means alone, read
+ * straight from the raster tensor with nothing else written -- the pooling
+ * pass of the gather-free path (vsa_forward_fused).
+ * x_raster: device, B*S*NH*D elem.  x_blk: device, B*NH*Npad*D elem, or NULL.
+ * pooled: device, B*NH*nb*D fp32, or NULL.
+ * Errors: INVALID_ARGUMENT for a null plan or x_raster, both x_blk and pooled
+ *   NULL, or an unknown role. */
 vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void* x_blk,
                       float* pooled, void* stream);
 
@@ -208,6 +213,31 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t plan, const void* q_blk, const v
                                      const int32_t* col_idx, int32_t uniform_k, int64_t nnz,
                                      void* o_blk, float* lse, void* stream);
 
+/* The same attention on raster tensors, with no gather or scatter pass
+ * ("FastVideo VSA" guide, "Choose top-k": tiling shapes that do not divide
+ * the grid cost routing and padding overhead; this variant leaves the tokens
+ * where they are).  Each query block's tokens and the selected key blocks'
+ * tokens are located by block index arithmetic inside the kernel, O is
+ * written straight to its raster rows, and the result is identical to
+ * vsa_block_sparse_attn_fwd followed by vsa_scatter (same products in the
+ * same order).
+ * q, k, v, o_raster: device elem raster [B,S,NH,D] (16-byte aligned rows).
+ * lse: device fp32 [B,NH,Npad] in the blocked row order, or NULL.
+ * row_ptr, col_idx, uniform_k, nnz: as for vsa_block_sparse_attn_fwd.
+ * gate, o_coarse: both NULL, or the gate (device elem raster) and the coarse
+ *   output (device fp32 pooled layout, 16-byte aligned): each token row is
+ *   then written as vsa_scatter_gated writes it, O + gate * o_coarse[block],
+ *   bit for bit.
+ * Errors: as vsa_block_sparse_attn_fwd, plus INVALID_ARGUMENT for only one of
+ *   gate / o_coarse or a misaligned o_coarse, and UNSUPPORTED for
+ *   seq_len >= 2^21 or (block span in tokens) * NH * 256 >= 2^32. */
+vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t plan, const void* q, const void* k,
+                                            const void* v, const int32_t* row_ptr,
+                                            const int32_t* col_idx, int32_t uniform_k,
+                                            int64_t nnz, const void* gate,
+                                            const float* o_coarse, void* o_raster, float* lse,
+                                            void* stream);
+
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
  * rowsum(dO*O) [B,NH,Npad] fp32, d-major copies of K, Q and dO, and the
  * transposed block map (B*NH*nb*nb + B*NH*nb int32), each 256-byte aligned. */
@@ -259,6 +289,25 @@ vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
 vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void* v,
                        const void* gate, void* out, void* workspace, size_t workspace_bytes,
                        int32_t* col_idx_out, float* lse, void* stream);
+
+/* Bytes of device workspace vsa_forward_fused needs for this plan (pooled Q,
+ * K and V, the coarse output and the selected block ids, each 256-byte
+ * aligned; no blocked copies of the tensors). */
+vsa_status vsa_forward_fused_workspace_size(vsa_plan_t plan, size_t* bytes);
+
+/* The whole hot path without the gather and scatter passes: the block means
+ * of Q and K are read from the raster tensors (vsa_gather with x_blk NULL),
+ * score and top-k select the blocks, and vsa_block_sparse_attn_fwd_raster
+ * attends and writes the raster output.  With `gate` the means of V and the
+ * coarse branch are computed first and the attention epilogue writes
+ * O + gate * o_coarse[block] as vsa_scatter_gated does.  Arguments, outputs
+ * and errors as for vsa_forward, with the workspace sized by
+ * vsa_forward_fused_workspace_size; plus UNSUPPORTED where the raster
+ * attention is. */
+vsa_status vsa_forward_fused(vsa_plan_t plan, const void* q, const void* k, const void* v,
+                             const void* gate, void* out, void* workspace,
+                             size_t workspace_bytes, int32_t* col_idx_out, float* lse,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* vsa_status_string(vsa_status status);

@@ -105,24 +105,26 @@ def _sample_rows(oplan, heads, batch, per_head=4, seed=0):
     return sorted(picks)
 
 
-def _full_forward(name, k=None, dtype=vsa.VSA_DTYPE_BF16):
+def _full_forward(name, k=None, dtype=vsa.VSA_DTYPE_BF16, fused=False):
     wl = WORKLOADS[name]
     k = wl.topk if k is None else k
     plan = _plan(wl, k, dtype)
     q, kk, v = make_qkv(wl, dtype=plan.torch_dtype())
-    ws = torch.empty(vsa.vsa_forward_workspace_size(plan), dtype=torch.uint8, device=DEV)
+    size = (vsa.vsa_forward_fused_workspace_size if fused else vsa.vsa_forward_workspace_size)(plan)
+    ws = torch.empty(size, dtype=torch.uint8, device=DEV)
     out = torch.empty(plan.raster_shape(), dtype=plan.torch_dtype(), device=DEV)
     col = torch.empty(plan.num_rows() * k, dtype=torch.int32, device=DEV)
     lse = torch.empty((plan.batch, plan.heads, plan.padded_len), dtype=torch.float32, device=DEV)
-    vsa.vsa_forward(plan, q.to(DEV), kk.to(DEV), v.to(DEV), out, ws, col, lse)
+    vsa.vsa_forward(plan, q.to(DEV), kk.to(DEV), v.to(DEV), out, ws, col, lse, fused=fused)
     torch.cuda.synchronize()
     return wl, k, q, kk, v, plan, out.cpu(), col.cpu().numpy(), lse.cpu().numpy()
 
 
-def check_full_forward_sampled(name, k=None, dtype=vsa.VSA_DTYPE_BF16):
+def check_full_forward_sampled(name, k=None, dtype=vsa.VSA_DTYPE_BF16, fused=False):
     """Whole path at full size: map rows exact outside near-ties, sampled rows
-    of O and LSE against the oracle run on the GPU's own map."""
-    wl, k, q, kk, v, plan, out, col, lse = _full_forward(name, k, dtype)
+    of O and LSE against the oracle run on the GPU's own map.  fused=True runs
+    the gather-free forward."""
+    wl, k, q, kk, v, plan, out, col, lse = _full_forward(name, k, dtype, fused)
     oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, k)
     q64, k64, v64 = bf16_to_f64(q), bf16_to_f64(kk), bf16_to_f64(v)
     ref_sc = oracle.block_scores(oracle.pool_blocks(q64, oplan), oracle.pool_blocks(k64, oplan))

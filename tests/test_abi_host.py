@@ -203,3 +203,43 @@ def test_backward_checks(plan):
     big = vsa.vsa_plan(4097 * 64, (1, 1, 4097 * 64), (1, 1, 64), topk=1)
     a = list(args); a[0] = big.handle; a[9] = 1; a[10] = 4097; a[15] = 1 << 40
     assert _raw(f, *a) == vsa.VSA_ERR_UNSUPPORTED
+
+
+def test_raster_attention_and_fused_forward_checks(plan):
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    f = "vsa_block_sparse_attn_fwd_raster"
+    # (plan, q, k, v, row_ptr, col, uniform_k, nnz, gate, o_coarse, o, lse, stream)
+    n0 = (None, None)
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 9, 9 * 16, *n0, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 63, *n0, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, FAKE, 0, -1, *n0, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, FAKE, None, 0, 5, *n0, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, None, None, FAKE, 4, 64, *n0, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 64, *n0, None, None, None) == bad
+    # gate and o_coarse come together; o_coarse is read as float4
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 64, FAKE, None, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 64, None, FAKE, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, 64, FAKE, FAKE + 8, FAKE, None,
+                None) == bad
+    # descriptors hold a block's origin token in 21 bits
+    n = 1 << 21
+    big = vsa.vsa_plan(n, (1, 1, n), (1, 1, 64), topk=1)
+    rows = big.num_rows()
+    assert _raw(f, big.handle, FAKE, FAKE, FAKE, None, FAKE, 1, rows, None, None, FAKE, None,
+                None) == vsa.VSA_ERR_UNSUPPORTED
+    assert "2^21" in vsa.vsa_last_error()
+    # the gather-free forward needs no blocked copies: pooled tensors and ids only
+    need = vsa.vsa_forward_fused_workspace_size(plan)
+    info = plan.info
+    assert need % 256 == 0
+    assert 4 * info["pooled_elems"] * 4 <= need < info["blocked_elems"] * 2
+    g = "vsa_forward_fused"   # (plan, q, k, v, gate, out, ws, ws_bytes, col_out, lse, stream)
+    assert _raw(g, h, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None, None, None) == bad
+    assert _raw(g, h, FAKE, FAKE, FAKE, None, FAKE, FAKE + 16, need, None, None, None) == bad
+    assert _raw(g, h, FAKE, FAKE, None, None, FAKE, FAKE, need, None, None, None) == bad
+    mp = vsa.vsa_plan(2048, (8, 16, 16), (4, 8, 8), topk=0)
+    assert _raw(g, mp.handle, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None, None,
+                None) == bad
+    # pooling alone: x_blk NULL needs `pooled`
+    assert _raw("vsa_gather", h, 2, FAKE, None, None, None) == bad
