@@ -145,6 +145,14 @@ __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Row max over the 16 scores of one tile.
+__device__ inline float tile_max1(const f32x16& st) {
+  float mx = st[0];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, st[j]);
+  return mx;
+}
+
 // Row max over the 32 scores this lane holds.
 __device__ inline float tile_max(const f32x16 (&st)[2]) {
   float mx = st[0][0];
@@ -195,8 +203,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   const int lane = tid % 64;
   const int half = lane / 32;
   const int l32 = lane & 31;
-  const int qrow = wave * 32 + l32;      // this lane's query row inside the block
-  const bool active = wave * 32 < cq;    // wave-uniform
+  // Query row groups.  Normally wave w owns rows 32w .. 32w+31.  With 8
+  // waves and 5 or 6 groups holding valid rows (a block cut by the grid
+  // edge), waves 4..7 share the last groups by keys instead: waves 4 and 6
+  // take group 4, waves 5 and 7 group 5; the first of each pair takes keys
+  // 0..31 of every sub-tile and the second keys 32..63, each with its own
+  // online softmax, and the pairs merge before the epilogue.  Waves w and w+4
+  // run on the same SIMD, so each SIMD then carries 1.5 waves of matrix work
+  // instead of 2 on two SIMDs and 1 on the others.
+  const int ngroups = (cq + 31) / 32;
+  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
+  const int qgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
+  const int khalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all 64 keys
+  const int qrow = qgroup * 32 + l32;    // this lane's query row inside the block
+  const bool active = qgroup * 32 < cq;  // wave-uniform
 
   int64_t beg, end;
   if (row_ptr != nullptr) {
@@ -318,6 +338,16 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // 8*half + e (e = (lane%16)/4), d column 64*((lane/16)%2) + 4*(lane%4)
   const int vtr = (8 * half + (lane & 15) / 4) * (kRasterVRow * 16) +
                   (64 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // operand bases of a key-half wave: keys 32*kh .. 32*kh+31 of each sub-tile
+  const int kh = khalf > 0 ? 1 : 0;
+  const int kread_h = kread + kh * 32 * kKRow;
+  const int vread_h = vread + kh * 4;
+  const int vtr_h = vtr + kh * 32 * (kRasterVRow * 16);
+  // The passes over the row (list building, prologue, pipelined steps) are
+  // compiled twice, for full waves (HV = false) and for key-half waves, each
+  // with its own register allocation; a wave runs one of them.
+  auto passes = [&](auto hv) __attribute__((always_inline)) {
+  constexpr bool HV = decltype(hv)::value;
   f32x16 sa[2], sb[2];
   float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
 
@@ -390,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     load_k(d1, kbuf1);
     wait_loads();
     __syncthreads();
-    if (active) {
+    if (active && !HV) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -402,15 +432,127 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           sa[mt] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), qf[s],
                                       sa[mt]);
       mx_pre = tile_max(sa);
+    } else if (active) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sa[0][j] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        sa[0] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread_h + 2 * s]), qf[s], sa[0]);
+      mx_pre = tile_max1(sa[0]);
     }
     // the first step copies K_2 into kbuf0: every wave must be done with K_0
     __syncthreads();
+
+    // The step of a key-half wave: the same pipeline on one 32-key S^T tile
+    // per sub-tile, laid out in 16 slots (8 QK^T, then 8 PV).
+    auto half_body = [&](f32x16& cur, f32x16& nxt, const uint4* kn, uint4* kw, const uint4* vn,
+                         uint4* vw, const uint4* sk, const uint4* sv, const uint32_t (&ko)[kMaxK],
+                         const uint32_t (&vo)[kMaxV]) __attribute__((always_inline)) {
+      float mx = mx_pre;
+      const int valid = (d0 & (RASTER ? 63 : 127)) + 1;
+      if (valid < kKvChunk) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kh * 32 + 16 * (j / 8) + 8 * half + (j % 8);
+          if (key >= valid) cur[j] = -INFINITY;
+        }
+        mx = tile_max1(cur);
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      if (__ballot(mx > m_run + rescale_thr) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+      }
+      // A key half may see only masked keys for a while (m_run = -inf); any
+      // finite reference then gives p = 0 for them.
+      const float mb = m_run == -INFINITY ? 0.f : m_run * scale_log2;
+      float rs0 = 0.f, rs1 = 0.f;
+      uint32_t pw[2][4];
+      float mxn = -INFINITY;
+      ev8 opk[8], opv[8];
+      auto read_k = [&](int u) { opk[u % 8] = as_ev8(kn[kread_h + 2 * u]); };
+      auto read_v = [&](int w) {  // PV slot w: keys 32*kh + 16*(w/4) + ..., d tile w%4
+        if constexpr (RASTER) {
+          const char* bp = reinterpret_cast<const char*>(vn) + vtr_h +
+                           (16 * (w / 4)) * (kRasterVRow * 16) + 32 * (w % 4);
+          const v4i16 lo = lds_read_tr16(bp);
+          const v4i16 hi = lds_read_tr16(bp + 4 * (kRasterVRow * 16));
+          opv[w % 8] = __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          opv[w % 8] = as_ev8(vn[vread_h + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < 4; ++u) read_k(u);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) nxt[j] = 0.f;
+      slot_fence();
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if constexpr (kSlotCopies) {
+#pragma unroll
+          for (int x = 0; x < kMaxK; ++x)
+            if (u == 1 + (x * 8) / kMaxK) copy_k(sk, ko[x], x, kw);
+#pragma unroll
+          for (int x = 0; x < kMaxV; ++x)
+            if (u == 9 + (x * 8) / kMaxV) copy_v(sv, vo[x], x, vw);
+        }
+        if (u < 8) {
+          if (u % 4 == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              if (u + 4 < 8) read_k(u + 4 + x);
+              else read_v(x);
+            }
+          }
+          nxt = mfma_32x32x16<F16>(opk[u % 8], qf[u], nxt);
+          // exponential pair u: keys 2(u%4), 2(u%4)+1 of PV step u/4
+          const int cc = u / 4, t = 2 * (u % 4);
+          float p0 = __builtin_amdgcn_exp2f(fmaf(cur[8 * cc + t], scale_log2, -mb));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(cur[8 * cc + t + 1], scale_log2, -mb));
+          rs0 += p0;
+          rs1 += p1;
+          pw[cc][t / 2] = pack2<F16>(p0, p1);
+          pin(rs0);
+          pin(rs1);
+          pin(pw[cc][t / 2]);
+        } else {
+          const int w = u - 8, cc = w / 4, dt = w % 4;
+          if (w == 0) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) read_v(4 + x);
+          }
+          const ev8 pb = __builtin_bit_cast(
+              ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+          oacc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, oacc[dt]);
+          if (u >= 12) {
+            const int j0 = (u - 12) * 4;
+            mxn = fmaxf(fmaxf(mxn, nxt[j0]), nxt[j0 + 1]);
+            mxn = fmaxf(fmaxf(mxn, nxt[j0 + 2]), nxt[j0 + 3]);
+            pin(mxn);
+          }
+        }
+        slot_fence();
+      }
+      l_run += rs0 + rs1;
+      mx_pre = mxn;
+    };
 
     // Finish sub-tile n (scores in `cur`) and compute the scores of n+1 into
     // `nxt`.  kn: K buffer holding K_{n+1}; kw: K buffer receiving K_{n+2};
     // vn: V buffer holding V_n; vw: V buffer receiving V_{n+1}.
     auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
-                    const uint4* vn, uint4* vw) {
+                    const uint4* vn, uint4* vw) __attribute__((always_inline)) {
       const uint4* const sk = src_of(kbase, d2);
       const uint4* const sv = src_of(vbase, d1);
       const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
@@ -422,7 +564,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         k_offsets(d2, ko);
         v_offsets(d1, vo);
       }
-      if (active) {
+      if (HV && active) {
+        half_body(cur[0], nxt[0], kn, kw, vn, vw, sk, sv, ko, vo);
+      } else if (!HV && active) {
         float mx = mx_pre;
         // mask keys past the block's valid count (only in its last sub-tile)
         const int valid = (d0 & (RASTER ? 63 : 127)) + 1;
@@ -570,6 +714,42 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       if (n >= T) break;
     }
   }
+  };
+  if (khalf >= 0) passes(std::true_type());
+  else passes(std::false_type());
+
+  // ---- key-half pairs: the second wave of a pair hands its (m, l, O^T) to
+  // the first through LDS (wave 6's in vbuf1, wave 7's in tlist + escan,
+  // none of which the epilogue's staging uses), which merges them:
+  // m = max(m_a, m_b), O = O_a 2^((m_a - m)c) + O_b 2^((m_b - m)c), l likewise.
+  const bool own_pad = split && khalf == 1;  // waves 6, 7: their own rows are padding
+  if (split) {
+    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(vbuf1)
+                                        : reinterpret_cast<float*>(tlist);
+    float* const part_ml = (wave & 1) == 0 ? part + 64 * 64 : reinterpret_cast<float*>(escan);
+    if (own_pad && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[(dt * 16 + j) * 64 + lane] = oacc[dt][j];
+      part_ml[lane] = m_run;
+      part_ml[64 + lane] = l_run;
+    }
+    __syncthreads();
+    if (khalf == 0 && active) {
+      const float mb = part_ml[lane], lb = part_ml[64 + lane];
+      const float m_new = fmaxf(m_run, mb);
+      const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - m_new) * scale_log2);
+      m_run = m_new;
+      l_run = l_run * wa + lb * wb;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          oacc[dt][j] = oacc[dt][j] * wa + part[(dt * 16 + j) * 64 + lane] * wb;
+    }
+  }
 
   // ---- epilogue: combine the two lane halves' partial sums, normalise, and
   // store O through LDS so that every global store is a full 256-byte row.
@@ -578,14 +758,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
                                                      __float_as_uint(l_run), false, false);
     l_run = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  const bool row_valid = active && qrow < cq;
+  const bool row_valid = active && !own_pad && qrow < cq;
   const float inv = (row_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
   // staging area of 32 rows x 272 B per wave: two waves per buffer
   uint4* const sbase = wave < 2 ? kbuf0 : (wave < 4 ? kbuf1 : (wave < 6 ? vbuf0 : vbuf1));
   uint4* const srows = sbase + (wave % 2) * 32 * kORow;
   uint2* const ostage = reinterpret_cast<uint2*>(srows);
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < 4 && !own_pad; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       // registers 4jj..4jj+3 hold O^T rows m = 8jj + 4*half + 0..3, i.e.
@@ -617,7 +797,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     for (int p = 0; p < 8; ++p) {
       const int rr = p * 4 + lane / 16;
       const int slot = wave * 32 + rr;
-      if (slot < cq) {
+      if (slot < cq && !own_pad) {
         const int64_t at = obase + soff[cls_i * kVol + slot];
         uint4 val = srows[rr * kORow + unit];
         if (gate != nullptr) {
@@ -641,11 +821,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int rr = p * 4 + lane / 16;
-      odst[rr * 16 + (lane & 15)] = srows[rr * kORow + (lane & 15)];
+      odst[rr * 16 + (lane & 15)] =
+          own_pad ? make_uint4(0u, 0u, 0u, 0u) : srows[rr * kORow + (lane & 15)];
     }
   }
   if (lse != nullptr && half == 0) {
-    lse[qk_row0 + qrow] =
+    lse[qk_row0 + (own_pad ? wave * 32 + l32 : qrow)] =
         (row_valid && l_run > 0.f) ? m_run * scale + __logf(l_run) : -INFINITY;
   }
 }
