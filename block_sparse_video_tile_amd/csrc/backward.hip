@@ -27,9 +27,11 @@
 //             kappa-permuted, so P and dS feed dV^T += dO^T P and
 //             dK^T += Q^T dS as B operands.  dV and dK are separate kernels so
 //             that each stays within 256 VGPRs per lane.
-// Sub-tiles are double-buffered (copies of the next one in flight while the
-// current one is computed); the forward's slot-level schedule is not applied
-// here.
+// dv runs the forward kernel's software pipeline (S of the next sub-tile on
+// the matrix cores while this sub-tile's P is formed, 32 fenced MFMA slots per
+// sub-tile).  dq and dk keep S and dP of one sub-tile at a time (their
+// operands leave no room for a second set), with the sub-tile copies
+// double-buffered.
 
 #include "attn_common.h"
 #include "vsa_internal.h"
@@ -400,7 +402,8 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   __shared__ __align__(16) uint4 qs1[kKUnits];
   __shared__ __align__(16) uint4 ds1[DK ? kKUnits : 1];
   __shared__ __align__(16) uint4 ts1[kVUnits];
-  __shared__ float lse_sh[2][kKvChunk], d_sh[2][kKvChunk];
+  __shared__ __align__(16) float lse_sh[2][kKvChunk];
+  __shared__ __align__(16) float d_sh[2][kKvChunk];
   __shared__ int tl[kPassTiles];
   __shared__ float tm[kPassTiles];  // multiplicity of each sub-tile's query block
   __shared__ int esc[kPassEntries];
@@ -468,23 +471,50 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
       }
     // B operand of the accumulation, by 16-query step cc
     uint32_t bw[4][4];
+    if constexpr (!DK) {
+      // dV: the 8 queries of step cc are 16cc + 8*half + 0..7, so their lse
+      // values come in as two 16-byte LDS reads
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+      for (int cc = 0; cc < 4; ++cc) {
+        const int q0 = query_of(cc / 2, 8 * (cc % 2), half);
+        float lq[8];
+        *reinterpret_cast<float4*>(&lq[0]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0]);
+        *reinterpret_cast<float4*>(&lq[4]) =
+            *reinterpret_cast<const float4*>(&lse_sh[set][q0 + 4]);
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        float x2[2];
+        for (int t = 0; t < 8; t += 2) {
+          float x2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int jj = 8 * (cc % 2) + t + u;
-          const int qi = query_of(cc / 2, jj, half);
-          // pad keys of this block take no part (their rows are also stored as 0)
-          const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
-                                                                 -lse_sh[set][qi])) * mult
-                                   : 0.f;
-          x2[u] = DK ? p * (dp[cc / 2][jj] - d_sh[set][qi]) : p;
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * (cc % 2) + t + u;
+            // pad keys of this block take no part (their rows are also stored as 0)
+            x2[u] = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
+                                                           -lq[t + u])) * mult
+                             : 0.f;
+          }
+          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
         }
-        bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
       }
+    } else {
+      // dK: one value at a time keeps the register footprint of S, dP and
+      // the two operand sets within 256
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          float x2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * (cc % 2) + t + u;
+            const int qi = query_of(cc / 2, jj, half);
+            const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
+                                                                   -lse_sh[set][qi])) * mult
+                                     : 0.f;
+            x2[u] = p * (dp[cc / 2][jj] - d_sh[set][qi]);
+          }
+          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
+        }
+    }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
@@ -540,6 +570,269 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
                   l32, half);
 }
 
+// ------------------------------------------------------------------ dV, pipelined
+
+// Keep the scheduler from moving work across a slot boundary, and keep a
+// VALU result in the slot where it is written (as in the forward kernel).
+__device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
+__device__ inline void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// dV with the forward kernel's software pipeline.  One workgroup per key
+// block, wave w owns keys 32w .. 32w+31 (their K fragments stay in VGPRs).
+// The 64-query sub-tiles of the query blocks whose rows list the block stream
+// through LDS, Q one sub-tile ahead of dO^T, so that while
+//   P_n = 2^(S_n log2(e)/sqrt(D) - lse log2(e) + log2(multiplicity))
+// feeds dV^T += dO^T_n P_n the matrix cores already compute
+// S_{n+1} = Q_{n+1} K^T.  32 MFMA slots per sub-tile (16 for S_{n+1}, then 16
+// for dV), the 16 exponential pairs of P_n spread over them.  Pad query rows
+// carry lse = +inf in LDS (P = 0); pad key rows are stored as zero.
+template <int NW, bool F16>
+__global__ __launch_bounds__(NW * 64) void dv_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ dot,
+    const float* __restrict__ lse, const int32_t* __restrict__ tlist,
+    const int32_t* __restrict__ tcount, uint4* __restrict__ dv, VsaGeom g, float scale_log2) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kPassTiles = kPassEntries * (NW / 2);
+  // Q sub-tiles (kappa rows, the "K" role of the forward) and dO^T sub-tiles
+  // (d rows, the "V^T" role); four arrays so the compiler sees that copies in
+  // flight never alias the buffers being read
+  __shared__ __align__(16) uint4 kbuf0[kKUnits];
+  __shared__ __align__(16) uint4 kbuf1[kKUnits];
+  __shared__ __align__(16) uint4 vbuf0[kVUnits];
+  __shared__ __align__(16) uint4 vbuf1[kVUnits];
+  __shared__ __align__(16) float lbuf[2][kKvChunk];
+  __shared__ int tl[kPassTiles];
+  __shared__ float tm[kPassTiles];
+  __shared__ int esc[kPassEntries];
+  __shared__ int ntl;
+  const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
+  const int64_t c = xcd_remap(blockIdx.x, ncols);
+  const int j = int(c % g.nb);
+  const int64_t bh = c / g.nb;
+  const int cj = block_count(g, j);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
+  const int key = wave * 32 + l32;
+  const bool active = wave * 32 < cj;
+  const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
+
+  ev8 kf[8];
+  if (active) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kf[s] = as_ev8(k[(key0 + key) * 16 + 2 * s + half]);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+
+  const uint4* const qbase = q + bh * g.npad * 16;
+  const uint4* const tbase = dot + bh * (g.npad / kKvChunk) * kUnits;
+  const float* const lbase = lse + bh * g.npad;
+  const int cpb = g.vol / kKvChunk;
+  constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
+  constexpr bool kSlotCopies = kMaxK + kMaxV <= 6;
+  uint32_t koff[kMaxK], voff[kMaxV];
+#pragma unroll
+  for (int x = 0; x < kMaxK; ++x) koff[x] = row_tile_off((wave + x * NW) * 64 + lane);
+#pragma unroll
+  for (int x = 0; x < kMaxV; ++x) voff[x] = col_tile_off((wave + x * NW) * 64 + lane);
+  auto src_of = [](const uint4* base, int d) { return base + int64_t(d >> 7) * kUnits; };
+  auto copy_k = [&](const uint4* src, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, koff[x], dst + (wave + x * NW) * 64);
+  };
+  auto copy_v = [&](const uint4* src, int x, uint4* dst) {
+    if (tid / 64 + x * NW < kVChunks) wave_copy_to_lds(src, voff[x], dst + (wave + x * NW) * 64);
+  };
+  auto load_k = [&](int d, uint4* dst) {
+#pragma unroll
+    for (int x = 0; x < kMaxK; ++x) copy_k(src_of(qbase, d), x, dst);
+  };
+  auto load_v = [&](int d, uint4* dst) {
+#pragma unroll
+    for (int x = 0; x < kMaxV; ++x) copy_v(src_of(tbase, d), x, dst);
+  };
+  // lse of the 64 query rows of sub-tile d, staged by wave 0: a plain load
+  // issued early, the LDS write late
+  auto lse_raw = [&](int d) { return wave == 0 ? lbase[int64_t(d >> 7) * kKvChunk + lane] : 0.f; };
+  auto lse_put = [&](float raw, int d, float mult, float* dst) {
+    if (wave == 0) dst[lane] = lane <= (d & 127) ? raw * kLog2e - __log2f(mult) : INFINITY;
+  };
+  const int kread = l32 * kKRow + half;
+  const int vread = l32 * kVRow + half;
+  f32x16 sa[2], sb[2];
+
+  const int nent = tcount[c];
+  const int32_t* list = tlist + c * int64_t(g.nb);
+  for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
+    const int m = min(kPassEntries, nent - e0);
+    for (int x = tid; x < m; x += kThreads)
+      esc[x] = (block_count(g, list[e0 + x] & 0xffff) + kKvChunk - 1) / kKvChunk;
+    __syncthreads();
+    scan_counts(esc, m, &ntl, wave, lane);
+    __syncthreads();
+    for (int x = tid; x < m; x += kThreads) {
+      const int32_t ent = list[e0 + x];
+      const int qi = ent & 0xffff;
+      const float mult = float(uint32_t(ent) >> 16);
+      const int cq = block_count(g, qi);
+      for (int sub = 0; sub * kKvChunk < cq; ++sub) {
+        tl[esc[x] + sub] = ((qi * cpb + sub) << 7) | (min(kKvChunk, cq - sub * kKvChunk) - 1);
+        tm[esc[x] + sub] = mult;
+      }
+    }
+    __syncthreads();
+    const int T = __builtin_amdgcn_readfirstlane(ntl);
+    if (T == 0) continue;
+    // descriptor / multiplicity of sub-tile n; past the end the last one
+    // repeats (its copies land in buffers that are not read again)
+    auto desc_at = [&](int n) { return tl[min(n, T - 1)]; };
+    auto mult_at = [&](int n) { return tm[min(n, T - 1)]; };
+
+    int n = 0;
+    int d0 = __builtin_amdgcn_readfirstlane(desc_at(0));
+    int d1 = __builtin_amdgcn_readfirstlane(desc_at(1));
+    int d2 = __builtin_amdgcn_readfirstlane(desc_at(2));
+    load_k(d0, kbuf0);
+    load_v(d0, vbuf0);
+    load_k(d1, kbuf1);
+    {
+      const float raw = lse_raw(d0);
+      wait_copies();
+      lse_put(raw, d0, mult_at(0), lbuf[0]);
+    }
+    __syncthreads();
+    if (active) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) sa[mt][jj] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          sa[mt] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), kf[s],
+                                      sa[mt]);
+    }
+    // the first step copies Q_2 into kbuf0: every wave must be done with Q_0
+    __syncthreads();
+
+    // Finish sub-tile n (S_n in `cur`, lse_n in lcur) and compute S_{n+1}
+    // into `nxt`.  kn: Q_{n+1}; kw receives Q_{n+2}; vn: dO^T_n; vw receives
+    // dO^T_{n+1}; lnx receives lse_{n+1}.
+    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
+                    const uint4* vn, uint4* vw, const float* lcur, float* lnx) {
+      const uint4* const sk = src_of(qbase, d2);
+      const uint4* const sv = src_of(tbase, d1);
+      const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
+      const float m1 = mult_at(n + 1);
+      const float raw = lse_raw(d1);
+      if constexpr (!kSlotCopies) {
+        load_k(d2, kw);
+        load_v(d1, vw);
+      }
+      if (active) {
+        uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 dV steps
+        ev8 opk[8], opv[8];
+        float4 lq[4][2];    // lse of the 8 queries of each dV step
+        auto read_k = [&](int u) {
+          opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
+        };
+        auto read_v = [&](int w) {
+          opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+        };
+        // queries of step cc: 16cc + 8*half + 0..7 (kappa-staged rows)
+        auto read_l = [&](int cc) {
+          lq[cc][0] = *reinterpret_cast<const float4*>(lcur + 16 * cc + 8 * half);
+          lq[cc][1] = *reinterpret_cast<const float4*>(lcur + 16 * cc + 8 * half + 4);
+        };
+        read_l(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) read_k(u);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) nxt[mt][jj] = 0.f;
+        slot_fence();
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          if constexpr (kSlotCopies) {
+#pragma unroll
+            for (int x = 0; x < kMaxK; ++x)
+              if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
+#pragma unroll
+            for (int x = 0; x < kMaxV; ++x)
+              if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
+          }
+          // lse of dV step cc read two steps' worth of slots ahead of its pairs
+          if (u == 2) read_l(1);
+          if (u == 10) read_l(2);
+          if (u == 18) read_l(3);
+          if (u < 16) {
+            const int s = u / 2, mt = u % 2;
+            if (u % 4 == 0) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                if (u + 4 < 16) read_k(u + 4 + x);
+                else read_v(x);
+              }
+            }
+            nxt[mt] = mfma_32x32x16<F16>(opk[u % 8], kf[s], nxt[mt]);
+          } else {
+            const int w = u - 16, cc = w / 4, dt = w % 4;
+            if (w % 4 == 0 && w + 4 < 16) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
+            }
+            const ev8 pb = __builtin_bit_cast(
+                ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+            acc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, acc[dt]);
+          }
+          // exponential pair e (queries 2e%8, +1 of step e/4): pairs 0..11 in
+          // even slots 0..22, pairs 12..15 in slots 24..27
+          const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+          if (e >= 0) {
+            const int cc = e / 4, t = 2 * (e % 4);
+            const float4 l4 = lq[cc][t / 4];
+            const float la = (t % 4 == 0) ? l4.x : l4.z;
+            const float lb = (t % 4 == 0) ? l4.y : l4.w;
+            const float p0 =
+                __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -la));
+            const float p1 =
+                __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -lb));
+            pw[cc][t / 2] = pack2<F16>(p0, p1);
+            pin_v(pw[cc][t / 2]);
+          }
+          slot_fence();
+        }
+      } else if constexpr (kSlotCopies) {
+#pragma unroll
+        for (int x = 0; x < kMaxK; ++x) copy_k(sk, x, kw);
+#pragma unroll
+        for (int x = 0; x < kMaxV; ++x) copy_v(sv, x, vw);
+      }
+      wait_copies();
+      lse_put(raw, d1, m1, lnx);
+      __syncthreads();
+      ++n;
+      d0 = d1;
+      d1 = d2;
+      d2 = __builtin_amdgcn_readfirstlane(d3);
+    };
+
+    while (true) {
+      step(sa, sb, kbuf1, kbuf0, vbuf0, vbuf1, lbuf[0], lbuf[1]);
+      if (n >= T) break;
+      step(sb, sa, kbuf0, kbuf1, vbuf1, vbuf0, lbuf[1], lbuf[0]);
+      if (n >= T) break;
+    }
+  }
+  // rows of this wave's keys; pad key rows are written as zero
+  store_rows<F16>(acc, key < cj ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32, half);
+}
+
 template <int NW, bool F16>
 hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
@@ -552,11 +845,10 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
                      a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), g, scale_log2, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<NW, F16, false>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((dv_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
-                     static_cast<const uint4*>(a.dout), static_cast<const uint4*>(a.dot), a.lse,
-                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dv), g, scale_log2, scale);
+                     static_cast<const uint4*>(a.dot), a.lse, a.tlist, a.tcount,
+                     static_cast<uint4*>(a.dv), g, scale_log2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((dkv_kernel<NW, F16, true>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
