@@ -31,7 +31,9 @@
 // the matrix cores while this sub-tile's P is formed, 32 fenced MFMA slots per
 // sub-tile).  dq and dk keep S and dP of one sub-tile at a time (their
 // operands leave no room for a second set), with the sub-tile copies
-// double-buffered.
+// double-buffered; dk lays each sub-tile out in 48 fenced slots so that the
+// dS pairs of one query tile run beside the matrix products of the next (for
+// dq, with a single lse per lane, the compiler's own order measured faster).
 
 #include "attn_common.h"
 #include "vsa_internal.h"
@@ -222,6 +224,11 @@ __device__ inline void scan_counts(int* cnt, int m, int* total, int wave, int la
   }
   if (lane == 63) *total = incl;
 }
+
+// Keep the scheduler from moving work across a slot boundary, and keep a
+// VALU result in the slot where it is written (as in the forward kernel).
+__device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
+__device__ inline void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // ------------------------------------------------------------------ dQ
 
@@ -453,75 +460,81 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
       d_sh[set][tid] = ok ? dsum[row] : 0.f;
     }
   };
+  // One query sub-tile in 48 fenced MFMA slots: S and dP of query tile 0
+  // (16), those of tile 1 (16) with the dS pairs of tile 0 on the VALU, dK^T
+  // for queries 0..31 (8) with the dS pairs of tile 1, dK^T for queries
+  // 32..63 (8).  Operands are read from LDS three slots ahead, the lse and D
+  // of a pair two pairs ahead.
   auto compute = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
     if (!active) return;
+    static_assert(DK, "the dV kernel is dv_kernel");
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) s[mt][jj] = dp[mt][jj] = 0.f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = mfma_32x32x16<F16>(as_ev8(qsb[qread + mt * 32 * kKRow + 2 * st]), kf[st], s[mt]);
-        if constexpr (DK)
-          dp[mt] = mfma_32x32x16<F16>(as_ev8(dsb[qread + mt * 32 * kKRow + 2 * st]), vf[st],
-                                      dp[mt]);
+    uint32_t bw[4][4];  // dS pairs: B operands of the 4 dK^T steps
+    // pad keys of this block take no part (their rows are also stored as 0):
+    // their K rows are zero, so P is finite there and the factor 0 removes it
+    const float mlane = key < cj ? mult : 0.f;
+    // pair k (0..15): query tile mt = k/8, step cc = 2mt + (k%8)/4, queries
+    // t, t+1 of it with t = 2(k%4), i.e. rows 16cc + 8*half + t (kappa-staged)
+    float2 lsep[3], dp2[3];
+    auto read_pair = [&](int k) {
+      const int cc = 2 * (k / 8) + (k % 8) / 4, t = 2 * (k % 4);
+      const int qi = 16 * cc + 8 * half + t;
+      lsep[k % 3] = *reinterpret_cast<const float2*>(&lse_sh[set][qi]);
+      dp2[k % 3] = *reinterpret_cast<const float2*>(&d_sh[set][qi]);
+    };
+    auto ds_pair = [&](int k) {
+      const int mt = k / 8, cc = 2 * mt + (k % 8) / 4, t = 2 * (k % 4);
+      const float2 l = lsep[k % 3], dd = dp2[k % 3];
+      const int jj = 8 * (cc % 2) + t;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mt][jj], scale_log2, -l.x)) * mlane;
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mt][jj + 1], scale_log2, -l.y)) * mlane;
+      bw[cc][t / 2] = pack2<F16>(p0 * (dp[mt][jj] - dd.x), p1 * (dp[mt][jj + 1] - dd.y));
+      pin_v(bw[cc][t / 2]);
+    };
+    ev8 op[4];
+    auto read_op = [&](int i) {
+      if (i < 32) {
+        const int mt = i / 16, st = (i % 16) / 2;
+        const uint4* b = (i % 2 == 0) ? qsb : dsb;
+        op[i % 4] = as_ev8(b[qread + mt * 32 * kKRow + 2 * st]);
+      } else {
+        const int x = i - 32, cc = x / 4, dt = x % 4;
+        op[i % 4] = as_ev8(tsb[tread + dt * 32 * kVRow + 2 * cc]);
       }
-    // B operand of the accumulation, by 16-query step cc
-    uint32_t bw[4][4];
-    if constexpr (!DK) {
-      // dV: the 8 queries of step cc are 16cc + 8*half + 0..7, so their lse
-      // values come in as two 16-byte LDS reads
+    };
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const int q0 = query_of(cc / 2, 8 * (cc % 2), half);
-        float lq[8];
-        *reinterpret_cast<float4*>(&lq[0]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0]);
-        *reinterpret_cast<float4*>(&lq[4]) =
-            *reinterpret_cast<const float4*>(&lse_sh[set][q0 + 4]);
+    for (int i = 0; i < 3; ++i) read_op(i);
+    read_pair(0);
+    read_pair(1);
+    slot_fence();
 #pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float x2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jj = 8 * (cc % 2) + t + u;
-            // pad keys of this block take no part (their rows are also stored as 0)
-            x2[u] = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
-                                                           -lq[t + u])) * mult
-                             : 0.f;
-          }
-          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
+    for (int i = 0; i < 48; ++i) {
+      if (i + 3 < 48) read_op(i + 3);
+      if (i < 32) {
+        const int mt = i / 16, st = (i % 16) / 2;
+        if (i % 2 == 0) s[mt] = mfma_32x32x16<F16>(op[i % 4], kf[st], s[mt]);
+        else dp[mt] = mfma_32x32x16<F16>(op[i % 4], vf[st], dp[mt]);
+        if (i >= 16 && i % 2 == 1) {
+          const int k = (i - 16) / 2;
+          if (k + 2 < 16) read_pair(k + 2);
+          ds_pair(k);
+        }
+      } else {
+        const int x = i - 32, cc = x / 4, dt = x % 4;
+        const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
+                                                         bw[cc][3]));
+        acc[dt] = mfma_32x32x16<F16>(op[i % 4], b, acc[dt]);
+        if (x < 8) {
+          const int k = 8 + x;
+          if (k + 2 < 16) read_pair(k + 2);
+          ds_pair(k);
         }
       }
-    } else {
-      // dK: one value at a time keeps the register footprint of S, dP and
-      // the two operand sets within 256
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-          float x2[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int jj = 8 * (cc % 2) + t + u;
-            const int qi = query_of(cc / 2, jj, half);
-            const float p = key < cj ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2,
-                                                                   -lse_sh[set][qi])) * mult
-                                     : 0.f;
-            x2[u] = p * (dp[cc / 2][jj] - d_sh[set][qi]);
-          }
-          bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
-        }
-    }
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
-                                                       bw[cc][3]));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma_32x32x16<F16>(as_ev8(tsb[tread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+      slot_fence();
     }
   };
 
@@ -571,11 +584,6 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
 }
 
 // ------------------------------------------------------------------ dV, pipelined
-
-// Keep the scheduler from moving work across a slot boundary, and keep a
-// VALU result in the slot where it is written (as in the forward kernel).
-__device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
-__device__ inline void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // dV with the forward kernel's software pipeline.  One workgroup per key
 // block, wave w owns keys 32w .. 32w+31 (their K fragments stay in VGPRs).
