@@ -392,10 +392,10 @@ __device__ inline int query_of(int mt, int jj, int half) {
   return 32 * mt + 16 * (jj / 8) + 8 * half + jj % 8;
 }
 
-template <int NW, bool F16, bool DK>
-__global__ __launch_bounds__(NW * 64) void dkv_kernel(
+template <int NW, bool F16>
+__global__ __launch_bounds__(NW * 64) void dk_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ qt, const uint4* __restrict__ dout, const uint4* __restrict__ dot,
+    const uint4* __restrict__ qt, const uint4* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ tlist, const int32_t* __restrict__ tcount,
     uint4* __restrict__ grad, VsaGeom g, float scale_log2, float scale) {
@@ -404,10 +404,10 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   // two buffer sets.  A operand of the first product(s): query rows (Q, and
   // dO for dK); A of the accumulation: d rows (dO^T for dV, Q^T for dK)
   __shared__ __align__(16) uint4 qs0[kKUnits];
-  __shared__ __align__(16) uint4 ds0[DK ? kKUnits : 1];
+  __shared__ __align__(16) uint4 ds0[kKUnits];
   __shared__ __align__(16) uint4 ts0[kVUnits];
   __shared__ __align__(16) uint4 qs1[kKUnits];
-  __shared__ __align__(16) uint4 ds1[DK ? kKUnits : 1];
+  __shared__ __align__(16) uint4 ds1[kKUnits];
   __shared__ __align__(16) uint4 ts1[kVUnits];
   __shared__ __align__(16) float lse_sh[2][kKvChunk];
   __shared__ __align__(16) float d_sh[2][kKvChunk];
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       kf[s] = as_ev8(k[(key0 + key) * 16 + 2 * s + half]);
-      if constexpr (DK) vf[s] = as_ev8(v[(key0 + key) * 16 + 2 * s + half]);
+      vf[s] = as_ev8(v[(key0 + key) * 16 + 2 * s + half]);
     }
   }
   f32x16 acc[4];
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
 
   const uint4* const qbase = q + bh * g.npad * 16;
   const uint4* const dbase = dout + bh * g.npad * 16;
-  const uint4* const tbase = (DK ? qt : dot) + bh * (g.npad / kKvChunk) * kUnits;
+  const uint4* const tbase = qt + bh * (g.npad / kKvChunk) * kUnits;
   const int cpb = g.vol / kKvChunk;
   const int qread = l32 * kKRow + half, tread = l32 * kVRow + half;
 
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   auto issue = [&](int d, uint4* qsb, uint4* dsb, uint4* tsb, int set) {
     const int64_t chunk = d >> 7;
     copy_tile<NW, kKChunks>(qbase + chunk * kUnits, qsb, wave, lane, true);
-    if constexpr (DK) copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsb, wave, lane, true);
+    copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsb, wave, lane, true);
     copy_tile<NW, kVChunks>(tbase + chunk * kUnits, tsb, wave, lane, false);
     if (tid < kKvChunk) {
       const int64_t row = bh * g.npad + chunk * kKvChunk + tid;
@@ -467,7 +467,6 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   // of a pair two pairs ahead.
   auto compute = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
     if (!active) return;
-    static_assert(DK, "the dV kernel is dv_kernel");
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -579,7 +578,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     }
   }
   // rows of this wave's keys; pad key rows are written as zero
-  store_rows<F16>(acc, key < cj ? (DK ? scale : 1.f) : 0.f, grad + (key0 + wave * 32) * 16,
+  store_rows<F16>(acc, key < cj ? scale : 0.f, grad + (key0 + wave * 32) * 16,
                   l32, half);
 }
 
@@ -858,10 +857,10 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
                      static_cast<const uint4*>(a.dot), a.lse, a.tlist, a.tcount,
                      static_cast<uint4*>(a.dv), g, scale_log2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<NW, F16, true>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((dk_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
                      static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
-                     static_cast<const uint4*>(a.dout), static_cast<const uint4*>(a.dot), a.lse,
+                     static_cast<const uint4*>(a.dout), a.lse,
                      a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk), g, scale_log2, scale);
   return hipGetLastError();
 }
