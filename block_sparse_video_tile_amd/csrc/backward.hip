@@ -35,6 +35,8 @@
 // dS pairs of one query tile run beside the matrix products of the next (for
 // dq, with a single lse per lane, the compiler's own order measured faster).
 
+#include <type_traits>
+
 #include "attn_common.h"
 #include "vsa_internal.h"
 
@@ -259,8 +261,18 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
-  const int qrow = wave * 32 + l32;
-  const bool active = wave * 32 < cq;
+  // Key-half waves for edge blocks, as in the forward kernel: with 8 waves and
+  // 5 or 6 groups of valid query rows, waves 4 and 6 share group 4 and waves 5
+  // and 7 group 5, the first of each pair taking keys 0..31 of every sub-tile
+  // and the second keys 32..63; the second's partial dQ is added to the
+  // first's before the store.  Waves w and w+4 share a SIMD.
+  const int ngroups = (cq + 31) / 32;
+  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
+  const int qgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
+  const int khalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all keys
+  const int kh = khalf > 0 ? 1 : 0;
+  const int qrow = qgroup * 32 + l32;
+  const bool active = qgroup * 32 < cq;
   const bool row_valid = qrow < cq;
   const int64_t row0 = bh * g.npad + int64_t(i) * g.vol;
 
@@ -296,6 +308,47 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     copy_tile<NW, kKChunks>(kbase + chunk * kUnits, ksb, wave, lane, true);
     copy_tile<NW, kKChunks>(vbase + chunk * kUnits, vsb, wave, lane, true);
     copy_tile<NW, kVChunks>(ktbase + chunk * kUnits, ktsb, wave, lane, false);
+  };
+  // key-half wave: one 32-key tile (keys 32kh..) of S^T and dP^T, dQ^T from
+  // the matching two 16-key steps
+  const int kread_h = kread + kh * 32 * kKRow, ktread_h = ktread + 4 * kh;
+  auto compute_half = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
+    if (!active) return;
+    f32x16 s, dp;
+#pragma unroll
+    for (int j2 = 0; j2 < 16; ++j2) s[j2] = dp[j2] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      s = mfma_32x32x16<F16>(as_ev8(ksb[kread_h + 2 * st]), qf[st], s);
+      dp = mfma_32x32x16<F16>(as_ev8(vsb[kread_h + 2 * st]), df[st], dp);
+    }
+    const int valid = (d & 127) + 1;
+    uint32_t dsw[2][4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        float d2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = 8 * cc + t + u;
+          const int key = 32 * kh + 16 * cc + 8 * half + t + u;
+          const float p = key < valid
+                              ? __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -lse_l2))
+                              : 0.f;
+          d2[u] = p * (dp[jj] - dq_row);
+        }
+        dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
+      }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
+                                                       dsw[cc][3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma_32x32x16<F16>(as_ev8(ktsb[ktread_h + dt * 32 * kVRow + 2 * cc]), b,
+                                     acc[dt]);
+    }
   };
   auto compute = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
     if (!active) return;
@@ -342,6 +395,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 
   int64_t beg, end;
   row_bounds(row_ptr, uniform_k, nnz, r, beg, end);
+  // the passes are compiled twice (full and key-half waves), each with its
+  // own register allocation
+  auto passes = [&](auto hv) __attribute__((always_inline)) {
+  constexpr bool HV = decltype(hv)::value;
+  auto work = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
+    if constexpr (HV) compute_half(d, ksb, vsb, ktsb);
+    else compute(d, ksb, vsb, ktsb);
+  };
   for (int64_t e0 = beg; e0 < end; e0 += kPassEntries) {
     const int m = int(min(int64_t(kPassEntries), end - e0));
     for (int x = tid; x < m; x += kThreads) {
@@ -369,18 +430,48 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
       const int d0 = __builtin_amdgcn_readfirstlane(tl[n]);
       const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
       if (n + 1 < T) issue(d1, ks1, vs1, kts1);
-      compute(d0, ks0, vs0, kts0);
+      work(d0, ks0, vs0, kts0);
       wait_copies();
       __syncthreads();
       if (n + 1 >= T) break;
       if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), ks0, vs0, kts0);
-      compute(d1, ks1, vs1, kts1);
+      work(d1, ks1, vs1, kts1);
       wait_copies();
       __syncthreads();
     }
   }
-  // dQ rows; pad query rows are written as zero
-  store_rows<F16>(acc, row_valid ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32, half);
+  };
+  if (khalf >= 0) passes(std::true_type());
+  else passes(std::false_type());
+  // key-half pairs: the second wave's partial dQ^T (wave 6's in ks1, wave 7's
+  // in vs1, both free after the last barrier) is added to the first's
+  const bool own_pad = split && khalf == 1;  // waves 6, 7: their own rows are padding
+  if (split) {
+    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(ks1)
+                                        : reinterpret_cast<float*>(vs1);
+    if (own_pad && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) part[(dt * 16 + j) * 64 + lane] = acc[dt][j];
+    }
+    __syncthreads();
+    if (khalf == 0 && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[dt][j] += part[(dt * 16 + j) * 64 + lane];
+    }
+    if (own_pad) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[dt][j] = 0.f;
+    }
+  }
+  // dQ rows (this wave's own 32 rows); pad query rows are written as zero
+  store_rows<F16>(acc, row_valid && !own_pad ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32,
+                  half);
 }
 
 // ------------------------------------------------------------------ dV, dK
@@ -423,8 +514,18 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
-  const int key = wave * 32 + l32;
-  const bool active = wave * 32 < cj;
+  // Query-half waves for edge key blocks: with 8 waves and 5 or 6 groups of
+  // valid keys, waves 4 and 6 share key group 4 and waves 5 and 7 group 5,
+  // the first of each pair taking queries 0..31 of every query sub-tile and
+  // the second queries 32..63; the second's partial dK is added to the
+  // first's before the store.  Waves w and w+4 share a SIMD.
+  const int ngroups = (cj + 31) / 32;
+  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
+  const int kgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
+  const int qhalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all queries
+  const int qh = qhalf > 0 ? 1 : 0;
+  const int key = kgroup * 32 + l32;
+  const bool active = kgroup * 32 < cj;
   const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
 
   ev8 kf[8], vf[8];
@@ -537,8 +638,64 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
     }
   };
 
+  // query-half wave: one 32-query tile (queries 32qh..) of S and dP, dK^T
+  // from the matching two 16-query steps
+  const int qread_h = qread + qh * 32 * kKRow, tread_h = tread + 4 * qh;
+  auto compute_half = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb,
+                          int set) {
+    if (!active) return;
+    f32x16 s1, dp1;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) s1[jj] = dp1[jj] = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      s1 = mfma_32x32x16<F16>(as_ev8(qsb[qread_h + 2 * st]), kf[st], s1);
+      dp1 = mfma_32x32x16<F16>(as_ev8(dsb[qread_h + 2 * st]), vf[st], dp1);
+    }
+    const float mlane = key < cj ? mult : 0.f;
+    uint32_t bw[2][4];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      // queries 32qh + 16cc + 8*half + 0..7
+      const int q0 = 32 * qh + 16 * cc + 8 * half;
+      float lq[8], dq8[8];
+      *reinterpret_cast<float4*>(&lq[0]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0]);
+      *reinterpret_cast<float4*>(&lq[4]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0 + 4]);
+      *reinterpret_cast<float4*>(&dq8[0]) = *reinterpret_cast<const float4*>(&d_sh[set][q0]);
+      *reinterpret_cast<float4*>(&dq8[4]) = *reinterpret_cast<const float4*>(&d_sh[set][q0 + 4]);
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        float x2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int jj = 8 * cc + t + u;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, -lq[t + u])) * mlane;
+          x2[u] = p * (dp1[jj] - dq8[t + u]);
+        }
+        bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
+                                                       bw[cc][3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = mfma_32x32x16<F16>(as_ev8(tsb[tread_h + dt * 32 * kVRow + 2 * cc]), b,
+                                     acc[dt]);
+    }
+  };
+
   const int nent = tcount[c];
   const int32_t* list = tlist + c * int64_t(g.nb);
+  // the passes are compiled twice (full and query-half waves), each with its
+  // own register allocation
+  auto passes = [&](auto hv) __attribute__((always_inline)) {
+  constexpr bool HV = decltype(hv)::value;
+  auto work = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
+    if constexpr (HV) compute_half(mult, qsb, dsb, tsb, set);
+    else compute(mult, qsb, dsb, tsb, set);
+  };
   for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
     const int m = min(kPassEntries, nent - e0);
     for (int x = tid; x < m; x += kThreads)
@@ -567,18 +724,47 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
       const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
       const float m1 = tm[min(n + 1, T - 1)];
       if (n + 1 < T) issue(d1, qs1, ds1, ts1, 1);
-      compute(m0, qs0, ds0, ts0, 0);
+      work(m0, qs0, ds0, ts0, 0);
       wait_copies();
       __syncthreads();
       if (n + 1 >= T) break;
       if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), qs0, ds0, ts0, 0);
-      compute(m1, qs1, ds1, ts1, 1);
+      work(m1, qs1, ds1, ts1, 1);
       wait_copies();
       __syncthreads();
     }
   }
-  // rows of this wave's keys; pad key rows are written as zero
-  store_rows<F16>(acc, key < cj ? scale : 0.f, grad + (key0 + wave * 32) * 16,
+  };
+  if (qhalf >= 0) passes(std::true_type());
+  else passes(std::false_type());
+  // query-half pairs: the second wave's partial dK^T (wave 6's in qs1, wave
+  // 7's in ds1, both free after the last barrier) is added to the first's
+  const bool own_pad = split && qhalf == 1;  // waves 6, 7: their own rows are padding
+  if (split) {
+    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(qs1)
+                                        : reinterpret_cast<float*>(ds1);
+    if (own_pad && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) part[(dt * 16 + jj) * 64 + lane] = acc[dt][jj];
+    }
+    __syncthreads();
+    if (qhalf == 0 && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] += part[(dt * 16 + jj) * 64 + lane];
+    }
+    if (own_pad) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+    }
+  }
+  // rows of this wave's own keys; pad key rows are written as zero
+  store_rows<F16>(acc, key < cj && !own_pad ? scale : 0.f, grad + (key0 + wave * 32) * 16,
                   l32, half);
 }
 
@@ -620,8 +806,14 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
-  const int key = wave * 32 + l32;
-  const bool active = wave * 32 < cj;
+  // query-half waves for edge key blocks, as in the dK kernel
+  const int ngroups = (cj + 31) / 32;
+  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
+  const int kgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
+  const int qhalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all queries
+  const int qh = qhalf > 0 ? 1 : 0;
+  const int key = kgroup * 32 + l32;
+  const bool active = kgroup * 32 < cj;
   const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
 
   ev8 kf[8];
@@ -669,10 +861,16 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
   };
   const int kread = l32 * kKRow + half;
   const int vread = l32 * kVRow + half;
-  f32x16 sa[2], sb[2];
+  // operand bases of a query-half wave: queries 32qh .. 32qh+31 of each sub-tile
+  const int kread_h = kread + qh * 32 * kKRow, vread_h = vread + 4 * qh;
 
   const int nent = tcount[c];
   const int32_t* list = tlist + c * int64_t(g.nb);
+  // the passes are compiled twice (full and query-half waves), each with its
+  // own register allocation
+  auto passes = [&](auto hv) __attribute__((always_inline)) {
+  constexpr bool HV = decltype(hv)::value;
+  f32x16 sa[2], sb[2];
   for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
     const int m = min(kPassEntries, nent - e0);
     for (int x = tid; x < m; x += kThreads)
@@ -711,7 +909,7 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
       lse_put(raw, d0, mult_at(0), lbuf[0]);
     }
     __syncthreads();
-    if (active) {
+    if (active && !HV) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -722,6 +920,12 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
         for (int mt = 0; mt < 2; ++mt)
           sa[mt] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), kf[s],
                                       sa[mt]);
+    } else if (active) {
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) sa[0][jj] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        sa[0] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread_h + 2 * s]), kf[s], sa[0]);
     }
     // the first step copies Q_2 into kbuf0: every wave must be done with Q_0
     __syncthreads();
@@ -740,7 +944,68 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
         load_k(d2, kw);
         load_v(d1, vw);
       }
-      if (active) {
+      if (HV && active) {
+        // query-half wave: one 32-query S tile, 8 + 8 MFMA slots
+        uint32_t pw[2][4];
+        ev8 opk[8], opv[8];
+        float4 lq[2][2];
+        auto read_k = [&](int u) { opk[u % 8] = as_ev8(kn[kread_h + 2 * u]); };
+        auto read_v = [&](int w) {
+          opv[w % 8] = as_ev8(vn[vread_h + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
+        };
+        auto read_l = [&](int cc) {  // queries 32qh + 16cc + 8*half + 0..7
+          lq[cc][0] = *reinterpret_cast<const float4*>(lcur + 32 * qh + 16 * cc + 8 * half);
+          lq[cc][1] = *reinterpret_cast<const float4*>(lcur + 32 * qh + 16 * cc + 8 * half + 4);
+        };
+        read_l(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) read_k(u);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) nxt[0][jj] = 0.f;
+        slot_fence();
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if constexpr (kSlotCopies) {
+#pragma unroll
+            for (int x = 0; x < kMaxK; ++x)
+              if (u == 1 + (x * 8) / kMaxK) copy_k(sk, x, kw);
+#pragma unroll
+            for (int x = 0; x < kMaxV; ++x)
+              if (u == 9 + (x * 8) / kMaxV) copy_v(sv, x, vw);
+          }
+          if (u == 1) read_l(1);
+          if (u < 8) {
+            if (u % 4 == 0) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                if (u + 4 < 8) read_k(u + 4 + x);
+                else read_v(x);
+              }
+            }
+            nxt[0] = mfma_32x32x16<F16>(opk[u % 8], kf[u], nxt[0]);
+            // exponential pair u: queries t, t+1 of step u/4
+            const int cc = u / 4, t = 2 * (u % 4);
+            const float4 l4 = lq[cc][t / 4];
+            const float la = (t % 4 == 0) ? l4.x : l4.z;
+            const float lb = (t % 4 == 0) ? l4.y : l4.w;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[0][8 * cc + t], scale_log2, -la));
+            const float p1 =
+                __builtin_amdgcn_exp2f(fmaf(cur[0][8 * cc + t + 1], scale_log2, -lb));
+            pw[cc][t / 2] = pack2<F16>(p0, p1);
+            pin_v(pw[cc][t / 2]);
+          } else {
+            const int w = u - 8, cc = w / 4, dt = w % 4;
+            if (w == 0) {
+#pragma unroll
+              for (int x = 0; x < 4; ++x) read_v(4 + x);
+            }
+            const ev8 pb = __builtin_bit_cast(
+                ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+            acc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, acc[dt]);
+          }
+          slot_fence();
+        }
+      } else if (!HV && active) {
         uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 dV steps
         ev8 opk[8], opv[8];
         float4 lq[4][2];    // lse of the 8 queries of each dV step
@@ -836,8 +1101,38 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
       if (n >= T) break;
     }
   }
-  // rows of this wave's keys; pad key rows are written as zero
-  store_rows<F16>(acc, key < cj ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32, half);
+  };
+  if (qhalf >= 0) passes(std::true_type());
+  else passes(std::false_type());
+  // query-half pairs: the second wave's partial dV^T (wave 6's in kbuf1, wave
+  // 7's in vbuf1, both free after the last barrier) is added to the first's
+  const bool own_pad = split && qhalf == 1;  // waves 6, 7: their own rows are padding
+  if (split) {
+    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(kbuf1)
+                                        : reinterpret_cast<float*>(vbuf1);
+    if (own_pad && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) part[(dt * 16 + jj) * 64 + lane] = acc[dt][jj];
+    }
+    __syncthreads();
+    if (qhalf == 0 && active) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] += part[(dt * 16 + jj) * 64 + lane];
+    }
+    if (own_pad) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+    }
+  }
+  // rows of this wave's own keys; pad key rows are written as zero
+  store_rows<F16>(acc, key < cj && !own_pad ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32,
+                  half);
 }
 
 template <int NW, bool F16>
