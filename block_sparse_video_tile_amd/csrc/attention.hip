@@ -9,7 +9,9 @@
 //
 // Work decomposition
 //   One workgroup per CSR row r = (b*NH + h)*nb + i, i.e. one query block of
-//   V = 32*NW tokens; wave w owns query rows 32w .. 32w+31.  Row ids are
+//   V = 32*NW tokens; wave w owns query rows 32w .. 32w+31 (in an 8-wave
+//   block cut by the grid edge to 5 or 6 row groups, waves 4..7 instead share
+//   the last groups by key halves: see the key-half waves below).  Row ids are
 //   remapped so that each of the 8 XCDs (workgroups are dispatched to XCDs
 //   round-robin) works through a contiguous range of rows, i.e. the same
 //   heads, and its L2 serves their shared key/value blocks.
