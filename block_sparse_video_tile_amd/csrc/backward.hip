@@ -122,26 +122,35 @@ __device__ inline void row_bounds(const int32_t* row_ptr, int uniform_k, int64_t
 
 // Transposed block map: for (bh, j), the ascending query blocks i whose row
 // lists j, packed as i | min(multiplicity, 65535) << 16, and their count.
-// One workgroup per (b, h); thread t handles columns t, t + 256, ...
+// One wave per column (b, h, j): lane t counts j in row i0 + t of each block
+// of 64 rows, and a ballot places the rows that list j in ascending order.
 __global__ __launch_bounds__(256) void tmap_kernel(const int32_t* __restrict__ row_ptr,
                                                    const int32_t* __restrict__ col,
                                                    int uniform_k, int64_t nnz,
                                                    int32_t* __restrict__ tlist,
                                                    int32_t* __restrict__ tcount, VsaGeom g) {
   const int nb = g.nb;
-  const int64_t bh = blockIdx.x;
-  for (int j = threadIdx.x; j < nb; j += 256) {
-    int cnt = 0;
-    int32_t* out = tlist + (bh * nb + j) * int64_t(nb);
-    for (int i = 0; i < nb; ++i) {
+  const int64_t ncols = int64_t(g.batch) * g.heads * nb;
+  const int64_t task = int64_t(blockIdx.x) * 4 + threadIdx.x / 64;  // wave-uniform
+  if (task >= ncols) return;
+  const int64_t bh = task / nb;
+  const int j = int(task % nb);
+  const int lane = threadIdx.x % 64;
+  int32_t* out = tlist + task * int64_t(nb);
+  int cnt = 0;
+  for (int i0 = 0; i0 < nb; i0 += 64) {
+    const int i = i0 + lane;
+    int m = 0;
+    if (i < nb) {
       int64_t beg, end;
       row_bounds(row_ptr, uniform_k, nnz, bh * nb + i, beg, end);
-      int m = 0;
       for (int64_t e = beg; e < end; ++e) m += col[e] == j ? 1 : 0;
-      if (m > 0) out[cnt++] = i | (min(m, 65535) << 16);
     }
-    tcount[bh * nb + j] = cnt;
+    const uint64_t listed = __ballot(m > 0);
+    if (m > 0) out[cnt + __popcll(listed & ((uint64_t(1) << lane) - 1))] = i | (min(m, 65535) << 16);
+    cnt += __popcll(listed);
   }
+  if (lane == 0) tcount[task] = cnt;
 }
 
 // Per-lane copy offsets (16-byte units inside one 64-token sub-tile) of the
@@ -1188,8 +1197,8 @@ hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
                        static_cast<const uint4*>(srcs[t]), static_cast<uint4*>(dsts[t]));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(tmap_kernel, dim3(unsigned(int64_t(g.batch) * g.heads)), dim3(256), 0, s,
-                     a.row_ptr, a.col, a.uniform_k, a.nnz, a.tlist, a.tcount, g);
+  hipLaunchKernelGGL(tmap_kernel, dim3(unsigned((int64_t(g.batch) * g.heads * g.nb + 3) / 4)),
+                     dim3(256), 0, s, a.row_ptr, a.col, a.uniform_k, a.nnz, a.tlist, a.tcount, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (g.vol / 32) {
     case 2: return launch_bwd_typed<2>(g, a, s);
