@@ -6,6 +6,10 @@ block-major form, score the pooled blocks and pick the top-k per query block,
 run the block-sparse attention, scatter O back to raster order.  Every stage is
 a kernel of libvsa_amd.so launched through the C ABI on torch's current
 stream; HIP events on that stream bracket each stage of every timed step.
+The attention stage is the balanced launch (vsa_block_sparse_attn_fwd_ws:
+workgroups claim rows from per-XCD queues; a one-block counter reset kernel
+runs first and is inside the stage's time); --fixed-order times the launch
+with one workgroup per row in a fixed order instead (same results).
 
 Metric: effective TFLOP/s counting the selected blocks' valid tokens only
 (4 * D * sum over query blocks i of c_i * sum_{j in row i} c_j, from the map
@@ -265,6 +269,9 @@ def main():
     ap.add_argument("--gated", action="store_true",
                     help="also run the gate-compress branch (pooled V, coarse attention, "
                          "gated scatter) with a synthetic gate")
+    ap.add_argument("--fixed-order", action="store_true",
+                    help="attention with one workgroup per row in a fixed order instead of "
+                         "the balanced launch (rows claimed from per-XCD queues)")
     ap.add_argument("--fused", action="store_true",
                     help="gather-free path: pool Q and K from the raster tensors, score/top-k, "
                          "raster attention writing the raster output (no gather or scatter)")
@@ -338,6 +345,16 @@ def main():
         col = torch.as_tensor(ci_host).to(dev)
         uk, nnz = 0, col.numel()
     stream = torch.cuda.current_stream(dev)
+    # row queues of the balanced attention launch
+    attn_ws = torch.empty(vsa.vsa_attn_fwd_workspace_size(plan), dtype=torch.uint8, device=dev)
+
+    def raster_attention(**gated):
+        if args.fixed_order:
+            vsa.vsa_block_sparse_attn_fwd_raster(plan, dq, dk, dv, rp_dev, col, uk, nnz, out,
+                                                 **gated)
+        else:
+            vsa.vsa_block_sparse_attn_fwd_raster_ws(plan, dq, dk, dv, rp_dev, col, uk, nnz, out,
+                                                    attn_ws, **gated)
 
     def fused_step(ev=None):
         def mark(n):
@@ -356,10 +373,9 @@ def main():
             mark(4)
             vsa.vsa_compress_attn(plan, qp, kp, vp, oc)
             mark(5)
-            vsa.vsa_block_sparse_attn_fwd_raster(plan, dq, dk, dv, rp_dev, col, uk, nnz, out,
-                                                 gate=gate, o_coarse=oc)
+            raster_attention(gate=gate, o_coarse=oc)
         else:
-            vsa.vsa_block_sparse_attn_fwd_raster(plan, dq, dk, dv, rp_dev, col, uk, nnz, out)
+            raster_attention()
         mark(len(stages))
 
     def step(ev=None):
@@ -379,7 +395,10 @@ def main():
         if wl.topk:
             vsa.vsa_score_topk(plan, qp, kp, wl.topk, col)
         mark(4)
-        vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vb, rp_dev, col, uk, nnz, ob)
+        if args.fixed_order:
+            vsa.vsa_block_sparse_attn_fwd(plan, qb, kb, vb, rp_dev, col, uk, nnz, ob)
+        else:
+            vsa.vsa_block_sparse_attn_fwd_ws(plan, qb, kb, vb, rp_dev, col, uk, nnz, ob, attn_ws)
         mark(5)
         if args.gated:
             vsa.vsa_compress_attn(plan, qp, kp, vp, oc)
@@ -434,6 +453,7 @@ def main():
                    "heads": wl.heads, "head_dim": wl.head_dim, "batch": wl.batch,
                    "topk": wl.topk, "num_blocks": plan.num_blocks,
                    "gate_compress": bool(args.gated), "gather_free": bool(args.fused),
+                   "attention_launch": "fixed order" if args.fixed_order else "balanced",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -24,7 +24,8 @@ __all__ = [
     "vsa_block_sparse_attn_fwd", "vsa_block_sparse_attn_bwd_workspace_size",
     "vsa_block_sparse_attn_bwd", "vsa_compress_attn", "vsa_scatter_gated",
     "vsa_forward_workspace_size", "vsa_forward", "vsa_block_sparse_attn_fwd_raster",
-    "vsa_forward_fused_workspace_size", "vsa_forward_fused", "vsa_status_string",
+    "vsa_forward_fused_workspace_size", "vsa_forward_fused", "vsa_attn_fwd_workspace_size",
+    "vsa_block_sparse_attn_fwd_ws", "vsa_block_sparse_attn_fwd_raster_ws", "vsa_status_string",
     "vsa_last_error",
 ]
 
@@ -86,6 +87,12 @@ _SIGS = {
     "vsa_forward_fused_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "vsa_forward_fused": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P, _P],
                           ctypes.c_int),
+    "vsa_attn_fwd_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
+    "vsa_block_sparse_attn_fwd_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P,
+                                      _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "vsa_block_sparse_attn_fwd_raster_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                             ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                             _P], ctypes.c_int),
     "vsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "vsa_last_error": ([], ctypes.c_char_p),
 }
@@ -344,6 +351,58 @@ def vsa_block_sparse_attn_fwd_raster(plan: Plan, q, k, v, row_ptr, col_idx, unif
         _stream(stream, q, o_raster)))
 
 
+def vsa_attn_fwd_workspace_size(plan: Plan) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().vsa_attn_fwd_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(workspace, ws_bytes):
+    """Device pointer and byte size of a workspace tensor (or a raw pointer)."""
+    import torch
+    if isinstance(workspace, torch.Tensor):
+        if workspace.numel() * workspace.element_size() < ws_bytes:
+            raise ValueError(f"workspace: fewer than {ws_bytes} bytes")
+        return _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
+    return int(workspace), ws_bytes
+
+
+def vsa_block_sparse_attn_fwd_ws(plan: Plan, q_blk, k_blk, v_blk, row_ptr, col_idx,
+                                 uniform_k: int, nnz: int, o_blk, workspace, lse=None,
+                                 stream=None):
+    """vsa_block_sparse_attn_fwd with rows claimed from per-XCD queues (balanced launch)."""
+    be = plan.info["blocked_elems"]
+    rows = plan.num_rows()
+    et = plan.torch_dtype()
+    ws_ptr, ws_len = _workspace(workspace, vsa_attn_fwd_workspace_size(plan))
+    _check(load_library().vsa_block_sparse_attn_fwd_ws(
+        plan.handle, _ptr(q_blk, be, et, "q_blk"), _ptr(k_blk, be, et, "k_blk"),
+        _ptr(v_blk, be, et, "v_blk"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
+        _ptr(col_idx, int(nnz), _i32(), "col_idx"), int(uniform_k), int(nnz),
+        _ptr(o_blk, be, et, "o_blk"),
+        _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
+        ws_ptr, ws_len, _stream(stream, q_blk, o_blk)))
+
+
+def vsa_block_sparse_attn_fwd_raster_ws(plan: Plan, q, k, v, row_ptr, col_idx, uniform_k: int,
+                                        nnz: int, o_raster, workspace, lse=None, stream=None,
+                                        gate=None, o_coarse=None):
+    """vsa_block_sparse_attn_fwd_raster with rows claimed from per-XCD queues (balanced launch)."""
+    n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
+    rows = plan.num_rows()
+    et = plan.torch_dtype()
+    ws_ptr, ws_len = _workspace(workspace, vsa_attn_fwd_workspace_size(plan))
+    _check(load_library().vsa_block_sparse_attn_fwd_raster_ws(
+        plan.handle, _ptr(q, n_raster, et, "q"), _ptr(k, n_raster, et, "k"),
+        _ptr(v, n_raster, et, "v"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
+        _ptr(col_idx, int(nnz), _i32(), "col_idx"), int(uniform_k), int(nnz),
+        _ptr(gate, n_raster, et, "gate"),
+        _ptr(o_coarse, plan.info["pooled_elems"], _f32(), "o_coarse"),
+        _ptr(o_raster, n_raster, et, "o_raster"),
+        _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
+        ws_ptr, ws_len, _stream(stream, q, o_raster)))
+
+
 def vsa_forward_fused_workspace_size(plan: Plan) -> int:
     n = ctypes.c_size_t()
     _check(load_library().vsa_forward_fused_workspace_size(plan.handle, ctypes.byref(n)))
@@ -410,15 +469,9 @@ def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
                 gate=None, fused=False):
     """The whole hot path, raster in and out; fused=True calls vsa_forward_fused
     (no gather or scatter passes) with its own, smaller workspace."""
-    import torch
     n_raster = plan.batch * plan.seq_len * plan.heads * plan.head_dim
     ws_bytes = (vsa_forward_fused_workspace_size if fused else vsa_forward_workspace_size)(plan)
-    if isinstance(workspace, torch.Tensor):
-        if workspace.numel() * workspace.element_size() < ws_bytes:
-            raise ValueError(f"workspace: fewer than {ws_bytes} bytes")
-        ws_ptr, ws_len = _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size()
-    else:
-        ws_ptr, ws_len = int(workspace), ws_bytes
+    ws_ptr, ws_len = _workspace(workspace, ws_bytes)
     et = plan.torch_dtype()
     lib = load_library()
     _check((lib.vsa_forward_fused if fused else lib.vsa_forward)(

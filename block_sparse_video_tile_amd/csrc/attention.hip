@@ -74,6 +74,7 @@
 // when the max grows by more than 2^8 (so p <= 256).  Padded keys of a partial sub-tile are masked
 // to -inf.  A row without blocks leaves l = 0 and writes O = 0, LSE = -inf.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -147,6 +148,45 @@ __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Dynamic row assignment of the balanced launch.  The rows are cut into 8
+// queues of consecutive rows (the ranges xcd_remap gives the XCDs, i.e.
+// whole heads).  queues[8] hands out tickets and queues[x] counts the rows
+// taken from queue x; all start at zero.  The launch has more workgroups
+// than rows; a workgroup whose ticket is below the row count takes the next
+// row of its own XCD's queue or, once that is empty, of the other queues in
+// turn, and the others leave at once.  Each XCD works through its share of
+// the workgroups as its CUs free up, so an XCD that runs faster takes more
+// rows.  A ticket holder always finds a row: a queue it finds empty stays
+// empty, and if all 8 were empty every row would already be held by one of
+// the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
+// reaches the workgroup through LDS.
+__device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, int64_t* row_sh) {
+  if (threadIdx.x == 0) {
+    int64_t row = -1;
+    if (atomicAdd(&queues[8], 1u) < uint64_t(nrows)) {
+      const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
+      const int64_t per = nrows / 8, rem = nrows % 8;
+      for (int j = 0; j < 8; ++j) {
+        const int x = (home + j) & 7;
+        const int64_t count = per + (x < rem ? 1 : 0);
+        if (count == 0) continue;
+        const unsigned int t = atomicAdd(&queues[x], 1u);
+        if (t < uint64_t(count)) {
+          row = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
+          break;
+        }
+      }
+    }
+    *row_sh = row;
+  }
+  __syncthreads();
+  return *row_sh;
+}
+
+__global__ void queue_reset_kernel(unsigned int* queues) {
+  if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
+}
+
 // Row max over the 16 scores of one tile.
 __device__ inline float tile_max1(const f32x16& st) {
   float mx = st[0];
@@ -173,7 +213,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
     int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, const uint4* __restrict__ gate,
-    const float* __restrict__ oc, VsaGeom g, float scale_log2, float scale) {
+    const float* __restrict__ oc, unsigned int* __restrict__ queues, VsaGeom g, float scale_log2,
+    float scale) {
   static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits), "O staging must fit in LDS");
   const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
   // Sub-tile buffers.  K runs one sub-tile ahead of V: while sub-tile n is
@@ -196,7 +237,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   __shared__ uint32_t soff[RASTER ? 8 * kVol : 1];
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
-  const int64_t r = xcd_remap(blockIdx.x, nrows);
+  // The row: fixed by the workgroup index (XCD-aware order), or, with
+  // `queues`, claimed at start-up (claim_row); a workgroup that finds every
+  // row taken leaves at once (workgroup-uniform, before any other barrier).
+  __shared__ int64_t row_sh;
+  const int64_t r = queues != nullptr ? claim_row(queues, nrows, &row_sh)
+                                      : xcd_remap(blockIdx.x, nrows);
+  if (r < 0) return;
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
@@ -836,14 +883,24 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
 template <int NW, bool F16, bool RASTER>
 hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
-                     void* o, float* lse, const void* gate, const float* oc, hipStream_t s) {
+                     void* o, float* lse, const void* gate, const float* oc,
+                     unsigned int* queues, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16, RASTER>), dim3(unsigned(rows)), dim3(NW * 64), 0,
+  int64_t grid = rows;
+  if (queues != nullptr) {
+    // a quarter more workgroups than rows, so that each XCD can take up to
+    // 1.25 times its share; the counters are cleared first on the same stream
+    grid = rows + std::max<int64_t>(8, rows / 4);
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, queues);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16, RASTER>), dim3(unsigned(grid)), dim3(NW * 64), 0,
                      s, static_cast<const uint4*>(q), static_cast<const uint4*>(k),
                      static_cast<const uint4*>(v), row_ptr, col, uniform_k, nnz,
-                     static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, g,
+                     static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, queues, g,
                      scale_log2, scale);
   return hipGetLastError();
 }
@@ -851,14 +908,15 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
 template <bool RASTER>
 hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void* v,
                       const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
-                      void* o, float* lse, const void* gate, const float* oc, hipStream_t s) {
+                      void* o, float* lse, const void* gate, const float* oc,
+                      unsigned int* queues, hipStream_t s) {
   auto launch = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
     return g.dtype == VSA_DTYPE_FP16
                ? launch_nw<NW, true, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                             gate, oc, s)
+                                             gate, oc, queues, s)
                : launch_nw<NW, false, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                              gate, oc, s);
+                                              gate, oc, queues, s);
   };
   switch (g.vol / 32) {
     case 2: return launch(std::integral_constant<int, 2>());
@@ -873,16 +931,17 @@ hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void
 
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
-                           int64_t nnz, void* o, float* lse, hipStream_t s) {
+                           int64_t nnz, void* o, float* lse, unsigned int* queues,
+                           hipStream_t s) {
   return launch_any<false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, nullptr, nullptr,
-                           s);
+                           queues, s);
 }
 
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
                                   const int32_t* row_ptr, const int32_t* col, int uniform_k,
                                   int64_t nnz, void* o, float* lse, const void* gate,
-                                  const float* oc, hipStream_t s) {
-  return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, s);
+                                  const float* oc, unsigned int* queues, hipStream_t s) {
+  return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, queues, s);
 }
 
 }  // namespace vsa

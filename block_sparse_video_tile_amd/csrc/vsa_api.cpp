@@ -38,7 +38,7 @@ vsa_status hip_status(hipError_t e, const char* what) {
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct Workspace {
-  size_t q, k, v, o, qp, kp, vp, oc, col, total;
+  size_t q, k, v, o, qp, kp, vp, oc, col, queue, total;
 };
 
 Workspace workspace_layout(const vsa_plan_s& p) {
@@ -57,6 +57,7 @@ Workspace workspace_layout(const vsa_plan_s& p) {
   w.vp = off; off += align256(pooled);
   w.oc = off; off += align256(pooled);
   w.col = off; off += align256(col);
+  w.queue = off; off += vsa::kAttnQueueBytes;
   w.total = off;
   return w;
 }
@@ -64,7 +65,7 @@ Workspace workspace_layout(const vsa_plan_s& p) {
 // Workspace of the raster (gather-free) forward: pooled Q, K (and V and the
 // coarse output for the gated branch) and the selected block ids.
 struct FusedWorkspace {
-  size_t qp, kp, vp, oc, col, total;
+  size_t qp, kp, vp, oc, col, queue, total;
 };
 FusedWorkspace fused_workspace_layout(const vsa_plan_s& p) {
   const VsaGeom& g = p.g;
@@ -77,6 +78,7 @@ FusedWorkspace fused_workspace_layout(const vsa_plan_s& p) {
   w.vp = off; off += align256(pooled);
   w.oc = off; off += align256(pooled);
   w.col = off; off += align256(col);
+  w.queue = off; off += vsa::kAttnQueueBytes;
   w.total = off;
   return w;
 }
@@ -294,64 +296,113 @@ vsa_status vsa_score_topk(vsa_plan_t p, const float* qp, const float* kp, int32_
                     "vsa_score_topk");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the attention entry points; returns ok() or the
+// failure status (with its reason recorded).
+vsa_status check_attn_args(const char* fn, vsa_plan_t p, const void* q, const void* k,
+                           const void* v, const int32_t* row_ptr, const int32_t* col,
+                           int32_t uniform_k, int64_t nnz, void* o) {
+  if (!p || !q || !k || !v || !o) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null argument", fn);
+  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: nnz < 0", fn);
+  if (nnz > 0 && !col)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null col_idx with nnz > 0", fn);
+  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
+  if (!row_ptr) {
+    if (uniform_k < 0 || uniform_k > p->g.nb)
+      return fail(VSA_ERR_INVALID_ARGUMENT, "%s: uniform_k %d outside [0, %d]", fn, uniform_k,
+                  p->g.nb);
+    if (nnz < rows * uniform_k)
+      return fail(VSA_ERR_INVALID_ARGUMENT, "%s: nnz %lld < rows*uniform_k = %lld", fn,
+                  (long long)nnz, (long long)(rows * uniform_k));
+  }
+  return ok();
+}
+
+vsa_status check_raster_args(const char* fn, vsa_plan_t p, const void* gate, const float* oc) {
+  if ((gate == nullptr) != (oc == nullptr))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: gate and o_coarse must both be given or both NULL",
+                fn);
+  if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: o_coarse not 16-byte aligned", fn);
+  if (const char* why = raster_unsupported(p->g))
+    return fail(VSA_ERR_UNSUPPORTED, "%s: %s", fn, why);
+  return ok();
+}
+
+// The row-queue counters of the balanced attention launch.
+vsa_status check_queue_workspace(const char* fn, void* ws, size_t ws_bytes) {
+  if (!ws) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null workspace", fn);
+  if (ws_bytes < vsa::kAttnQueueBytes)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
+                vsa::kAttnQueueBytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: workspace not 256-byte aligned", fn);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k, const void* v,
                                      const int32_t* row_ptr, const int32_t* col,
                                      int32_t uniform_k, int64_t nnz, void* o, float* lse,
                                      void* stream) {
-  if (!p || !q || !k || !v || !o)
-    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: null argument");
-  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: nnz < 0");
-  if (nnz > 0 && !col)
-    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd: null col_idx with nnz > 0");
-  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
-  if (!row_ptr) {
-    if (uniform_k < 0 || uniform_k > p->g.nb)
-      return fail(VSA_ERR_INVALID_ARGUMENT,
-                  "vsa_block_sparse_attn_fwd: uniform_k %d outside [0, %d]", uniform_k, p->g.nb);
-    if (nnz < rows * uniform_k)
-      return fail(VSA_ERR_INVALID_ARGUMENT,
-                  "vsa_block_sparse_attn_fwd: nnz %lld < rows*uniform_k = %lld", (long long)nnz,
-                  (long long)(rows * uniform_k));
-  }
+  static const char* fn = "vsa_block_sparse_attn_fwd";
+  if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                         hipStream_t(stream)),
-                    "vsa_block_sparse_attn_fwd");
+                                         nullptr, hipStream_t(stream)),
+                    fn);
 }
 
+vsa_status vsa_attn_fwd_workspace_size(vsa_plan_t p, size_t* bytes) {
+  if (!p || !bytes) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_attn_fwd_workspace_size: null");
+  *bytes = vsa::kAttnQueueBytes;
+  return ok();
+}
+
+vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t p, const void* q, const void* k, const void* v,
+                                        const int32_t* row_ptr, const int32_t* col,
+                                        int32_t uniform_k, int64_t nnz, void* o, float* lse,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  static const char* fn = "vsa_block_sparse_attn_fwd_ws";
+  if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
+  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                         static_cast<unsigned int*>(ws), hipStream_t(stream)),
+                    fn);
+}
 
 vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const void* k,
                                             const void* v, const int32_t* row_ptr,
                                             const int32_t* col, int32_t uniform_k, int64_t nnz,
                                             const void* gate, const float* oc, void* o,
                                             float* lse, void* stream) {
-  if (!p || !q || !k || !v || !o)
-    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd_raster: null argument");
-  if ((gate == nullptr) != (oc == nullptr))
-    return fail(VSA_ERR_INVALID_ARGUMENT,
-                "vsa_block_sparse_attn_fwd_raster: gate and o_coarse must both be given or both NULL");
-  if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
-    return fail(VSA_ERR_INVALID_ARGUMENT,
-                "vsa_block_sparse_attn_fwd_raster: o_coarse not 16-byte aligned");
-  if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_block_sparse_attn_fwd_raster: nnz < 0");
-  if (nnz > 0 && !col)
-    return fail(VSA_ERR_INVALID_ARGUMENT,
-                "vsa_block_sparse_attn_fwd_raster: null col_idx with nnz > 0");
-  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
-  if (!row_ptr) {
-    if (uniform_k < 0 || uniform_k > p->g.nb)
-      return fail(VSA_ERR_INVALID_ARGUMENT,
-                  "vsa_block_sparse_attn_fwd_raster: uniform_k %d outside [0, %d]", uniform_k,
-                  p->g.nb);
-    if (nnz < rows * uniform_k)
-      return fail(VSA_ERR_INVALID_ARGUMENT,
-                  "vsa_block_sparse_attn_fwd_raster: nnz %lld < rows*uniform_k = %lld",
-                  (long long)nnz, (long long)(rows * uniform_k));
-  }
-  if (const char* why = raster_unsupported(p->g))
-    return fail(VSA_ERR_UNSUPPORTED, "vsa_block_sparse_attn_fwd_raster: %s", why);
+  static const char* fn = "vsa_block_sparse_attn_fwd_raster";
+  if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
-                                                lse, gate, oc, hipStream_t(stream)),
-                    "vsa_block_sparse_attn_fwd_raster");
+                                                lse, gate, oc, nullptr, hipStream_t(stream)),
+                    fn);
+}
+
+vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t p, const void* q, const void* k,
+                                               const void* v, const int32_t* row_ptr,
+                                               const int32_t* col, int32_t uniform_k, int64_t nnz,
+                                               const void* gate, const float* oc, void* o,
+                                               float* lse, void* ws, size_t ws_bytes,
+                                               void* stream) {
+  static const char* fn = "vsa_block_sparse_attn_fwd_raster_ws";
+  if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
+  if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
+  return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
+                                                lse, gate, oc, static_cast<unsigned int*>(ws),
+                                                hipStream_t(stream)),
+                    fn);
 }
 
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t p, size_t* bytes) {
@@ -446,7 +497,9 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
     return hip_status(e, "vsa_forward: gather V");
   if ((e = vsa::launch_score_topk(g, qp, kp, p->topk, col, nullptr, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: score/top-k");
-  if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, s)) != hipSuccess)
+  unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
+  if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, queues, s)) !=
+      hipSuccess)
     return hip_status(e, "vsa_forward: attention");
   if (gate && (e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: coarse attention");
@@ -502,8 +555,9 @@ vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const v
     if ((e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
       return hip_status(e, "vsa_forward_fused: coarse attention");
   }
+  unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
   if ((e = vsa::launch_attn_fwd_raster(g, q, k, v, nullptr, col, p->topk, nnz, out, lse, gate,
-                                       gate ? oc : nullptr, s)) != hipSuccess)
+                                       gate ? oc : nullptr, queues, s)) != hipSuccess)
     return hip_status(e, "vsa_forward_fused: attention");
   return ok();
 }

@@ -75,14 +75,19 @@ hipError_t launch_compress_attn(const VsaGeom& g, const float* qp, const float* 
                                 const float* vp, float* oc, hipStream_t s);
 hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp, int topk,
                              int32_t* col, float* scores, hipStream_t s);
+// queues == nullptr: one workgroup per row in a fixed order; otherwise 9
+// device counters (kAttnQueueBytes of workspace) from which the workgroups
+// of a larger launch claim their rows.
+constexpr size_t kAttnQueueBytes = 256;
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
-                           int64_t nnz, void* o, float* lse, hipStream_t s);
+                           int64_t nnz, void* o, float* lse, unsigned int* queues,
+                           hipStream_t s);
 // Raster [B,S,NH,D] q, k, v and o; gate (raster) and oc (fp32 [B,NH,nb,D])
 // optional: o = attention + gate * oc[block].
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
                                   const int32_t* row_ptr, const int32_t* col, int uniform_k,
                                   int64_t nnz, void* o, float* lse, const void* gate,
-                                  const float* oc, hipStream_t s);
+                                  const float* oc, unsigned int* queues, hipStream_t s);
 
 }  // namespace vsa

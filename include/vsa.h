@@ -238,6 +238,37 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t plan, const void* q, cons
                                             const float* o_coarse, void* o_raster, float* lse,
                                             void* stream);
 
+/* Balanced launches of the two attention forwards above: the same operation
+ * and the same arguments, bit-identical results, plus a small device
+ * workspace.  Instead of a fixed row per workgroup, each workgroup of a
+ * launch with a quarter more workgroups than rows takes the next row from
+ * one of 8 row queues (one per XCD, each a contiguous range of rows, i.e.
+ * whole heads): its own XCD's queue, or once that is empty the others', and
+ * the workgroups left over when every row is taken exit at once.  XCDs that
+ * run faster thus finish more rows and the kernel does not wait for the
+ * slowest one.  The queue counters live in the workspace and are cleared
+ * by a kernel on `stream` before the attention kernel, so the workspace needs
+ * no initialisation; it must not be used by another call while this one runs
+ * (concurrent calls need their own workspaces).
+ * vsa_attn_fwd_workspace_size writes the bytes needed (a few hundred, the
+ *   same for every plan).
+ * ws: device memory, 256-byte aligned, ws_bytes at least that size; owned by
+ *   the caller.
+ * Errors: as the unbalanced entry points, plus INVALID_ARGUMENT for a null,
+ *   misaligned or too small workspace. */
+vsa_status vsa_attn_fwd_workspace_size(vsa_plan_t plan, size_t* bytes);
+vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t plan, const void* q_blk, const void* k_blk,
+                                        const void* v_blk, const int32_t* row_ptr,
+                                        const int32_t* col_idx, int32_t uniform_k, int64_t nnz,
+                                        void* o_blk, float* lse, void* ws, size_t ws_bytes,
+                                        void* stream);
+vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t plan, const void* q, const void* k,
+                                               const void* v, const int32_t* row_ptr,
+                                               const int32_t* col_idx, int32_t uniform_k,
+                                               int64_t nnz, const void* gate,
+                                               const float* o_coarse, void* o_raster, float* lse,
+                                               void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
  * rowsum(dO*O) [B,NH,Npad] fp32, d-major copies of K, Q and dO, and the
  * transposed block map (B*NH*nb*nb + B*NH*nb int32), each 256-byte aligned. */
@@ -269,13 +300,15 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t plan, const void* q_blk, const v
                                      size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace vsa_forward needs for this plan (blocked Q, K,
- * V, O, pooled Q, K and V, the coarse output, and the selected block ids,
- * each 256-byte aligned). */
+ * V, O, pooled Q, K and V, the coarse output, the selected block ids and the
+ * row queues of the balanced attention launch, each 256-byte aligned). */
 vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path for a plan with topk >= 1, raster in and raster out:
  * gather Q, K (with pooling) and V; score and top-k; block-sparse attention;
- * scatter O.  q, k, v: device elem raster.  out: device elem raster.
+ * scatter O.  The attention step is the balanced launch of
+ * vsa_block_sparse_attn_fwd_ws.  q, k, v: device elem raster.  out: device
+ * elem raster.
  * gate: device elem raster [B,S,NH,D] or NULL.  NULL runs the sparse branch
  * alone (the guide's "Checkpoint behavior": without to_gate_compress
  * weights there is no compensation); otherwise V is pooled too, the coarse
@@ -291,13 +324,13 @@ vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void
                        int32_t* col_idx_out, float* lse, void* stream);
 
 /* Bytes of device workspace vsa_forward_fused needs for this plan (pooled Q,
- * K and V, the coarse output and the selected block ids, each 256-byte
- * aligned; no blocked copies of the tensors). */
+ * K and V, the coarse output, the selected block ids and the attention row
+ * queues, each 256-byte aligned; no blocked copies of the tensors). */
 vsa_status vsa_forward_fused_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path without the gather and scatter passes: the block means
  * of Q and K are read from the raster tensors (vsa_gather with x_blk NULL),
- * score and top-k select the blocks, and vsa_block_sparse_attn_fwd_raster
+ * score and top-k select the blocks, and vsa_block_sparse_attn_fwd_raster_ws
  * attends and writes the raster output.  With `gate` the means of V and the
  * coarse branch are computed first and the attention epilogue writes
  * O + gate * o_coarse[block] as vsa_scatter_gated does.  Arguments, outputs

@@ -243,3 +243,38 @@ def test_raster_attention_and_fused_forward_checks(plan):
                 None) == bad
     # pooling alone: x_blk NULL needs `pooled`
     assert _raw("vsa_gather", h, 2, FAKE, None, None, None) == bad
+
+
+def test_balanced_attention_workspace_checks(plan):
+    """The balanced (queued) attention launches: a fixed small workspace, the
+    same argument checks as the plain entry points, and a null, short or
+    misaligned workspace rejected before any device call."""
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    need = vsa.vsa_attn_fwd_workspace_size(plan)
+    assert need == 256
+    big = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), batch=1, num_heads=24, topk=64)
+    assert vsa.vsa_attn_fwd_workspace_size(big) == need
+    f = "vsa_block_sparse_attn_fwd_ws"
+    # (plan, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, ws, ws_bytes, stream)
+    rows = plan.num_rows()
+    ok_args = (FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None)
+    assert _raw(f, h, *ok_args, None, need, None) == bad
+    assert "null workspace" in vsa.vsa_last_error()
+    assert _raw(f, h, *ok_args, FAKE, need - 1, None) == bad
+    assert _raw(f, h, *ok_args, FAKE + 16, need, None) == bad
+    assert "256-byte" in vsa.vsa_last_error()
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 9, 9 * rows, FAKE, None, FAKE, need,
+                None) == bad   # uniform_k > nb, as the plain entry point
+    assert _raw(f, h, FAKE, FAKE, None, None, FAKE, 4, rows * 4, FAKE, None, FAKE, need,
+                None) == bad
+    g = "vsa_block_sparse_attn_fwd_raster_ws"
+    # (plan, q, k, v, row_ptr, col, uniform_k, nnz, gate, o_coarse, o, lse, ws, ws_bytes, stream)
+    r_args = (FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4)
+    assert _raw(g, h, *r_args, None, None, FAKE, None, None, need, None) == bad
+    assert _raw(g, h, *r_args, None, None, FAKE, None, FAKE, need - 256, None) == bad
+    assert _raw(g, h, *r_args, FAKE, None, FAKE, None, FAKE, need, None) == bad
+    assert "gate and o_coarse" in vsa.vsa_last_error()
+    # the layer entry points carry the queues in their own workspaces
+    assert vsa.vsa_forward_workspace_size(plan) % 256 == 0
+    assert vsa.vsa_forward_fused_workspace_size(plan) % 256 == 0
