@@ -148,41 +148,6 @@ __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-// Dynamic row assignment of the balanced launch.  The rows are cut into 8
-// queues of consecutive rows (the ranges xcd_remap gives the XCDs, i.e.
-// whole heads).  queues[8] hands out tickets and queues[x] counts the rows
-// taken from queue x; all start at zero.  The launch has more workgroups
-// than rows; a workgroup whose ticket is below the row count takes the next
-// row of its own XCD's queue or, once that is empty, of the other queues in
-// turn, and the others leave at once.  Each XCD works through its share of
-// the workgroups as its CUs free up, so an XCD that runs faster takes more
-// rows.  A ticket holder always finds a row: a queue it finds empty stays
-// empty, and if all 8 were empty every row would already be held by one of
-// the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
-// reaches the workgroup through LDS.
-__device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, int64_t* row_sh) {
-  if (threadIdx.x == 0) {
-    int64_t row = -1;
-    if (atomicAdd(&queues[8], 1u) < uint64_t(nrows)) {
-      const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
-      const int64_t per = nrows / 8, rem = nrows % 8;
-      for (int j = 0; j < 8; ++j) {
-        const int x = (home + j) & 7;
-        const int64_t count = per + (x < rem ? 1 : 0);
-        if (count == 0) continue;
-        const unsigned int t = atomicAdd(&queues[x], 1u);
-        if (t < uint64_t(count)) {
-          row = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
-          break;
-        }
-      }
-    }
-    *row_sh = row;
-  }
-  __syncthreads();
-  return *row_sh;
-}
-
 __global__ void queue_reset_kernel(unsigned int* queues) {
   if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
 }

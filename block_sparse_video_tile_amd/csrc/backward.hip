@@ -35,6 +35,7 @@
 // dS pairs of one query tile run beside the matrix products of the next (for
 // dq, with a single lse per lane, the compiler's own order measured faster).
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -241,6 +242,11 @@ __device__ inline void scan_counts(int* cnt, int m, int* total, int wave, int la
 __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Clears the row-queue counters of the balanced launches (claim_row).
+__global__ void bwd_queue_reset_kernel(unsigned int* queues) {
+  if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
+}
+
 // ------------------------------------------------------------------ dQ
 
 template <int NW, bool F16>
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const uint4* __restrict__ kt, const uint4* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, int uniform_k, int64_t nnz, uint4* __restrict__ dq,
-    VsaGeom g, float scale_log2, float scale) {
+    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale) {
   constexpr int kThreads = NW * 64;
   constexpr int kPassTiles = kPassEntries * (NW / 2);  // <= vol/64 sub-tiles per block
   // two buffer sets: K rows, V rows (kappa, padded), K^T (d-major, padded)
@@ -263,7 +269,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   __shared__ int esc[kPassEntries];
   __shared__ int ntl;
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
-  const int64_t r = xcd_remap(blockIdx.x, nrows);
+  __shared__ int64_t row_sh;   // row claimed from the queues (balanced launch)
+  const int64_t r = queues != nullptr ? claim_row(queues, nrows, &row_sh)
+                                      : xcd_remap(blockIdx.x, nrows);
+  if (r < 0) return;
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
@@ -498,7 +507,8 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
     const uint4* __restrict__ qt, const uint4* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ tlist, const int32_t* __restrict__ tcount,
-    uint4* __restrict__ grad, VsaGeom g, float scale_log2, float scale) {
+    uint4* __restrict__ grad, unsigned int* __restrict__ queues, VsaGeom g, float scale_log2,
+    float scale) {
   constexpr int kThreads = NW * 64;
   constexpr int kPassTiles = kPassEntries * (NW / 2);
   // two buffer sets.  A operand of the first product(s): query rows (Q, and
@@ -516,7 +526,10 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
   __shared__ int esc[kPassEntries];
   __shared__ int ntl;
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
-  const int64_t c = xcd_remap(blockIdx.x, ncols);
+  __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
+  const int64_t c = queues != nullptr ? claim_row(queues, ncols, &col_sh)
+                                      : xcd_remap(blockIdx.x, ncols);
+  if (c < 0) return;
   const int j = int(c % g.nb);
   const int64_t bh = c / g.nb;
   const int cj = block_count(g, j);
@@ -792,7 +805,8 @@ template <int NW, bool F16>
 __global__ __launch_bounds__(NW * 64) void dv_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ dot,
     const float* __restrict__ lse, const int32_t* __restrict__ tlist,
-    const int32_t* __restrict__ tcount, uint4* __restrict__ dv, VsaGeom g, float scale_log2) {
+    const int32_t* __restrict__ tcount, uint4* __restrict__ dv, unsigned int* __restrict__ queues,
+    VsaGeom g, float scale_log2) {
   constexpr int kThreads = NW * 64;
   constexpr int kPassTiles = kPassEntries * (NW / 2);
   // Q sub-tiles (kappa rows, the "K" role of the forward) and dO^T sub-tiles
@@ -808,7 +822,10 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
   __shared__ int esc[kPassEntries];
   __shared__ int ntl;
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
-  const int64_t c = xcd_remap(blockIdx.x, ncols);
+  __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
+  const int64_t c = queues != nullptr ? claim_row(queues, ncols, &col_sh)
+                                      : xcd_remap(blockIdx.x, ncols);
+  if (c < 0) return;
   const int j = int(c % g.nb);
   const int64_t bh = c / g.nb;
   const int cj = block_count(g, j);
@@ -1149,23 +1166,33 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((dq_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+  // Balanced launches (claim_row): a quarter more workgroups than rows or
+  // columns, the queue counters cleared before each of the three kernels
+  // (they run one after another on `s`, so one counter block serves all).
+  const unsigned grid = unsigned(rows + std::max<int64_t>(8, rows / 4));
+  auto reset = [&] {
+    hipLaunchKernelGGL(bwd_queue_reset_kernel, dim3(1), dim3(64), 0, s, a.queues);
+    return hipGetLastError();
+  };
+  hipError_t e = reset();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
                      static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.kt),
                      static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.row_ptr, a.col,
-                     a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), g, scale_log2, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dv_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+                     a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), a.queues, g, scale_log2,
+                     scale);
+  if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dv_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
                      static_cast<const uint4*>(a.dot), a.lse, a.tlist, a.tcount,
-                     static_cast<uint4*>(a.dv), g, scale_log2);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dk_kernel<NW, F16>), dim3(unsigned(rows)), dim3(NW * 64), 0, s,
+                     static_cast<uint4*>(a.dv), a.queues, g, scale_log2);
+  if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
+  hipLaunchKernelGGL((dk_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
                      static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
-                     static_cast<const uint4*>(a.dout), a.lse,
-                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk), g, scale_log2, scale);
+                     static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.tlist, a.tcount,
+                     static_cast<uint4*>(a.dk), a.queues, g, scale_log2, scale);
   return hipGetLastError();
 }
 

@@ -94,7 +94,7 @@ const char* raster_unsupported(const VsaGeom& g) {
 }
 
 struct BwdWorkspace {
-  size_t dsum, kt, qt, dot, tlist, tcount, total;
+  size_t dsum, kt, qt, dot, tlist, tcount, queue, total;
 };
 BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
   const VsaGeom& g = p.g;
@@ -108,6 +108,7 @@ BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
   w.dot = off; off += align256(blk);
   w.tlist = off; off += align256(heads * g.nb * size_t(g.nb) * 4);
   w.tcount = off; off += align256(heads * g.nb * 4);
+  w.queue = off; off += vsa::kAttnQueueBytes;
   w.total = off;
   return w;
 }
@@ -451,6 +452,7 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t p, const void* q, const void* k,
   a.kt = base + w.kt; a.qt = base + w.qt; a.dot = base + w.dot;
   a.tlist = reinterpret_cast<int32_t*>(base + w.tlist);
   a.tcount = reinterpret_cast<int32_t*>(base + w.tcount);
+  a.queues = reinterpret_cast<unsigned int*>(base + w.queue);
   return hip_status(vsa::launch_attn_bwd(p->g, a, hipStream_t(stream)),
                     "vsa_block_sparse_attn_bwd");
 }

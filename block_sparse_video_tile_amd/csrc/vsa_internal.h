@@ -68,6 +68,7 @@ struct BwdArgs {
   void *kt, *qt, *dot;                // d-major 64-token chunks of K, Q, dO
   int32_t* tlist;                     // [B*NH*nb][nb] transposed block map
   int32_t* tcount;                    // [B*NH*nb]
+  unsigned int* queues;               // row-queue counters (kAttnQueueBytes)
 };
 hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s);
 

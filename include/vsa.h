@@ -271,7 +271,9 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t plan, const void* q, c
 
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
  * rowsum(dO*O) [B,NH,Npad] fp32, d-major copies of K, Q and dO, and the
- * transposed block map (B*NH*nb*nb + B*NH*nb int32), each 256-byte aligned. */
+ * transposed block map (B*NH*nb*nb + B*NH*nb int32) and the row-queue
+ * counters of its balanced launches (rows and columns are claimed per XCD at
+ * run time, as in vsa_block_sparse_attn_fwd_ws), each 256-byte aligned. */
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* Gradients of vsa_block_sparse_attn_fwd (h3-perf-stack log, sm_100a route
