@@ -111,70 +111,90 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
 // V: raster [B,S,NH,D] -> blocked-V^T [B,NH,Npad/64,D,64] (each 64-token
 // chunk stored d-major), transposed through LDS; optionally the fp32 mean of
 // each block's valid tokens (the gate-compress branch pools values per tile
-// as well).  Pad tokens are zero, so summing all 64 rows of a chunk and
-// dividing by the valid count gives the mean.
+// as well).  The means are summed in the order of gather_qk_kernel (each
+// thread its tokens in ascending order, then the 16 token lanes in order), so
+// both kernels give the same bits.
+//
+// The transpose reads LDS with the gfx950 transposing read ds_read_b64_tr_b16:
+// in each group of 16 lanes, lane i receives element i%4 of the 8-byte pieces
+// addressed by lanes 4e + i/4 (e = 0..3).  Lane L of a group addresses token
+// row t0 + L/4, columns d0 + 4(L%4) .. +3, so lane i receives tokens
+// t0 .. t0+3 of column d0 + i; two reads (t0 and t0 + 4) give the 8 tokens of
+// one 16-byte V^T unit.  With 288-byte LDS rows the 16 pieces of a read fall
+// on 16 distinct 8-byte bank slots.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ inline v4i16 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+}
+
 template <bool F16>
 __global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restrict__ x,
                                                             uint4* __restrict__ xbt,
                                                             float* __restrict__ pooled,
                                                             VsaGeom g) {
-  static_assert(kThreads == 2 * kHeadDim, "two threads per d column");
-  // [token][d]; the 16-byte row pad keeps the 16-byte row stores aligned.
-  __shared__ __align__(16) uint16_t tile[kKvChunk][kHeadDim + 8];
-  __shared__ float red[2][kHeadDim];
-  float acc = 0.f;  // this thread's share of column d = threadIdx.x % D
+  constexpr int kRow = kHeadDim + 16;  // 16-bit elements per LDS row (288 bytes)
+  __shared__ __align__(16) uint16_t tile[kKvChunk][kRow];
+  __shared__ float red[kThreads / kUnitsPerRow][kHeadDim + 1];
   const int wg = blockIdx.x;
   const int beta = wg % g.nb;
   const int bh = wg / g.nb;
   const int h = bh % g.heads;
   const int b = bh / g.heads;
   const BlockBox box = block_box(g, beta);
+  const int unit = threadIdx.x % kUnitsPerRow;
+  const int lt = threadIdx.x / kUnitsPerRow;  // token lane: tokens lt, lt + 16, ...
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int grp = lane / 16, li = lane % 16;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int chunks = g.vol / kKvChunk;
   for (int c = 0; c < chunks; ++c) {
-    // load 64 token rows: 64 x 16 units, 4 per thread
+    // load the chunk's 64 token rows (pad rows zero)
 #pragma unroll
-    for (int p = 0; p < kKvChunk * kUnitsPerRow / kThreads; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      const int tok = idx / kUnitsPerRow;
-      const int unit = idx % kUnitsPerRow;
+    for (int p = 0; p < kKvChunk / (kThreads / kUnitsPerRow); ++p) {
+      const int tok = lt + p * (kThreads / kUnitsPerRow);
       const int r = c * kKvChunk + tok;
       uint4 val = make_uint4(0u, 0u, 0u, 0u);
       if (r < box.cnt) {
         const int64_t s = token_of(g, box, r);
         val = x[((int64_t(b) * g.S + s) * g.heads + h) * kUnitsPerRow + unit];
+        acc[0] += elem_lo<F16>(val.x); acc[1] += elem_hi<F16>(val.x);
+        acc[2] += elem_lo<F16>(val.y); acc[3] += elem_hi<F16>(val.y);
+        acc[4] += elem_lo<F16>(val.z); acc[5] += elem_hi<F16>(val.z);
+        acc[6] += elem_lo<F16>(val.w); acc[7] += elem_hi<F16>(val.w);
       }
       *reinterpret_cast<uint4*>(&tile[tok][unit * 8]) = val;
     }
     __syncthreads();
-    // write 128 d-rows x 64 tokens: 128 x 8 units of 8 tokens, 4 per thread
+    // write 128 d-rows x 8 units of 8 tokens: each 16-lane group writes 16
+    // consecutive columns of one token octet per pass, a wave 16 columns x 4
+    // octets (16 rows x 64 contiguous bytes)
     uint4* dst = xbt + ((int64_t(bh) * (g.npad / kKvChunk) + int64_t(beta) * chunks + c) *
                         kHeadDim) * (kKvChunk * 2 / 16);
+    const char* lds = reinterpret_cast<const char*>(&tile[0][0]);
 #pragma unroll
-    for (int p = 0; p < kHeadDim * 8 / kThreads; ++p) {
-      const int idx = threadIdx.x + p * kThreads;
-      // d fastest across lanes: the 2-byte column reads of one instruction
-      // then touch consecutive LDS words (no bank conflicts)
-      const int d = idx % kHeadDim;
-      const int ku = idx / kHeadDim;
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = tile[ku * 8 + 2 * e][d];
-        const uint32_t hi = tile[ku * 8 + 2 * e + 1][d];
-        w[e] = lo | (hi << 16);
-        if (pooled != nullptr) acc += tile::elem_to_f32<F16>(lo) + tile::elem_to_f32<F16>(hi);
-      }
-      dst[int64_t(d) * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int it = 0; it < kHeadDim * 8 / 16 / (kThreads / 16); ++it) {
+      const int task = it * (kThreads / 16) + wave * 4 + grp;
+      const int cg = task / 8, ku = task % 8;
+      const int col = 16 * cg + 4 * (li % 4);
+      const v4i16 lo = lds_read_tr16(lds + ((8 * ku + li / 4) * kRow + col) * 2);
+      const v4i16 hi = lds_read_tr16(lds + ((8 * ku + 4 + li / 4) * kRow + col) * 2);
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      dst[int64_t(16 * cg + li) * 8 + ku] = make_uint4(l2.x, l2.y, h2.x, h2.y);
     }
     __syncthreads();
   }
   if (pooled != nullptr) {
-    // column d was summed by threads d and d + D
-    red[threadIdx.x / kHeadDim][threadIdx.x % kHeadDim] = acc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[lt][unit * 8 + i] = acc[i];
     __syncthreads();
-    if (threadIdx.x < kHeadDim)
-      pooled[(int64_t(bh) * g.nb + beta) * kHeadDim + threadIdx.x] =
-          (red[0][threadIdx.x] + red[1][threadIdx.x]) / float(box.cnt);
+    if (threadIdx.x < kHeadDim) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < kThreads / kUnitsPerRow; ++k) s += red[k][threadIdx.x];
+      pooled[(int64_t(bh) * g.nb + beta) * kHeadDim + threadIdx.x] = s / float(box.cnt);
+    }
   }
 }
 

@@ -71,6 +71,26 @@ def test_pooled_means(name):
         np.testing.assert_allclose(_host(dev), ref, rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("name", ["padded_tiny", "wan5b_k64"])
+def test_pooled_v_from_the_v_gather_equals_the_means_only_pass(name):
+    """The V gather sums each block in the order of the means-only pass, so the
+    blocked and the gather-free paths feed the coarse branch the same bits."""
+    wl = WORKLOADS[name]
+    _, _, v = make_qkv(wl)
+    plan = _plan(wl)
+    oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
+    dv = v.to(DEV)
+    vb = torch.empty(plan.blocked_vt_shape(), dtype=torch.bfloat16, device=DEV)
+    vp = torch.empty(plan.pooled_shape(), dtype=torch.float32, device=DEV)
+    vp_alone = torch.full_like(vp, 7.0)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, vb, vp)
+    vsa.vsa_gather(plan, vsa.VSA_ROLE_V, dv, None, vp_alone)
+    torch.cuda.synchronize()
+    assert torch.equal(vp.cpu(), vp_alone.cpu())
+    np.testing.assert_allclose(_host(vp), oracle.pool_blocks(bf16_to_f64(v), oplan), rtol=0,
+                               atol=1e-5)
+
+
 def test_pooled_planted_exact():
     shape = (7, 13, 10)
     x, mu = make_planted_block_means(11, 1, 2, shape, (4, 8, 8), 128)
