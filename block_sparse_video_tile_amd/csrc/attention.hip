@@ -14,7 +14,9 @@
 //   the last groups by key halves: see the key-half waves below).  Row ids are
 //   remapped so that each of the 8 XCDs (workgroups are dispatched to XCDs
 //   round-robin) works through a contiguous range of rows, i.e. the same
-//   heads, and its L2 serves their shared key/value blocks.
+//   heads, and its L2 serves their shared key/value blocks.  In the balanced
+//   launch the same ranges are queues from which the workgroups claim their
+//   rows at run time (claim_row), so XCDs that run faster take more rows.
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
 //   loaded).  The workgroup first flattens its CSR entries into a list of
