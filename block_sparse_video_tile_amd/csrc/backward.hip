@@ -34,6 +34,9 @@
 // double-buffered; dk lays each sub-tile out in 48 fenced slots so that the
 // dS pairs of one query tile run beside the matrix products of the next (for
 // dq, with a single lse per lane, the compiler's own order measured faster).
+// All three take their query block or key block from per-XCD queues at run
+// time (claim_row, counters in the workspace), as the forward's balanced
+// launch does; the results do not depend on which workgroup takes which.
 
 #include <algorithm>
 #include <type_traits>
