@@ -141,6 +141,94 @@ def _counter_means(path, name_filter):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def _short_kernel_name(name):
+    """Kernel name without namespace and argument list, template arguments kept."""
+    if name.startswith("void "):
+        name = name[5:]
+    return name.replace("vsa::(anonymous namespace)::", "").split("(")[0]
+
+
+def _calibration_factors(cal_fetch_csv, cal_write_csv, cal_mib):
+    cal_bytes = cal_mib * (1 << 20)
+    f = _counter_means(cal_fetch_csv, "vectorized_elementwise_kernel")["FETCH_SIZE"][0]
+    w = _counter_means(cal_write_csv, "vectorized_elementwise_kernel")["WRITE_SIZE"][0]
+    return cal_bytes / (f * 1024.0), cal_bytes / (w * 1024.0)
+
+
+def stage_traffic(args):
+    """HBM bytes and rates of every kernel of a layer run (markdown rows).
+
+    FETCH_SIZE and WRITE_SIZE per dispatch (KiB) of each kernel, scaled by the
+    calibration copy's factors, against the mean duration of the same kernel in
+    a --kernel-trace --stats run of the same command; the algorithmic bytes of
+    the gathers and the scatter (B*S*NH*D*2 read, B*NH*Npad*D*2 written, or the
+    reverse) are given for the 27280-token layer.
+    """
+    import csv
+    import collections
+    fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, stats_csv = args.stage_traffic
+    kf, kw = _calibration_factors(cal_fetch_csv, cal_write_csv, args.cal_mib)
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path, counter in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    vals[_short_kernel_name(row["Kernel_Name"])][counter].append(
+                        float(row["Counter_Value"]))
+    dur = {}
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            dur[_short_kernel_name(row["Name"])] = float(row["AverageNs"]) * 1e-9
+    print("| kernel | mean duration (us) | fetched (MB) | written (MB) | measured GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|")
+    for name, c in sorted(vals.items()):
+        if name not in dur or not c.get("FETCH_SIZE") or not c.get("WRITE_SIZE"):
+            continue
+        fb = np.mean(c["FETCH_SIZE"]) * 1024.0 * kf
+        wb = np.mean(c["WRITE_SIZE"]) * 1024.0 * kw
+        rate = (fb + wb) / dur[name] / 1e9
+        print(f"| {name} | {dur[name] * 1e6:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {rate:.0f} | "
+              f"{100 * rate / HBM_PEAK_GBS:.1f} |")
+
+
+def mfma_utilisation(args):
+    """MFMA busy fraction and sustained clock of the attention kernel.
+
+    From a rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA
+    --kernel-trace run: GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the
+    kernel's cycles are GRBM_GUI_ACTIVE / 8; SQ_VALU_MFMA_BUSY_CYCLES is summed
+    over the 1024 SIMDs.  busy = MFMA busy cycles / (cycles * 1024); clock =
+    cycles / duration (duration from the same run's kernel trace).
+    """
+    import csv
+    import collections
+    pmc_csv, trace_csv = args.mfma_util
+    per = collections.defaultdict(dict)
+    names = {}
+    with open(pmc_csv) as f:
+        for row in csv.DictReader(f):
+            if "attn_fwd_kernel" in row["Kernel_Name"]:
+                per[row["Dispatch_Id"]][row["Counter_Name"]] = float(row["Counter_Value"])
+                names[row["Dispatch_Id"]] = _short_kernel_name(row["Kernel_Name"])
+    durs = {}
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            durs[row["Dispatch_Id"]] = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+    rows = []
+    for d, c in per.items():
+        cycles = c["GRBM_GUI_ACTIVE"] / 8
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 1024)
+        rows.append((busy, cycles / durs[d] / 1e9, c["SQ_VALU_MFMA_BUSY_CYCLES"] / c["SQ_INSTS_MFMA"],
+                     durs[d] * 1e3, c["SQ_INSTS_MFMA"]))
+    r = np.array(rows)
+    print(json.dumps({"kernel": sorted(set(names.values())), "dispatches": len(rows),
+                      "mfma_busy": round(float(r[:, 0].mean()), 4),
+                      "clock_ghz": round(float(r[:, 1].mean()), 3),
+                      "busy_cycles_per_mfma": round(float(r[:, 2].mean()), 2),
+                      "duration_ms": round(float(r[:, 3].mean()), 3),
+                      "mfma_instructions": float(r[:, 4].mean())}))
+
+
 def record_traffic(args):
     fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.record_traffic
     cal_bytes = args.cal_mib * (1 << 20)
@@ -283,6 +371,12 @@ def main():
     ap.add_argument("--copy-calibration", type=int, metavar="MIB")
     ap.add_argument("--record-traffic", nargs=4, metavar="CSV")
     ap.add_argument("--cal-mib", type=int, default=1024)
+    ap.add_argument("--stage-traffic", nargs=5, metavar="CSV",
+                    help="FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv KERNEL_STATS.csv: "
+                         "HBM bytes and GB/s of every kernel of the layer")
+    ap.add_argument("--mfma-util", nargs=2, metavar="CSV",
+                    help="COUNTER_COLLECTION.csv KERNEL_TRACE.csv of one --pmc --kernel-trace "
+                         "run: MFMA busy fraction and clock of the attention kernel")
     args = ap.parse_args()
     if args.traffic_json is None:
         args.traffic_json = os.path.join(
@@ -291,6 +385,12 @@ def main():
 
     if args.record_traffic:
         record_traffic(args)
+        return
+    if args.stage_traffic:
+        stage_traffic(args)
+        return
+    if args.mfma_util:
+        mfma_utilisation(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; "
