@@ -119,9 +119,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // and the byte offset 16*off is formed in 32 bits (callers keep it below
 // 2^32), so the copy takes the scalar-base + 32-bit vector-offset form.
 __device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* dst) {
+  // The empty asm keeps the byte offset a 32-bit value at the copy: offsets
+  // that are loop-invariant would otherwise be widened to 64 bits once,
+  // outside the loop, and every copy would pay a 64-bit address add.
+  uint32_t bytes = off * 16u;
+  asm volatile("" : "+v"(bytes));
   __builtin_amdgcn_global_load_lds(
-      static_cast<const void*>(reinterpret_cast<const char*>(src) + off * 16u), (lds_ptr_t)(dst),
-      16, 0, 0);
+      static_cast<const void*>(reinterpret_cast<const char*>(src) + bytes), (lds_ptr_t)(dst), 16,
+      0, 0);
 }
 
 }  // namespace tile
