@@ -72,8 +72,11 @@ __global__ __launch_bounds__(kThreads) void gather_qk_kernel(const uint4* __rest
                                                              VsaGeom g) {
   __shared__ float red[kThreads / kUnitsPerRow][kHeadDim + 1];
   const int wg = blockIdx.x;
-  const int beta = wg % g.nb;
-  const int bh = wg / g.nb;  // b * heads + h
+  // consecutive workgroups take the heads of one block: together they read
+  // (or write) whole raster token rows, all heads contiguous
+  const int nbh = g.batch * g.heads;
+  const int beta = wg / nbh;
+  const int bh = wg % nbh;  // b * heads + h
   const int h = bh % g.heads;
   const int b = bh / g.heads;
   const BlockBox box = block_box(g, beta);
@@ -138,8 +141,9 @@ __global__ __launch_bounds__(kThreads) void gather_v_kernel(const uint4* __restr
   __shared__ __align__(16) uint16_t tile[kKvChunk][kRow];
   __shared__ float red[kThreads / kUnitsPerRow][kHeadDim + 1];
   const int wg = blockIdx.x;
-  const int beta = wg % g.nb;
-  const int bh = wg / g.nb;
+  const int nbh = g.batch * g.heads;
+  const int beta = wg / nbh;  // consecutive workgroups: the heads of one block
+  const int bh = wg % nbh;
   const int h = bh % g.heads;
   const int b = bh / g.heads;
   const BlockBox box = block_box(g, beta);
@@ -228,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restri
                                                            const uint4* __restrict__ gate,
                                                            uint4* __restrict__ o, VsaGeom g) {
   const int wg = blockIdx.x;
-  const int beta = wg % g.nb;
-  const int bh = wg / g.nb;
+  const int nbh = g.batch * g.heads;
+  const int beta = wg / nbh;  // consecutive workgroups: the heads of one block
+  const int bh = wg % nbh;
   const int h = bh % g.heads;
   const int b = bh / g.heads;
   const BlockBox box = block_box(g, beta);
