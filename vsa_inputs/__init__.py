@@ -65,6 +65,8 @@ WORKLOADS = {
     "wan5b_k16": Workload("wan5b_k16", (31, 22, 40), (4, 8, 8), 1, 24, 128, 16, seed=1),
     "wan5b_k32": Workload("wan5b_k32", (31, 22, 40), (4, 8, 8), 1, 24, 128, 32, seed=1),
     "wan5b_k120": Workload("wan5b_k120", (31, 22, 40), (4, 8, 8), 1, 24, 128, 120, seed=1),
+    # one GPU's share of the 27280-token layer sharded over 8 GPUs by heads
+    "wan5b_k64_h3": Workload("wan5b_k64_h3", (31, 22, 40), (4, 8, 8), 1, 3, 128, 64, seed=1),
     "tile64_csr": Workload("tile64_csr", (1, 1, 33280), (1, 1, 64), 1, 24, 128, None,
                            seed=3, map_seed=1003, prefix_tiles=8, max_video_k=64),
     "tile64_csr_zero": Workload("tile64_csr_zero", (1, 1, 33280), (1, 1, 64), 1, 24, 128,
