@@ -208,7 +208,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // `queues`, claimed at start-up (claim_row); a workgroup that finds every
   // row taken leaves at once (workgroup-uniform, before any other barrier).
   __shared__ int64_t row_sh;
-  const int64_t r = queues != nullptr ? claim_row(queues, nrows, &row_sh)
+  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh)
                                       : xcd_remap(blockIdx.x, nrows);
   if (r < 0) return;
   const int i = int(r % g.nb);

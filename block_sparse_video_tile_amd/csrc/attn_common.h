@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vsa_internal.h"
+
 namespace vsa {
 namespace tile {
 
@@ -59,9 +61,60 @@ __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + loc;
 }
 
+// Block at position p of a head's cost order: blocks grouped by edge class
+// (which of the T, H and W extents the grid edge cuts: bit 2, 1, 0), the
+// classes by descending valid-token count (then class number), the blocks
+// of a class ascending.  A bijection on [0, nb).
+__device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
+  const int nbd[3] = {g.nbt, g.nbh, g.nbw};
+  const int full[3] = {g.bt, g.bh, g.bw};
+  const int last[3] = {g.T - (g.nbt - 1) * g.bt, g.H - (g.nbh - 1) * g.bh,
+                       g.W - (g.nbw - 1) * g.bw};
+  int cnt[8], vol[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    cnt[c] = 1;
+    vol[c] = 1;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const bool edge = (c >> (2 - d)) & 1;
+      cnt[c] *= edge ? 1 : nbd[d] - 1;
+      vol[c] *= edge ? last[d] : full[d];
+    }
+  }
+  int taken = 0;
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    int c = -1;
+#pragma unroll 1
+    for (int x = 0; x < 8; ++x)
+      if (!((taken >> x) & 1) && (c < 0 || vol[x] > vol[c])) c = x;
+    if (p < cnt[c]) {
+      int idx[3];
+      int q = p;
+#pragma unroll
+      for (int d = 2; d >= 0; --d) {
+        const bool edge = (c >> (2 - d)) & 1;
+        const int radix = edge ? 1 : nbd[d] - 1;
+        idx[d] = edge ? nbd[d] - 1 : q % radix;
+        q = edge ? q : q / radix;
+      }
+      return (idx[0] * g.nbh + idx[1]) * g.nbw + idx[2];
+    }
+    p -= cnt[c];
+    taken |= 1 << c;
+  }
+  return 0;  // not reached for p in [0, nb)
+}
+
 // Dynamic row assignment of the balanced launch.  The rows are cut into 8
-// queues of consecutive rows (the ranges xcd_remap gives the XCDs, i.e.
-// whole heads).  queues[8] hands out tickets and queues[x] counts the rows
+// queues of consecutive positions (the ranges xcd_remap gives the XCDs, i.e.
+// whole heads); the position r of a row within its head's nb is read through
+// block_in_cost_order, so each head hands out its full blocks first and its
+// cheaper edge blocks last: the workgroups running at once on an XCD have
+// about equal cost (they stream the head's key blocks in step, which keeps
+// shared blocks in L2), and the rows left at the end of the kernel are the
+// cheap ones.  queues[8] hands out tickets and queues[x] counts the rows
 // taken from queue x; all start at zero.  The launch has more workgroups
 // than rows; a workgroup whose ticket is below the row count takes the next
 // row of its own XCD's queue or, once that is empty, of the other queues in
@@ -71,7 +124,8 @@ __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
 // empty, and if all 8 were empty every row would already be held by one of
 // the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
 // reaches the workgroup through LDS.
-__device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, int64_t* row_sh) {
+__device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const VsaGeom& g,
+                                    int64_t* row_sh) {
   if (threadIdx.x == 0) {
     int64_t row = -1;
     if (atomicAdd(&queues[8], 1u) < uint64_t(nrows)) {
@@ -83,7 +137,8 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, int64_t
         if (count == 0) continue;
         const unsigned int t = atomicAdd(&queues[x], 1u);
         if (t < uint64_t(count)) {
-          row = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
+          const int64_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
+          row = (pos / g.nb) * g.nb + block_in_cost_order(g, int(pos % g.nb));
           break;
         }
       }

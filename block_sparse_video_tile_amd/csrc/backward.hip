@@ -273,7 +273,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   __shared__ int ntl;
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   __shared__ int64_t row_sh;   // row claimed from the queues (balanced launch)
-  const int64_t r = queues != nullptr ? claim_row(queues, nrows, &row_sh)
+  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh)
                                       : xcd_remap(blockIdx.x, nrows);
   if (r < 0) return;
   const int i = int(r % g.nb);
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(NW * 64) void dk_kernel(
   __shared__ int ntl;
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
   __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
-  const int64_t c = queues != nullptr ? claim_row(queues, ncols, &col_sh)
+  const int64_t c = queues != nullptr ? claim_row(queues, ncols, g, &col_sh)
                                       : xcd_remap(blockIdx.x, ncols);
   if (c < 0) return;
   const int j = int(c % g.nb);
@@ -826,7 +826,7 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
   __shared__ int ntl;
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
   __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
-  const int64_t c = queues != nullptr ? claim_row(queues, ncols, &col_sh)
+  const int64_t c = queues != nullptr ? claim_row(queues, ncols, g, &col_sh)
                                       : xcd_remap(blockIdx.x, ncols);
   if (c < 0) return;
   const int j = int(c % g.nb);
