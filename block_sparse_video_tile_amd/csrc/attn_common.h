@@ -66,45 +66,30 @@ __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
 // classes by descending valid-token count (then class number), the blocks
 // of a class ascending.  A bijection on [0, nb).
 __device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
-  const int nbd[3] = {g.nbt, g.nbh, g.nbw};
-  const int full[3] = {g.bt, g.bh, g.bw};
-  const int last[3] = {g.T - (g.nbt - 1) * g.bt, g.H - (g.nbh - 1) * g.bh,
-                       g.W - (g.nbw - 1) * g.bw};
-  int cnt[8], vol[8];
+  // the class holding p: the last k whose start is <= p (an empty class
+  // shares its start with the next one, so it is passed over)
+  int k = 0;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    cnt[c] = 1;
-    vol[c] = 1;
+  for (int x = 1; x < 8; ++x) k += p >= g.cstart[x] ? 1 : 0;
+  int c = g.corder[0], q = p;
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      const bool edge = (c >> (2 - d)) & 1;
-      cnt[c] *= edge ? 1 : nbd[d] - 1;
-      vol[c] *= edge ? last[d] : full[d];
+  for (int x = 1; x < 8; ++x)
+    if (k == x) {
+      c = g.corder[x];
+      q = p - g.cstart[x];
     }
+  // q-th block of class c, W fastest; a cut axis holds the last block index
+  int iw = g.nbw - 1, ih = g.nbh - 1, it = g.nbt - 1;
+  if (!(c & 1)) {
+    iw = q % (g.nbw - 1);
+    q /= g.nbw - 1;
   }
-  int taken = 0;
-#pragma unroll 1
-  for (int k = 0; k < 8; ++k) {
-    int c = -1;
-#pragma unroll 1
-    for (int x = 0; x < 8; ++x)
-      if (!((taken >> x) & 1) && (c < 0 || vol[x] > vol[c])) c = x;
-    if (p < cnt[c]) {
-      int idx[3];
-      int q = p;
-#pragma unroll
-      for (int d = 2; d >= 0; --d) {
-        const bool edge = (c >> (2 - d)) & 1;
-        const int radix = edge ? 1 : nbd[d] - 1;
-        idx[d] = edge ? nbd[d] - 1 : q % radix;
-        q = edge ? q : q / radix;
-      }
-      return (idx[0] * g.nbh + idx[1]) * g.nbw + idx[2];
-    }
-    p -= cnt[c];
-    taken |= 1 << c;
+  if (!(c & 2)) {
+    ih = q % (g.nbh - 1);
+    q /= g.nbh - 1;
   }
-  return 0;  // not reached for p in [0, nb)
+  if (!(c & 4)) it = q;
+  return (it * g.nbh + ih) * g.nbw + iw;
 }
 
 // Dynamic row assignment of the balanced launch.  The rows are cut into 8
@@ -128,17 +113,20 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const V
                                     int64_t* row_sh) {
   if (threadIdx.x == 0) {
     int64_t row = -1;
-    if (atomicAdd(&queues[8], 1u) < uint64_t(nrows)) {
+    // rows number at most 2^30 (the plan's limit): 32-bit arithmetic
+    const uint32_t n = uint32_t(nrows);
+    if (atomicAdd(&queues[8], 1u) < n) {
       const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
-      const int64_t per = nrows / 8, rem = nrows % 8;
+      const uint32_t per = n / 8, rem = n % 8;
       for (int j = 0; j < 8; ++j) {
-        const int x = (home + j) & 7;
-        const int64_t count = per + (x < rem ? 1 : 0);
+        const uint32_t x = (home + j) & 7;
+        const uint32_t count = per + (x < rem ? 1 : 0);
         if (count == 0) continue;
-        const unsigned int t = atomicAdd(&queues[x], 1u);
-        if (t < uint64_t(count)) {
-          const int64_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
-          row = (pos / g.nb) * g.nb + block_in_cost_order(g, int(pos % g.nb));
+        const uint32_t t = atomicAdd(&queues[x], 1u);
+        if (t < count) {
+          const uint32_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
+          const uint32_t nb = uint32_t(g.nb);
+          row = int64_t(pos / nb) * nb + block_in_cost_order(g, int(pos % nb));
           break;
         }
       }

@@ -2,6 +2,7 @@
 // routing line, argument checks, and the sequencing of kernel launches.
 // Every argument check runs before the first HIP call.
 
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -129,6 +130,36 @@ const char* vsa_status_string(vsa_status st) {
 
 const char* vsa_last_error(void) { return g_last_error.c_str(); }
 
+// Class order of a head's blocks for the balanced launches: the blocks of
+// edge class c (bit 2, 1, 0: the grid edge cuts the T, H, W extent) number
+// the product over the axes of 1 (cut) or blocks-along-the-axis - 1 (not cut),
+// and hold the product of the cut extents and full block sizes as valid
+// tokens.  Classes go by descending valid-token count, ties by class number.
+static void fill_cost_order(VsaGeom& g) {
+  const int nbd[3] = {g.nbt, g.nbh, g.nbw};
+  const int full[3] = {g.bt, g.bh, g.bw};
+  const int last[3] = {g.T - (g.nbt - 1) * g.bt, g.H - (g.nbh - 1) * g.bh,
+                       g.W - (g.nbw - 1) * g.bw};
+  int cnt[8], vol[8], ord[8];
+  for (int c = 0; c < 8; ++c) {
+    cnt[c] = 1;
+    vol[c] = 1;
+    for (int d = 0; d < 3; ++d) {
+      const bool cut = (c >> (2 - d)) & 1;
+      cnt[c] *= cut ? 1 : nbd[d] - 1;
+      vol[c] *= cut ? last[d] : full[d];
+    }
+    ord[c] = c;
+  }
+  std::stable_sort(ord, ord + 8, [&](int a, int b) { return vol[a] > vol[b]; });
+  int start = 0;
+  for (int k = 0; k < 8; ++k) {
+    g.corder[k] = ord[k];
+    g.cstart[k] = start;
+    start += cnt[ord[k]];
+  }
+}
+
 vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
   if (!d || !out) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: null desc or out pointer");
   *out = nullptr;
@@ -183,6 +214,7 @@ vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
   g.S = d->seq_len;
   g.npad = npad;
   g.dtype = d->dtype;
+  fill_cost_order(g);
   p->topk = d->topk;
   p->dtype = d->dtype;
   *out = p;

@@ -20,6 +20,13 @@ struct VsaGeom {
   int64_t S;              // tokens
   int64_t npad;           // nb * vol
   int32_t dtype;          // vsa_dtype of Q, K, V and O
+  // A head's blocks in cost order (read by the balanced launches): blocks
+  // grouped by edge class (bit 2, 1, 0 set when the grid edge cuts the
+  // block's T, H, W extent), classes by descending valid-token count, ties
+  // by class number, blocks of a class in ascending index.  corder[k] is
+  // the k-th class, cstart[k] the position of its first block.
+  int32_t corder[8];
+  int32_t cstart[8];
 };
 
 struct vsa_plan_s {
