@@ -88,7 +88,8 @@ namespace {
 using namespace tile;
 
 
-// A row's CSR entries are flattened, up to kListEntries at a time, into a list
+// A row's CSR entries are flattened, up to kListEntries at a time (768 in the
+// 2-wave kernel), into a list
 // of 64-key sub-tile descriptors in LDS:
 //   (64-token chunk index of the sub-tile within its head) << 7 | (valid keys - 1)
 // K rows of chunk c start at token row 64c of the head and V^T chunk c is the
@@ -196,12 +197,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // sub-tile descriptor list of the current pass over the row, and the
   // per-entry scan that places each entry's descriptors
   constexpr int kThreads = NW * 64;
-  constexpr int kListTiles = kListEntries * (32 * NW / kKvChunk);
+  // Two 2-wave workgroups share a CU only if each holds at most half of its
+  // 160 KB of LDS; their list passes are shorter to leave room for the
+  // raster slot table.
+  constexpr int kList = NW == 2 ? 768 : kListEntries;
+  constexpr int kListTiles = kList * (32 * NW / kKvChunk);
   __shared__ int tlist[kListTiles];
-  __shared__ int escan[kListEntries];
+  __shared__ int escan[kList];
   __shared__ int ntiles_sh;
   constexpr int kVol = 32 * NW;
   __shared__ uint32_t soff[RASTER ? 8 * kVol : 1];
+  static_assert(NW != 2 || 16 * 2 * (kKUnits + kVUnits) + 4 * (kListTiles + kList) +
+                               4 * (RASTER ? 8 * kVol : 1) + 64 <= 160 * 1024 / 2,
+                "two 2-wave workgroups must fit in one CU's LDS");
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   // The row: fixed by the workgroup index (XCD-aware order), or, with
@@ -367,8 +375,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   f32x16 sa[2], sb[2];
   float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
 
-  for (int e0 = 0; e0 < len; e0 += kListEntries) {
-    const int m = min(kListEntries, len - e0);
+  for (int e0 = 0; e0 < len; e0 += kList) {
+    const int m = min(kList, len - e0);
     // ---- flatten entries e0 .. e0+m-1 into the sub-tile list: per-entry
     // sub-tile counts, an exclusive scan of them, then the descriptors
     for (int e = tid; e < m; e += kThreads) {
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
     __syncthreads();
     if (wave == 0) {
-      constexpr int kPerLane = kListEntries / 64;
+      constexpr int kPerLane = kList / 64;
       int loc[kPerLane];
       int sum = 0;
 #pragma unroll
