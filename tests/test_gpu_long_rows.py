@@ -1,5 +1,6 @@
 """GPU parity for block maps whose lists exceed one pass of the kernels'
-LDS work lists (1024 entries): a 1-D layout of 1100 64-token tiles where a few
+LDS work lists (1024 entries; 768 in the 2-wave forward kernel that 64-token
+tiles use): a 1-D layout of 1100 64-token tiles where a few
 query rows list every tile and every other row lists tile 0 only, so those
 rows (forward and dQ) and the column of tile 0 (dK, dV) are flattened in two
 passes.  Oracle rows are computed for the long rows and a sample of the short
