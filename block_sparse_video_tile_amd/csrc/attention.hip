@@ -472,6 +472,11 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     auto half_body = [&](f32x16& cur, f32x16& nxt, const uint4* kn, uint4* kw, const uint4* vn,
                          uint4* vw, const uint4* sk, const uint4* sv, const uint32_t (&ko)[kMaxK],
                          const uint32_t (&vo)[kMaxV]) __attribute__((always_inline)) {
+      // first K operands before the row-max exchange, as in the full step
+      ev8 opk[8], opv[8];
+      auto read_k = [&](int u) { opk[u % 8] = as_ev8(kn[kread_h + 2 * u]); };
+#pragma unroll
+      for (int u = 0; u < 4; ++u) read_k(u);
       float mx = mx_pre;
       const int valid = (d0 & (RASTER ? 63 : 127)) + 1;
       if (valid < kKvChunk) {
@@ -503,8 +508,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       float rs0 = 0.f, rs1 = 0.f;
       uint32_t pw[2][4];
       float mxn = -INFINITY;
-      ev8 opk[8], opv[8];
-      auto read_k = [&](int u) { opk[u % 8] = as_ev8(kn[kread_h + 2 * u]); };
       auto read_v = [&](int w) {  // PV slot w: keys 32*kh + 16*(w/4) + ..., d tile w%4
         if constexpr (RASTER) {
           const char* bp = reinterpret_cast<const char*>(vn) + vtr_h +
@@ -516,8 +519,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           opv[w % 8] = as_ev8(vn[vread_h + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
         }
       };
-#pragma unroll
-      for (int u = 0; u < 4; ++u) read_k(u);
 #pragma unroll
       for (int j = 0; j < 16; ++j) nxt[j] = 0.f;
       slot_fence();
@@ -591,6 +592,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
       if (HV && active) {
         half_body(cur[0], nxt[0], kn, kw, vn, vw, sk, sv, ko, vo);
       } else if (!HV && active) {
+        // The first K operands of the QK^T slots are read before the row-max
+        // exchange and the rescale test, so the LDS latency after the
+        // barrier overlaps that chain.
+        ev8 opk[8], opv[8];
+        auto read_k = [&](int u) {  // operand of QK slot u
+          opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
+        };
+#pragma unroll
+        for (int u = 0; u < 4; ++u) read_k(u);
         float mx = mx_pre;
         // mask keys past the block's valid count (only in its last sub-tile)
         const int valid = (d0 & (RASTER ? 63 : 127)) + 1;
@@ -637,10 +647,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         // LDS operands are read in groups of 4, one group ahead of the slots
         // that consume them, so any wait for LDS data lands on reads issued
         // four slots (about 130 cycles) earlier.
-        ev8 opk[8], opv[8];
-        auto read_k = [&](int u) {  // operand of QK slot u
-          opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
-        };
         auto read_v = [&](int w) {  // operand of PV slot w
           if constexpr (RASTER) {
             // keys 16*(w/4) + 8*half + 0..7 of d column
@@ -654,8 +660,6 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
             opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
           }
         };
-#pragma unroll
-        for (int u = 0; u < 4; ++u) read_k(u);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
