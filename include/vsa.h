@@ -246,7 +246,10 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t plan, const void* q, cons
  * whole heads): its own XCD's queue, or once that is empty the others', and
  * the workgroups left over when every row is taken exit at once.  XCDs that
  * run faster thus finish more rows and the kernel does not wait for the
- * slowest one.  The queue counters live in the workspace and are cleared
+ * slowest one.  Within a head the queue hands out the query blocks in cost
+ * order: blocks the grid edge does not cut first, then the edge blocks by
+ * descending valid-token count, so the workgroups running together cost
+ * about the same (they share key blocks in L2) and the cheap rows come last.  The queue counters live in the workspace and are cleared
  * by a kernel on `stream` before the attention kernel, so the workspace needs
  * no initialisation; it must not be used by another call while this one runs
  * (concurrent calls need their own workspaces).
