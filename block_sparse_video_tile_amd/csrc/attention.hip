@@ -697,8 +697,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
             oacc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, oacc[dt]);
           }
           // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
-          // in even slots 0..22, pairs 12..15 in slots 24..27
-          const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+          // in the odd slots 1..23 (blocked kernel; away from the slots that
+          // wait for an LDS operand group) or the even slots 0..22 (raster
+          // kernel, whose transposing V reads measured better so), pairs
+          // 12..15 in slots 24..27
+          constexpr int kExpPhase = RASTER ? 0 : 1;
+          const int e = (u < 24) ? ((u % 2 == kExpPhase) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
           if (e >= 0) {
             const int cc = e / 4, t = 2 * (e % 4);
             float p0 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -mb));
