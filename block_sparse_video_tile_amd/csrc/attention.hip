@@ -636,6 +636,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         }
         const float mb = m_run * scale_log2;
         float rs0 = 0.f, rs1 = 0.f;
+        float p12[2] = {0.f, 0.f};  // pair 12 until it joins the row sums (blocked)
         uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 PV steps
         float mxn = -INFINITY;
 
@@ -696,19 +697,34 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
                 ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
             oacc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, oacc[dt]);
           }
-          // exponential pair e (keys 2e, 2e+1 of this lane's 32): pairs 0..11
-          // in the odd slots 1..23 (blocked kernel; away from the slots that
-          // wait for an LDS operand group) or the even slots 0..22 (raster
-          // kernel, whose transposing V reads measured better so), pairs
-          // 12..15 in slots 24..27
-          constexpr int kExpPhase = RASTER ? 0 : 1;
-          const int e = (u < 24) ? ((u % 2 == kExpPhase) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+          // exponential pair e (keys 2e, 2e+1 of this lane's 32).  Blocked
+          // kernel: pairs 0..11 in the odd slots 1..23, pair 12 in slot 22
+          // and pairs 13..15 in slots 25..27, away from the slots that wait
+          // for an LDS operand group (0, 4, ..., 24); pair 12 joins the row
+          // sums in slot 25, so the pairs are summed in ascending order as
+          // in the raster kernel.  Raster kernel (whose transposing V reads
+          // measured better so): pairs 0..11 in the even slots 0..22, pairs
+          // 12..15 in slots 24..27.
+          int e;
+          if constexpr (RASTER)
+            e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
+          else
+            e = (u < 24 && u % 2 == 1) ? u / 2 : u == 22 ? 12 : (u >= 25 && u < 28) ? u - 12 : -1;
+          if (!RASTER && u == 25) {
+            rs0 += p12[0];
+            rs1 += p12[1];
+          }
           if (e >= 0) {
             const int cc = e / 4, t = 2 * (e % 4);
             float p0 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -mb));
             float p1 = __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -mb));
-            rs0 += p0;
-            rs1 += p1;
+            if (!RASTER && e == 12) {
+              p12[0] = p0;
+              p12[1] = p1;
+            } else {
+              rs0 += p0;
+              rs1 += p1;
+            }
             pw[cc][t / 2] = pack2<F16>(p0, p1);
             pin(rs0);
             pin(rs1);
