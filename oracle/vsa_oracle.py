@@ -36,8 +36,10 @@ Readings where the pages are silent (each also listed with the design notes):
      divide by their own token count, not by the full block volume);
   R4 the block score is the raw dot product of pooled query and pooled key
      (no scale, no softmax -- both are monotone per row);
-  R5 ties in the top-k go to the lower block index; the decision is taken on
-     scores rounded to fp32, the precision the device path scores in;
+  R5 ties in the top-k go to the lower block index; the ranking uses the
+     float64 scores as computed here (no rounding to a device precision:
+     rows whose k-th and (k+1)-th scores lie within the stated 1e-3 margin
+     are near-ties, where a lower-precision implementation may differ);
   R6 a selected row is reported sorted ascending by block index;
   R7 no block is forced into its own row (pure top-k);
   R8 an empty row gives O = 0 and LSE = -inf;
@@ -52,6 +54,12 @@ Readings where the pages are silent (each also listed with the design notes):
      like Q (the projection's output, supplied by the caller); no gate means
      the sparse output alone.
 
+Precision: every function computes in float64 except the two *_f32 ones,
+which take the same steps in float32 torch-CPU ops.  They exist for the
+layer-sized shapes (the timed CPU baseline, and checking every output row of
+a full layer), where the float64 loop is too slow; they are pinned to the
+float64 functions and to the brute-force formulation on small shapes.
+
 Parity pins for every function live in tests/test_oracle_pins.py.
 """
 from __future__ import annotations
@@ -65,7 +73,7 @@ __all__ = [
     "pool_blocks", "block_scores", "select_topk", "selection_to_csr",
     "map_to_csr", "block_sparse_attention", "vsa_reference", "valid_flops",
     "compress_attention", "gated_combine", "vsa_gated_reference",
-    "block_sparse_attention_bwd",
+    "block_sparse_attention_bwd", "block_sparse_attention_f32", "vsa_reference_f32",
 ]
 
 
@@ -184,29 +192,28 @@ def block_scores(qbar, kbar) -> np.ndarray:
 def select_topk(scores, k):
     """Per-row top-k of the block scores ("FastVideo VSA" guide, intro and "Choose top-k").
 
-    Keeps the k highest-scoring key blocks of each query-block row.  The
-    decision is taken on the scores rounded to fp32 with ties to the lower
-    block index (R5); each row is returned sorted ascending (R6).
+    Keeps the k highest-scoring key blocks of each query-block row, ranking
+    the float64 scores with ties to the lower block index (R5): the key is
+    (-score, block index), ascending.  Each row is returned sorted ascending
+    (R6).
 
     Returns (sel int64 [..., nb, k], margin float64 [..., nb]) where margin is
-    the gap between the k-th and (k+1)-th largest float64 scores of the row
-    (+inf when k == nb): rows with a small margin are near-ties.
+    the gap between the k-th and (k+1)-th largest scores of the row (+inf
+    when k == nb): rows with a small margin are near-ties.
     """
     s64 = np.asarray(scores, np.float64)
     nb = s64.shape[-1]
     if not 1 <= k <= nb:
         raise ValueError(f"topk {k} outside [1, {nb}]")
-    s32 = s64.astype(np.float32)
-    rows = s32.reshape(-1, nb)
-    rows64 = s64.reshape(-1, nb)
+    rows = s64.reshape(-1, nb)
     sel = np.empty((rows.shape[0], k), dtype=np.int64)
     margin = np.empty(rows.shape[0])
     idx = np.arange(nb)
     for r in range(rows.shape[0]):
         # primary key: score descending; secondary key: block index ascending
-        order = np.lexsort((idx, -rows[r].astype(np.float64)))
+        order = np.lexsort((idx, -rows[r]))
         sel[r] = np.sort(order[:k])
-        desc = np.sort(rows64[r])[::-1]
+        desc = rows[r][order]
         margin[r] = math.inf if k == nb else desc[k - 1] - desc[k]
     return sel.reshape(*s64.shape[:-1], k), margin.reshape(s64.shape[:-1])
 
@@ -399,3 +406,78 @@ def valid_flops(plan: Plan, row_ptr, col_idx, head_dim) -> int:
     keys_per_row = np.where(np.diff(row_ptr) > 0, keys_per_row, 0)
     q_counts = np.tile(c, rows // nb)
     return int(4 * head_dim * np.sum(q_counts * keys_per_row))
+
+
+def block_sparse_attention_f32(q, k, v, plan: Plan, row_ptr, col_idx, heads=None):
+    """block_sparse_attention in float32 torch-CPU ops (same steps, row by row).
+
+    For every row (batch b, head h, query block i): the logits of the block's
+    valid queries against the concatenated valid keys of the row's blocks,
+    scaled by head_size**-0.5, a max-subtracted softmax, and the product with
+    the same keys' values ("FastVideo VSA" guide, intro and "Verify routing
+    and fallback").  Empty rows give O = 0 and LSE = -inf (R8).
+
+    q, k, v: [B, S, heads, D] torch tensors or arrays (cast to float32).
+    heads: optional iterable of head indices to compute (every batch); the
+    other heads' outputs are NaN.  Returns (O [B, S, heads, D],
+    LSE [B, S, heads]) as float32 torch tensors; LSE is the natural log.
+    """
+    import torch
+    q, k, v = (torch.as_tensor(x).to(torch.float32) for x in (q, k, v))
+    bsz, s, nh, d = q.shape
+    nb = plan.num_blocks
+    lists = [torch.as_tensor(t, dtype=torch.long) for t in block_token_lists(plan)]
+    row_ptr = np.asarray(row_ptr, np.int64)
+    col_idx = np.asarray(col_idx, np.int64)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((bsz, s, nh), float("nan"))
+    for b in range(bsz):
+        for h in (range(nh) if heads is None else heads):
+            qh, kh, vh = q[b, :, h].contiguous(), k[b, :, h].contiguous(), v[b, :, h].contiguous()
+            for i in range(nb):
+                r = (b * nh + h) * nb + i
+                qtok = lists[i]
+                cols = col_idx[row_ptr[r]:row_ptr[r + 1]]
+                if len(cols) == 0:
+                    out[b, qtok, h] = 0.0
+                    lse[b, qtok, h] = float("-inf")
+                    continue
+                ktok = torch.cat([lists[j] for j in cols])
+                logits = (qh[qtok] @ kh[ktok].T) * scale
+                mx = logits.amax(dim=1, keepdim=True)
+                p = torch.exp(logits - mx)
+                denom = p.sum(dim=1, keepdim=True)
+                out[b, qtok, h] = (p @ vh[ktok]) / denom
+                lse[b, qtok, h] = (mx + torch.log(denom))[:, 0]
+    return out, lse
+
+
+def vsa_reference_f32(q, k, v, dit_seq_shape, block_size, topk, heads=None):
+    """Whole hot path in float32 torch-CPU ops: plan, pool, score, top-k, attention.
+
+    Same steps as vsa_reference: block means over valid tokens (R3), raw dot
+    product scores (R4), per-row top-k on the float32 scores with ties to the
+    lower block index (a stable sort of the negated scores, R5), rows sorted
+    ascending (R6), then block_sparse_attention_f32.  heads: optional subset
+    of heads to attend (pooling, scoring and selection cover every head).
+    Returns a dict with the plan, the selection, the CSR and O / LSE.
+    """
+    import torch
+    q, k, v = (torch.as_tensor(x).to(torch.float32) for x in (q, k, v))
+    plan = make_plan(q.shape[1], dit_seq_shape, block_size, topk)
+    beta = torch.as_tensor(token_block_ids(plan), dtype=torch.long)
+    counts = torch.as_tensor(plan.block_counts(), dtype=torch.float32)
+
+    def pool(x):
+        sums = torch.zeros(x.shape[0], plan.num_blocks, x.shape[2], x.shape[3])
+        sums.index_add_(1, beta, x)
+        return (sums / counts[None, :, None, None]).permute(0, 2, 1, 3)   # [B, heads, nb, D]
+
+    scores = pool(q) @ pool(k).transpose(-1, -2)
+    order = torch.sort(-scores, dim=-1, stable=True).indices[..., :topk]
+    sel = torch.sort(order, dim=-1).values.numpy().astype(np.int64)
+    row_ptr, col_idx = selection_to_csr(sel)
+    o, lse = block_sparse_attention_f32(q, k, v, plan, row_ptr, col_idx, heads=heads)
+    return dict(plan=plan, scores=scores, sel=sel, row_ptr=row_ptr, col_idx=col_idx, out=o,
+                lse=lse)

@@ -58,6 +58,17 @@ def test_keeping_smallest_scores_is_caught(monkeypatch):
     _fails(pins.test_topk_hand_examples_with_ties)
 
 
+def test_ranking_float32_rounded_scores_is_caught(monkeypatch):
+    orig = ov.select_topk
+
+    def bad(scores, k):
+        s = np.asarray(scores, np.float64)
+        sel, _ = orig(s.astype(np.float32).astype(np.float64), k)
+        return sel, orig(s, k)[1]
+    _patch(monkeypatch, "select_topk", bad)
+    _fails(pins.test_topk_ranks_full_precision_scores)
+
+
 def _attention_with(logit_fn):
     def att(q, k, v, plan, row_ptr, col_idx, query_rows=None):
         q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
@@ -222,3 +233,36 @@ def test_backward_mutation_harness_is_faithful(monkeypatch):
     _patch(monkeypatch, "block_sparse_attention_bwd", _bwd_variant())
     pins.test_backward_matches_torch_autograd_masked(4)
     pins.test_backward_repeated_block_counts_twice()
+
+
+# ------------------------------------------ the float32 forms (test_oracle_f32_pins.py)
+
+import tests.test_oracle_f32_pins as f32pins  # noqa: E402
+
+
+def test_f32_attention_without_scale_is_caught(monkeypatch):
+    import torch
+    orig = ov.block_sparse_attention_f32
+
+    def bad(q, k, v, plan, row_ptr, col_idx, heads=None):
+        d = torch.as_tensor(q).shape[-1]
+        # logits unscaled: feed q * sqrt(d) to the correct function
+        return orig(torch.as_tensor(q).to(torch.float32) * math.sqrt(d), k, v, plan, row_ptr,
+                    col_idx, heads)
+    _patch(monkeypatch, "block_sparse_attention_f32", bad)
+    _fails(f32pins.test_f32_attention_matches_dense_masked_bruteforce, 4)
+
+
+def test_f32_selection_tie_to_higher_index_is_caught(monkeypatch):
+    orig = ov.vsa_reference_f32
+
+    def bad(q, k, v, dit_seq_shape, block_size, topk, heads=None):
+        ref = orig(q, k, v, dit_seq_shape, block_size, topk, heads)
+        s = ref["scores"]
+        nb = s.shape[-1]
+        import torch
+        order = torch.sort(-s.flip(-1), dim=-1, stable=True).indices[..., :topk]
+        ref["sel"] = np.sort((nb - 1 - order).numpy(), axis=-1)
+        return ref
+    _patch(monkeypatch, "vsa_reference_f32", bad)
+    _fails(f32pins.test_f32_selection_planted_exact_ties_prefer_lower_index)

@@ -218,6 +218,21 @@ def test_topk_planted_exact_ties_prefer_lower_index():
         assert sel[0, 0, i].tolist() == sorted(order)
 
 
+def test_topk_ranks_full_precision_scores():
+    # Two scores closer than one float32 ulp: rounded to float32 they would
+    # tie and the lower index would win; the definition ranks the scores
+    # themselves, so the larger one (the higher index here) is kept.
+    a = 1.0
+    b = 1.0 + 2.0 ** -30
+    assert np.float32(a) == np.float32(b) and b > a
+    sel, margin = oracle.select_topk(np.array([[a, b, 0.5]]), 1)
+    assert sel.tolist() == [[1]] and margin.tolist() == [b - a]
+    sel, _ = oracle.select_topk(np.array([[0.25, a, -3.0, b]]), 2)
+    assert sel.tolist() == [[1, 3]]
+    sel, _ = oracle.select_topk(np.array([[0.25, a, -3.0, b]]), 1)
+    assert sel.tolist() == [[3]]
+
+
 # ---------------------------------------------------------------- CSR compaction
 
 def test_map_to_csr_hand_example():
