@@ -26,7 +26,7 @@ __all__ = [
     "vsa_forward_workspace_size", "vsa_forward", "vsa_block_sparse_attn_fwd_raster",
     "vsa_forward_fused_workspace_size", "vsa_forward_fused", "vsa_attn_fwd_workspace_size",
     "vsa_block_sparse_attn_fwd_ws", "vsa_block_sparse_attn_fwd_raster_ws", "vsa_status_string",
-    "vsa_last_error",
+    "vsa_last_error", "vsa_bench_mfma_peak", "vsa_bench_hbm_copy",
 ]
 
 VSA_OK, VSA_ERR_INVALID_ARGUMENT, VSA_ERR_UNSUPPORTED, VSA_ERR_HIP = 0, 1, 2, 3
@@ -93,6 +93,9 @@ _SIGS = {
     "vsa_block_sparse_attn_fwd_raster_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                              ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                              _P], ctypes.c_int),
+    "vsa_bench_mfma_peak": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.POINTER(ctypes.c_int64),
+                             _P], ctypes.c_int),
+    "vsa_bench_hbm_copy": ([_P, _P, ctypes.c_int64, _P], ctypes.c_int),
     "vsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "vsa_last_error": ([], ctypes.c_char_p),
 }
@@ -481,3 +484,24 @@ def vsa_forward(plan: Plan, q, k, v, out, workspace, col_idx_out=None, lse=None,
         _ptr(col_idx_out, plan.num_rows() * max(plan.topk, 0), _i32(), "col_idx_out"),
         _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
         _stream(stream, q, out)))
+
+
+# ------------------------------------------------------------------ measurement kernels
+
+def vsa_bench_mfma_peak(num_workgroups: int, iters: int, timing, stream=None) -> int:
+    """Launch the dense bf16 MFMA loop; fills `timing` (int64 device tensor of
+    16 * num_workgroups entries) and returns the wall clock's rate in Hz."""
+    import torch
+    hz = ctypes.c_int64()
+    _check(load_library().vsa_bench_mfma_peak(
+        int(num_workgroups), int(iters), _ptr(timing, 16 * int(num_workgroups), torch.int64,
+                                              "timing"),
+        ctypes.byref(hz), _stream(stream, timing)))
+    return hz.value
+
+
+def vsa_bench_hbm_copy(src, dst, nbytes: int, stream=None):
+    """dst[:nbytes] = src[:nbytes] on the device (uint8 tensors or raw addresses)."""
+    _check(load_library().vsa_bench_hbm_copy(
+        _ptr(src, int(nbytes), None, "src"), _ptr(dst, int(nbytes), None, "dst"), int(nbytes),
+        _stream(stream, src, dst)))

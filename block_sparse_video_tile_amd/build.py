@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libvsa_amd.so")
 ARCH = "gfx950"
 
-SOURCES = ["vsa_api.cpp", "gather_scatter.hip", "score_topk.hip", "attention.hip", "coarse.hip", "backward.hip"]
+SOURCES = ["vsa_api.cpp", "gather_scatter.hip", "score_topk.hip", "attention.hip", "coarse.hip", "backward.hip",
+           "microbench.hip"]
 
 # Packed fp32 VALU ops are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

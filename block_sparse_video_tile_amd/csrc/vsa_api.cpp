@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <new>
 #include <string>
 
@@ -37,6 +38,15 @@ vsa_status hip_status(hipError_t e, const char* what) {
 }
 
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// True when any non-null pointer of the list is not a multiple of `a` bytes
+// (element tensors are read and written as 16-byte units, fp32 and int32
+// arrays as 4-byte words).
+bool misaligned(uintptr_t a, std::initializer_list<const void*> ptrs) {
+  for (const void* x : ptrs)
+    if ((reinterpret_cast<uintptr_t>(x) & (a - 1)) != 0) return true;
+  return false;
+}
 
 struct Workspace {
   size_t q, k, v, o, qp, kp, vp, oc, col, queue, total;
@@ -276,6 +286,9 @@ vsa_status vsa_gather(vsa_plan_t p, int32_t role, const void* x, void* xb, float
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: null argument");
   if (role != VSA_ROLE_Q && role != VSA_ROLE_K && role != VSA_ROLE_V)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_gather: unknown role %d", role);
+  if (misaligned(16, {x, xb}) || misaligned(4, {pooled}))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_gather: x_raster and x_blk must be 16-byte aligned, pooled 4-byte aligned");
   if (!xb)  // block means only, for any role
     return hip_status(vsa::launch_gather_qk(p->g, x, nullptr, pooled, hipStream_t(stream)),
                       "vsa_gather(pooling)");
@@ -288,6 +301,8 @@ vsa_status vsa_gather(vsa_plan_t p, int32_t role, const void* x, void* xb, float
 
 vsa_status vsa_scatter(vsa_plan_t p, const void* ob, void* o, void* stream) {
   if (!p || !ob || !o) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter: null argument");
+  if (misaligned(16, {ob, o}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter: o_blk and o_raster not 16-byte aligned");
   return hip_status(vsa::launch_scatter(p->g, ob, nullptr, nullptr, o, hipStream_t(stream)),
                     "vsa_scatter");
 }
@@ -298,6 +313,8 @@ vsa_status vsa_compress_attn(vsa_plan_t p, const float* qp, const float* kp, con
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_compress_attn: null argument");
   if ((reinterpret_cast<uintptr_t>(kp) & 15) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_compress_attn: k_pooled not 16-byte aligned");
+  if (misaligned(4, {qp, vp, oc}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_compress_attn: pooled arrays not 4-byte aligned");
   if (p->g.nb > 1024)
     return fail(VSA_ERR_UNSUPPORTED, "vsa_compress_attn: num_blocks %d > 1024 not implemented",
                 p->g.nb);
@@ -311,6 +328,9 @@ vsa_status vsa_scatter_gated(vsa_plan_t p, const void* ob, const float* oc, cons
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter_gated: null argument");
   if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_scatter_gated: o_coarse not 16-byte aligned");
+  if (misaligned(16, {ob, gate, o}))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_scatter_gated: o_blk, gate and o_raster not 16-byte aligned");
   return hip_status(vsa::launch_scatter(p->g, ob, oc, gate, o, hipStream_t(stream)),
                     "vsa_scatter_gated");
 }
@@ -322,6 +342,11 @@ vsa_status vsa_score_topk(vsa_plan_t p, const float* qp, const float* kp, int32_
   if (topk < 1 || topk > p->g.nb)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_score_topk: topk %d outside [1, %d]", topk,
                 p->g.nb);
+  if (misaligned(16, {kp}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_score_topk: k_pooled not 16-byte aligned");
+  if (misaligned(4, {qp, col, scores}))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_score_topk: q_pooled, col_idx and scores not 4-byte aligned");
   if (p->g.nb > 1024)
     return fail(VSA_ERR_UNSUPPORTED, "vsa_score_topk: num_blocks %d > 1024 not implemented",
                 p->g.nb);
@@ -342,6 +367,10 @@ vsa_status check_attn_args(const char* fn, vsa_plan_t p, const void* q, const vo
   if (nnz < 0) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: nnz < 0", fn);
   if (nnz > 0 && !col)
     return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null col_idx with nnz > 0", fn);
+  if (misaligned(16, {q, k, v, o}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: q, k, v and o must be 16-byte aligned", fn);
+  if (misaligned(4, {row_ptr, col}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: row_ptr and col_idx must be 4-byte aligned", fn);
   const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
   if (!row_ptr) {
     if (uniform_k < 0 || uniform_k > p->g.nb)
@@ -354,12 +383,19 @@ vsa_status check_attn_args(const char* fn, vsa_plan_t p, const void* q, const vo
   return ok();
 }
 
+vsa_status check_lse(const char* fn, const float* lse) {
+  if (misaligned(4, {lse})) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: lse not 4-byte aligned", fn);
+  return ok();
+}
+
 vsa_status check_raster_args(const char* fn, vsa_plan_t p, const void* gate, const float* oc) {
   if ((gate == nullptr) != (oc == nullptr))
     return fail(VSA_ERR_INVALID_ARGUMENT, "%s: gate and o_coarse must both be given or both NULL",
                 fn);
   if ((reinterpret_cast<uintptr_t>(oc) & 15) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "%s: o_coarse not 16-byte aligned", fn);
+  if (misaligned(16, {gate}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: gate not 16-byte aligned", fn);
   if (const char* why = raster_unsupported(p->g))
     return fail(VSA_ERR_UNSUPPORTED, "%s: %s", fn, why);
   return ok();
@@ -386,6 +422,7 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k,
                                      void* stream) {
   static const char* fn = "vsa_block_sparse_attn_fwd";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_lse(fn, lse)) return st;
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
                                          nullptr, hipStream_t(stream)),
                     fn);
@@ -403,6 +440,7 @@ vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t p, const void* q, const void*
                                         void* ws, size_t ws_bytes, void* stream) {
   static const char* fn = "vsa_block_sparse_attn_fwd_ws";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
                                          static_cast<unsigned int*>(ws), hipStream_t(stream)),
@@ -416,6 +454,7 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const v
                                             float* lse, void* stream) {
   static const char* fn = "vsa_block_sparse_attn_fwd_raster";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
                                                 lse, gate, oc, nullptr, hipStream_t(stream)),
@@ -430,6 +469,7 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t p, const void* q, cons
                                                void* stream) {
   static const char* fn = "vsa_block_sparse_attn_fwd_raster_ws";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
   return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
@@ -465,6 +505,12 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t p, const void* q, const void* k,
                   "vsa_block_sparse_attn_bwd: nnz %lld < rows*uniform_k = %lld", (long long)nnz,
                   (long long)(rows * uniform_k));
   }
+  if (misaligned(16, {q, k, v, o, dout, dq, dk, dv}))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_bwd: element tensors must be 16-byte aligned");
+  if (misaligned(4, {lse, row_ptr, col}))
+    return fail(VSA_ERR_INVALID_ARGUMENT,
+                "vsa_block_sparse_attn_bwd: lse, row_ptr and col_idx must be 4-byte aligned");
   if (p->g.nb > 4096)
     return fail(VSA_ERR_UNSUPPORTED,
                 "vsa_block_sparse_attn_bwd: num_blocks %d > 4096 not implemented", p->g.nb);
@@ -511,6 +557,10 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
                 ws_bytes, w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: workspace not 256-byte aligned");
+  if (misaligned(16, {q, k, v, gate, out}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: q, k, v, gate and out must be 16-byte aligned");
+  if (misaligned(4, {col_out, lse}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward: col_idx_out and lse must be 4-byte aligned");
   char* base = static_cast<char*>(ws);
   void* qb = base + w.q;
   void* kb = base + w.k;
@@ -567,6 +617,10 @@ vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const v
                 ws_bytes, w.total);
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: workspace not 256-byte aligned");
+  if (misaligned(16, {q, k, v, gate, out}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: q, k, v, gate and out must be 16-byte aligned");
+  if (misaligned(4, {col_out, lse}))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_forward_fused: col_idx_out and lse must be 4-byte aligned");
   char* base = static_cast<char*>(ws);
   float* qp = reinterpret_cast<float*>(base + w.qp);
   float* kp = reinterpret_cast<float*>(base + w.kp);
@@ -594,6 +648,42 @@ vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const v
                                        gate ? oc : nullptr, queues, s)) != hipSuccess)
     return hip_status(e, "vsa_forward_fused: attention");
   return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- measurement kernels
+
+extern "C" {
+
+vsa_status vsa_bench_mfma_peak(int32_t num_workgroups, int32_t iters, uint64_t* timing,
+                               int64_t* wall_clock_hz, void* stream) {
+  static const char* fn = "vsa_bench_mfma_peak";
+  if (!timing || !wall_clock_hz)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null timing or wall_clock_hz", fn);
+  if (num_workgroups < 1 || num_workgroups > (1 << 20))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: num_workgroups %d outside [1, 2^20]", fn,
+                num_workgroups);
+  if (iters < 1) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: iters %d < 1", fn, iters);
+  if ((reinterpret_cast<uintptr_t>(timing) & 7) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: timing not 8-byte aligned", fn);
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return hip_status(e, "vsa_bench_mfma_peak: wall clock rate");
+  *wall_clock_hz = int64_t(khz) * 1000;
+  return hip_status(vsa::launch_mfma_peak(num_workgroups, iters, timing, hipStream_t(stream)), fn);
+}
+
+vsa_status vsa_bench_hbm_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  static const char* fn = "vsa_bench_hbm_copy";
+  if (!src || !dst) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null buffer", fn);
+  if (bytes < 16 || bytes % 16 != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: bytes %lld not a positive multiple of 16", fn,
+                (long long)bytes);
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) != 0)
+    return fail(VSA_ERR_INVALID_ARGUMENT, "%s: buffers not 16-byte aligned", fn);
+  return hip_status(vsa::launch_hbm_copy(src, dst, bytes, hipStream_t(stream)), fn);
 }
 
 }  // extern "C"

@@ -98,4 +98,8 @@ hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k
                                   int64_t nnz, void* o, float* lse, const void* gate,
                                   const float* oc, unsigned int* queues, hipStream_t s);
 
+// Measurement kernels (microbench.hip): `timing` holds 4 uint64 per wave.
+hipError_t launch_mfma_peak(int num_workgroups, int iters, uint64_t* timing, hipStream_t s);
+hipError_t launch_hbm_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
 }  // namespace vsa

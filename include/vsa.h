@@ -28,6 +28,11 @@
  *     plan's dtype, 2-byte bfloat16 or IEEE binary16 ("Verify routing and
  *     fallback" admits FP16 or BF16); fp32 is IEEE binary32, indices are
  *     int32.  Pooled means, scores and LSE are fp32 for either dtype.
+ *   - Alignment: elem tensors (Q, K, V, O, gate, gradients) are read and
+ *     written as 16-byte units and must be 16-byte aligned; k_pooled and
+ *     o_coarse are read as float4 and must be 16-byte aligned too; every
+ *     other fp32 or int32 array must be 4-byte aligned.  A misaligned
+ *     pointer is INVALID_ARGUMENT.
  *   - Host-side argument checks happen before any HIP call, so every
  *     VSA_ERR_INVALID_ARGUMENT / VSA_ERR_UNSUPPORTED path works without a GPU.
  *
@@ -144,8 +149,13 @@ vsa_status vsa_plan_block_counts(vsa_plan_t plan, int32_t* counts, int64_t n);
 vsa_status vsa_gather(vsa_plan_t plan, int32_t role, const void* x_raster, void* x_blk,
                       float* pooled, void* stream);
 
-/* Blocked -> raster scatter of an output tensor (pad rows are dropped).
- * o_blk: device, blocked layout, elem.  o_raster: device, raster layout, elem. */
+/* Blocked -> raster scatter of an output tensor: the inverse of vsa_gather's
+ * token permutation, so that the attention output is handed back in the
+ * post-patch latent order the layer received ("FastVideo VSA" guide, intro:
+ * the blocks are a partition of that grid; "Choose top-k": padding of edge
+ * blocks is an overhead of the tiling, not part of the result).  Pad rows are
+ * dropped.  o_blk: device, blocked layout, elem.  o_raster: device, raster
+ * layout, elem.  Errors: INVALID_ARGUMENT for a null plan or buffer. */
 vsa_status vsa_scatter(vsa_plan_t plan, const void* o_blk, void* o_raster, void* stream);
 
 /* Gate-compress (coarse) branch ("FastVideo VSA" guide, "Checkpoint
@@ -346,6 +356,32 @@ vsa_status vsa_forward_fused(vsa_plan_t plan, const void* q, const void* k, cons
                              const void* gate, void* out, void* workspace,
                              size_t workspace_bytes, int32_t* col_idx_out, float* lse,
                              void* stream);
+
+/* ---- Measurement kernels: the roofline denominators of the kernels above,
+ * measured on the machine that runs them (dense bf16 matrix-core rate and
+ * engine clock, plain copy bandwidth).  They compute nothing of the method.
+ *
+ * vsa_bench_mfma_peak: launches num_workgroups workgroups of 4 waves; every
+ * wave issues iters * 16 v_mfma_f32_32x32x16_bf16 (32768 flops each) on four
+ * independent accumulators and records, in lane 0, timing[4w + 0] = shader
+ * clock cycles and timing[4w + 1] = constant-rate wall-clock ticks spent in
+ * its loop (timing[4w + 2] holds a checksum of the products, [4w + 3] = 0);
+ * w = workgroup * 4 + wave.  timing: device, 16*num_workgroups uint64,
+ * 8-byte aligned.  *wall_clock_hz (host) receives the wall clock's rate, so
+ * cycles / (ticks / rate) is the engine clock the loop ran at.  Flops / the
+ * kernel's duration is the sustained dense bf16 rate.
+ * Errors: INVALID_ARGUMENT for null pointers, num_workgroups outside
+ *   [1, 2^20], iters < 1 or a misaligned timing buffer; HIP for a failed
+ *   device query or launch. */
+vsa_status vsa_bench_mfma_peak(int32_t num_workgroups, int32_t iters, uint64_t* timing,
+                               int64_t* wall_clock_hz, void* stream);
+
+/* vsa_bench_hbm_copy: dst[0 .. bytes) = src[0 .. bytes) with 16-byte loads
+ * and stores (bytes read + bytes written = 2 * bytes of HBM traffic when the
+ * buffers exceed the caches).  src, dst: device, 16-byte aligned, not
+ * overlapping.  Errors: INVALID_ARGUMENT for null or misaligned buffers or
+ * bytes not a positive multiple of 16; HIP for a failed launch. */
+vsa_status vsa_bench_hbm_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 /* Static description of a status code. */
 const char* vsa_status_string(vsa_status status);

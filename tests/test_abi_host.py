@@ -278,3 +278,78 @@ def test_balanced_attention_workspace_checks(plan):
     # the layer entry points carry the queues in their own workspaces
     assert vsa.vsa_forward_workspace_size(plan) % 256 == 0
     assert vsa.vsa_forward_fused_workspace_size(plan) % 256 == 0
+
+
+def test_alignment_checks_before_any_device_call(plan):
+    """Element tensors are moved as 16-byte units and fp32/int32 arrays as
+    4-byte words: an offset pointer is rejected before any device call."""
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    m16, m4 = FAKE + 8, FAKE + 2
+    rows = plan.num_rows()
+    assert _raw("vsa_gather", h, 0, m16, FAKE, None, None) == bad
+    assert _raw("vsa_gather", h, 0, FAKE, m16, None, None) == bad
+    assert _raw("vsa_gather", h, 0, FAKE, None, m4, None) == bad
+    assert _raw("vsa_scatter", h, m16, FAKE, None) == bad
+    assert _raw("vsa_scatter", h, FAKE, m16, None) == bad
+    assert _raw("vsa_score_topk", h, FAKE, FAKE + 4, 4, FAKE, None, None) == bad   # float4 reads
+    assert _raw("vsa_score_topk", h, m4, FAKE, 4, FAKE, None, None) == bad
+    assert _raw("vsa_score_topk", h, FAKE, FAKE, 4, m4, None, None) == bad
+    assert _raw("vsa_score_topk", h, FAKE, FAKE, 4, FAKE, m4, None) == bad
+    assert "aligned" in vsa.vsa_last_error()
+    assert _raw("vsa_scatter_gated", h, FAKE, FAKE, m16, FAKE, None) == bad
+    assert _raw("vsa_compress_attn", h, m4, FAKE, FAKE, FAKE, None) == bad
+    # attention: (plan, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, stream)
+    f = "vsa_block_sparse_attn_fwd"
+    for idx in (1, 2, 3, 8):
+        a = [h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None, None]
+        a[idx] = m16
+        assert _raw(f, *a) == bad, idx
+    assert _raw(f, h, FAKE, FAKE, FAKE, m4, FAKE, 0, 8, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, m4, 4, rows * 4, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, m4, None) == bad
+    assert "lse" in vsa.vsa_last_error()
+    g = "vsa_block_sparse_attn_fwd_ws"
+    assert _raw(g, h, m16, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None, FAKE, 256, None) == bad
+    r = "vsa_block_sparse_attn_fwd_raster"
+    assert _raw(r, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, m16, FAKE, FAKE, None,
+                None) == bad   # gate
+    assert _raw(r, h, FAKE, m16, FAKE, None, FAKE, 4, rows * 4, None, None, FAKE, None,
+                None) == bad
+    rw = "vsa_block_sparse_attn_fwd_raster_ws"
+    assert _raw(rw, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, None, None, m16, None, FAKE,
+                256, None) == bad
+    # backward: (plan, q, k, v, o, do, lse, row_ptr, col, uk, nnz, dq, dk, dv, ws, ws_bytes, s)
+    need = vsa.vsa_block_sparse_attn_bwd_workspace_size(plan)
+    base = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE,
+            need, None]
+    for idx, val in ((2, m16), (5, m16), (6, m4), (8, m4), (13, m16)):
+        a = list(base)
+        a[idx] = val
+        assert _raw("vsa_block_sparse_attn_bwd", *a) == bad, idx
+    # whole-path entry points: (plan, q, k, v, gate, out, ws, ws_bytes, col_out, lse, stream)
+    for fn, size in (("vsa_forward", vsa.vsa_forward_workspace_size(plan)),
+                     ("vsa_forward_fused", vsa.vsa_forward_fused_workspace_size(plan))):
+        assert _raw(fn, h, FAKE, FAKE, m16, None, FAKE, FAKE, size, None, None, None) == bad
+        assert _raw(fn, h, FAKE, FAKE, FAKE, m16, FAKE, FAKE, size, None, None, None) == bad
+        assert _raw(fn, h, FAKE, FAKE, FAKE, None, FAKE, FAKE, size, m4, None, None) == bad
+        assert _raw(fn, h, FAKE, FAKE, FAKE, None, FAKE, FAKE, size, None, m4, None) == bad
+
+
+def test_measurement_kernel_checks():
+    import ctypes
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    hz = ctypes.c_int64()
+    f = "vsa_bench_mfma_peak"   # (num_workgroups, iters, timing, wall_clock_hz, stream)
+    assert _raw(f, 0, 10, FAKE, ctypes.byref(hz), None) == bad
+    assert _raw(f, (1 << 20) + 1, 10, FAKE, ctypes.byref(hz), None) == bad
+    assert _raw(f, 4, 0, FAKE, ctypes.byref(hz), None) == bad
+    assert _raw(f, 4, 10, None, ctypes.byref(hz), None) == bad
+    assert _raw(f, 4, 10, FAKE, None, None) == bad
+    assert _raw(f, 4, 10, FAKE + 4, ctypes.byref(hz), None) == bad
+    g = "vsa_bench_hbm_copy"    # (src, dst, bytes, stream)
+    assert _raw(g, None, FAKE, 64, None) == bad
+    assert _raw(g, FAKE, FAKE, 0, None) == bad
+    assert _raw(g, FAKE, FAKE, 40, None) == bad
+    assert _raw(g, FAKE + 8, FAKE, 64, None) == bad
+    assert "16-byte" in vsa.vsa_last_error()

@@ -12,7 +12,7 @@ import torch
 import block_sparse_video_tile_amd as vsa
 import oracle
 from tests.gpu_common import (DEV, MARGIN, MAX_ABS, MEAN_ABS, _gather_all, _host, _plan, _say,
-                              _sample_rows, need_gpu)
+                              check_selection_rows, compare_all_rows, need_gpu)
 from vsa_inputs import WORKLOADS, bf16_to_f64, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -128,30 +128,19 @@ def test_forward_gated_end_to_end(name, dtype):
     assert torch.equal(out_plain, out_zero)
 
 
-def test_forward_gated_full_size_sampled():
+def test_forward_gated_full_size_every_row():
     wl = WORKLOADS["wan5b_k64"]
     gate = _gate(wl)
     plan, q, kk, v, out, col = _gated_forward(wl, wl.topk, gate)
     oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, wl.topk)
     q64, k64, v64 = bf16_to_f64(q), bf16_to_f64(kk), bf16_to_f64(v)
     qbar, kbar, vbar = (oracle.pool_blocks(x, oplan) for x in (q64, k64, v64))
-    sel, margin = oracle.select_topk(oracle.block_scores(qbar, kbar), wl.topk)
-    gsel = col.reshape(sel.shape)
-    exact = margin >= MARGIN
-    assert np.array_equal(gsel[exact], sel[exact])
-    rows = [r for r in _sample_rows(oplan, wl.heads, wl.batch) if exact.reshape(-1)[r]]
+    gsel = col.reshape(wl.batch, wl.heads, oplan.num_blocks, wl.topk)
+    check_selection_rows(gsel, oracle.block_scores(qbar, kbar), wl.topk)
     rp, ci = oracle.selection_to_csr(gsel)
-    o_sparse, _ = oracle.block_sparse_attention(q64, k64, v64, oplan, rp, ci, query_rows=rows)
+    # every row: the float32 block loop for the sparse branch, the float64
+    # coarse branch and gated combination
+    o_sparse, _ = oracle.block_sparse_attention_f32(q, kk, v, oplan, rp, ci)
     oc = oracle.compress_attention(qbar, kbar, vbar, wl.head_dim)
-    want = oracle.gated_combine(np.nan_to_num(o_sparse), oc, bf16_to_f64(gate), oplan)
-    lists = oracle.block_token_lists(oplan)
-    nb = oplan.num_blocks
-    errs = []
-    for r in rows:
-        b, rem = divmod(r, wl.heads * nb)
-        h, i = divmod(rem, nb)
-        toks = lists[i]
-        errs.append(np.abs(out[b, toks, h].double().numpy() - want[b, toks, h]).reshape(-1))
-    e = np.concatenate(errs)
-    _say(f"    {len(rows)} rows: max-abs {e.max():.3e} mean-abs {e.mean():.3e}")
-    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS
+    want = oracle.gated_combine(o_sparse.double().numpy(), oc, bf16_to_f64(gate), oplan)
+    compare_all_rows("gated, all rows vs oracle", out, want)

@@ -12,7 +12,7 @@ import torch
 import block_sparse_video_tile_amd as vsa
 import oracle
 from tests.gpu_common import (DEV, MAX_ABS, MEAN_ABS, _attend, _compare_rows, _gather_all,
-                              _host, _plan, _say, check_full_forward_sampled, need_gpu)
+                              _host, _plan, _say, check_full_forward, need_gpu)
 from vsa_inputs import WORKLOADS, bf16_to_f64 as to_f64, make_qkv, make_tile64_map
 
 pytestmark = pytest.mark.gpu
@@ -83,8 +83,8 @@ def test_fp16_attention_csr_with_zero_rows():
     assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= 1e-3
 
 
-def test_fp16_full_size_forward_sampled():
-    check_full_forward_sampled("wan5b_k64", dtype=F16)
+def test_fp16_full_size_forward_every_row():
+    check_full_forward("wan5b_k64", dtype=F16)
 
 
 def test_fp16_rejects_bf16_tensors():

@@ -18,7 +18,7 @@ import block_sparse_video_tile_amd as vsa
 import oracle
 from tests.gpu_common import (DEV, MARGIN, MAX_ABS, MEAN_ABS, _attend, _compare_rows,
                               _full_forward, _gather_all, _host, _plan, _say,
-                              check_full_forward_sampled, need_gpu)
+                              blocked_positions, check_full_forward, compare_all_rows, need_gpu)
 from vsa_inputs import (WORKLOADS, bf16_to_f64, make_planted_block_means, make_qkv,
                         make_tile64_map)
 
@@ -263,27 +263,56 @@ def test_forward_tiny_end_to_end_and_deterministic():
 
 @pytest.mark.parametrize("name,k", [("wan5b_k64", None), ("wan5b_k16", None), ("wan5b_k32", None),
                                     ("wan13b_long", None)])
-def test_full_size_forward_sampled(name, k):
-    check_full_forward_sampled(name, k)
+def test_full_size_forward_every_row(name, k):
+    # every row of every head vs the float32 oracle, two whole heads vs float64
+    check_full_forward(name, k)
+
+
+def test_full_size_attention_fed_oracle_map_every_row():
+    """Attention fed the float64 oracle's own selection (not the GPU's), every row."""
+    wl = WORKLOADS["wan5b_k64"]
+    k = wl.topk
+    q, kk, v = make_qkv(wl)
+    plan = _plan(wl, k)
+    oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, k)
+    q64, k64 = bf16_to_f64(q), bf16_to_f64(kk)
+    sc = oracle.block_scores(oracle.pool_blocks(q64, oplan), oracle.pool_blocks(k64, oplan))
+    sel, margin = oracle.select_topk(sc, k)
+    _say(f"    oracle map: near-tie rows {int((margin < MARGIN).sum())} of {margin.size}")
+    rp, ci = oracle.selection_to_csr(sel)
+    qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
+    ob, lse = _attend(plan, qb, kb, vb, None, ci, uniform_k=k)
+    out = torch.empty(plan.raster_shape(), dtype=torch.bfloat16, device=DEV)
+    vsa.vsa_scatter(plan, ob, out)
+    torch.cuda.synchronize()
+    o32, l32 = oracle.block_sparse_attention_f32(q, kk, v, oplan, rp, ci)
+    compare_all_rows("oracle map, all rows vs float32 oracle", out.cpu(), o32, lse.cpu().numpy(),
+                     l32.numpy(), oplan)
+    # pad query slots of the blocked output are written as zero
+    _, _, pads = blocked_positions(oplan)
+    assert torch.all(ob[:, :, pads] == 0)
 
 
 def test_all_blocks_equals_dense_attention_full_size():
     # topk == num_blocks: the sparse kernel over every block is dense attention
-    wl, k, q, kk, v, plan, out, col, lse = _full_forward("wan5b_k120")
+    wl, k, q, kk, v, plan, out, col, lse = check_full_forward("wan5b_k120")
     assert np.array_equal(col.reshape(-1, 120), np.tile(np.arange(120), (plan.num_rows(), 1)))
-    rng = np.random.default_rng(7)
-    for h in (0, 13, 23):
-        toks = np.sort(rng.choice(wl.seq_len, 96, replace=False))
-        tq = q[0, toks, h].double()
-        tk = kk[0, :, h].double()
-        tv = v[0, :, h].double()
-        dense = torch.softmax(tq @ tk.T / math.sqrt(wl.head_dim), dim=-1) @ tv
-        err = (out[0, toks, h].double() - dense).abs()
+    # two whole heads against torch's dense attention over all 27280 tokens
+    for h in (0, 23):
+        tq, tk, tv = (t[0, :, h].to(torch.float32) for t in (q, kk, v))
+        errs = []
+        for c0 in range(0, wl.seq_len, 2048):
+            dense = torch.nn.functional.scaled_dot_product_attention(
+                tq[None, c0:c0 + 2048], tk[None], tv[None])[0]
+            errs.append((out[0, c0:c0 + 2048, h].to(torch.float32) - dense).abs())
+        err = torch.cat(errs)
+        _say(f"    head {h} vs dense SDPA: max-abs {err.max().item():.3e} "
+             f"mean-abs {err.mean().item():.3e}")
         assert err.max().item() <= MAX_ABS and err.mean().item() <= MEAN_ABS
 
 
 @pytest.mark.parametrize("name", ["tile64_csr", "tile64_csr_zero"])
-def test_tile64_csr_full_size_sampled(name):
+def test_tile64_csr_full_size_every_row(name):
     wl = WORKLOADS[name]
     q, kk, v = make_qkv(wl)
     rp, ci, nt = make_tile64_map(wl)
@@ -292,15 +321,21 @@ def test_tile64_csr_full_size_sampled(name):
     qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
     ob, lse = _attend(plan, qb, kb, vb, rp, ci)
     torch.cuda.synchronize()
+    # 1-D 64-token tiles of a 64-divisible sequence: the blocked layout is the raster one
+    got = ob.cpu().permute(0, 2, 1, 3)
+    o32, l32 = oracle.block_sparse_attention_f32(q, kk, v, oplan, rp, ci)
+    compare_all_rows("all rows vs float32 oracle", got, o32, lse.cpu().numpy(), l32.numpy(),
+                     oplan)
+    rows = list(range(nt)) + list(range(23 * nt, 24 * nt))
+    o64, l64 = oracle.block_sparse_attention(bf16_to_f64(q), bf16_to_f64(kk), bf16_to_f64(v),
+                                             oplan, rp, ci, query_rows=rows)
+    compare_all_rows("heads [0, 23] vs float64 oracle", got, o64, lse.cpu().numpy(), l64, oplan,
+                     heads=(0, 23))
     counts = np.diff(rp)
-    rows = sorted(set([0, 7, 8, 9, nt - 1, nt * 23, nt * 23 + 3, nt * 12 + 300] +
-                      [int(r) for r in np.nonzero(counts == 0)[0][:3]] +
-                      [int(r) for r in np.nonzero(counts == counts.max())[0][:2]]))
-    q64, k64, v64 = bf16_to_f64(q), bf16_to_f64(kk), bf16_to_f64(v)
-    ref_o, ref_l = oracle.block_sparse_attention(q64, k64, v64, oplan, rp, ci, query_rows=rows)
-    mx, mean, lerr = _compare_rows(oplan, _host(ob), _host(lse), ref_o, ref_l, rows, wl.heads, 64)
-    _say(f"    {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e} lse {lerr:.2e}")
-    assert mx <= MAX_ABS and mean <= MEAN_ABS and lerr <= 1e-3
+    for r in np.nonzero(counts == 0)[0]:
+        h, i = divmod(int(r), nt)
+        assert torch.all(got[0, i * 64:(i + 1) * 64, h] == 0)
+    _say(f"    rows with no blocks: {int((counts == 0).sum())}; longest row {int(counts.max())}")
 
 
 def test_repeat_runs_bitwise_equal_full_size():

@@ -14,7 +14,7 @@ import torch
 import block_sparse_video_tile_amd as vsa
 import oracle
 from tests.gpu_common import (DEV, MARGIN, MAX_ABS, MEAN_ABS, _attend, _gather_all, _plan, _say,
-                              check_full_forward_sampled, need_gpu)
+                              check_full_forward, need_gpu)
 from tests.test_gpu_coarse import _gate
 from vsa_inputs import WORKLOADS, bf16_to_f64, make_qkv, make_tile64_map
 
@@ -201,5 +201,5 @@ def test_fused_forward_gated(name, dtype):
 
 
 @pytest.mark.parametrize("name", ["wan5b_k64", "wan13b_long"])
-def test_fused_forward_full_size_sampled(name):
-    check_full_forward_sampled(name, fused=True)
+def test_fused_forward_full_size_every_row(name):
+    check_full_forward(name, fused=True)
