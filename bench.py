@@ -15,7 +15,11 @@ Metric: effective TFLOP/s counting the selected blocks' valid tokens only
 (4 * D * sum over query blocks i of c_i * sum_{j in row i} c_j, from the map
 the step produced), divided by the whole step time; ms/layer is reported
 alongside.  The attention kernel's own rate against the dense MFMA peak is the
-roofline object.
+roofline object, with the MFMA rate, engine clock and copy bandwidth measured
+on the same machine beside the published figures (measure_denominators).
+Unless --no-cpu-baseline is given, the step's block ids are checked against
+the float64 oracle (map_check: near-tie rows counted) and the float32 CPU
+oracle is timed over the same layer on the host's cores (cpu_baseline).
 
 Default workload: the 27280-token (31, 22, 40) layer, block (4, 8, 8),
 24 heads, head_dim 128, topk 64, bf16 -- the shape of the routing example in
@@ -26,9 +30,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 Two helper modes serve the HBM traffic record of the attention kernel:
   python bench.py --copy-calibration MIB
-      runs a plain device copy (dst = src * 1, fp32) of MIB MiB a few times, so
-      that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE can be read for a kernel
-      whose byte count is known;
+      runs the library's plain device copy (vsa_bench_hbm_copy, hbm_copy_kernel)
+      of MIB MiB a few times, so that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+      can be read for a kernel whose byte count is known;
   python bench.py --record-traffic FETCH.csv WRITE.csv CAL_FETCH.csv CAL_WRITE.csv
                   --cal-mib MIB [--workload NAME] [--traffic-json PATH]
       turns the four counter_collection.csv files (attention runs, then the
@@ -56,8 +60,12 @@ if ROOT not in sys.path:
 import block_sparse_video_tile_amd as vsa  # noqa: E402
 from vsa_inputs import WORKLOADS, make_qkv, make_tile64_map  # noqa: E402
 
-MFMA_16BIT_PEAK_TFLOPS = 2500.0   # MI355X dense MFMA, bf16 and fp16 alike
+# MI355X published figures: dense bf16/fp16 MFMA 256 CUs x 2.4 GHz x 4096
+# flop/clock = 2516.6 TFLOP/s ("2.5 PFLOP/s"), HBM3E 8 TB/s.
+MFMA_16BIT_PEAK_TFLOPS = 2516.6
 HBM_PEAK_GBS = 8000.0
+MFMA_FLOPS_PER_INSTR = 32 * 32 * 16 * 2   # v_mfma_f32_32x32x16_bf16
+COPY_KERNEL = "hbm_copy_kernel"
 
 STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "scatter"]
 GATED_STAGES = ["gather_q", "gather_k", "gather_v", "score_topk", "attention", "coarse",
@@ -119,14 +127,65 @@ def recorded_traffic(path, workload, dtype, variant="blocked"):
 
 
 def copy_calibration(mib, reps=5):
-    """A plain device copy of a known size for counter calibration."""
-    n = mib * (1 << 20) // 4
-    src = torch.rand(n, device="cuda:0")
+    """The library's plain device copy (vsa_bench_hbm_copy) of a known size,
+    for counter calibration."""
+    n = mib * (1 << 20)
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(reps):
-        torch.mul(src, 1.0, out=dst)
+        vsa.vsa_bench_hbm_copy(src, dst, n)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "reps": reps}))
+    assert torch.equal(src, dst)
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "reps": reps,
+                      "kernel": COPY_KERNEL}))
+
+
+def measure_denominators(dev, mfma_iters=4000, copy_mib=2048, reps=3):
+    """Roofline denominators measured on this machine.
+
+    Dense bf16 MFMA rate: vsa_bench_mfma_peak with two 4-wave workgroups per
+    CU (the attention kernel's two waves per SIMD); flops = waves x iters x 16
+    x 32768 over the launch's HIP-event time, best of `reps`; the engine clock
+    is each wave's shader-clock cycles over its wall-clock time, averaged.
+    Copy bandwidth: vsa_bench_hbm_copy of `copy_mib` MiB, 2 x bytes over the
+    event time, best of `reps`.
+    """
+    props = torch.cuda.get_device_properties(dev)
+    wgs = 2 * props.multi_processor_count
+    timing = torch.zeros(16 * wgs, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    vsa.vsa_bench_mfma_peak(wgs, 100, timing)          # warm-up
+    best_tf, clocks = 0.0, []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        hz = vsa.vsa_bench_mfma_peak(wgs, mfma_iters, timing)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        flops = wgs * 4 * mfma_iters * 16 * MFMA_FLOPS_PER_INSTR
+        best_tf = max(best_tf, flops / (ms * 1e-3) / 1e12)
+        t = timing.view(-1, 4).cpu().numpy().astype(np.float64)
+        clocks.append(float(np.mean(t[:, 0] / (t[:, 1] / hz))) / 1e9)
+    n = copy_mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty_like(src)
+    vsa.vsa_bench_hbm_copy(src, dst, n)
+    best_gbs = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        vsa.vsa_bench_hbm_copy(src, dst, n)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        best_gbs = max(best_gbs, 2 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"mfma_bf16_tflops": round(best_tf, 1), "mfma_clock_ghz": round(float(np.mean(clocks)), 3),
+            "mfma_loop": f"{wgs} workgroups x 4 waves x {mfma_iters} x 16 "
+                         "v_mfma_f32_32x32x16_bf16, best of 3",
+            "hbm_copy_gbs": round(best_gbs, 1),
+            "hbm_copy": f"{copy_mib} MiB device copy (read + write), best of 3",
+            "compute_units": props.multi_processor_count}
 
 
 def _counter_means(path, name_filter):
@@ -150,8 +209,8 @@ def _short_kernel_name(name):
 
 def _calibration_factors(cal_fetch_csv, cal_write_csv, cal_mib):
     cal_bytes = cal_mib * (1 << 20)
-    f = _counter_means(cal_fetch_csv, "vectorized_elementwise_kernel")["FETCH_SIZE"][0]
-    w = _counter_means(cal_write_csv, "vectorized_elementwise_kernel")["WRITE_SIZE"][0]
+    f = _counter_means(cal_fetch_csv, COPY_KERNEL)["FETCH_SIZE"][0]
+    w = _counter_means(cal_write_csv, COPY_KERNEL)["WRITE_SIZE"][0]
     return cal_bytes / (f * 1024.0), cal_bytes / (w * 1024.0)
 
 
@@ -236,7 +295,7 @@ def record_traffic(args):
     for label, att_csv, cal_csv, counter in (("fetch", fetch_csv, cal_fetch_csv, "FETCH_SIZE"),
                                               ("write", write_csv, cal_write_csv, "WRITE_SIZE")):
         att, n_att = _counter_means(att_csv, "attn_fwd_kernel")[counter]
-        cal, n_cal = _counter_means(cal_csv, "vectorized_elementwise_kernel")[counter]
+        cal, n_cal = _counter_means(cal_csv, COPY_KERNEL)[counter]
         factor = cal_bytes / (cal * 1024.0)   # counter reads KiB
         out[label] = {"counter": counter, "kib_per_dispatch": att, "dispatches": n_att,
                       "calibration_kib": cal, "calibration_dispatches": n_cal,
@@ -251,34 +310,87 @@ def record_traffic(args):
     print(json.dumps(rec))
 
 
+def _cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, q, k, v, budget_s):
-    """Time the CPU oracle on whole heads of the same layer until ~budget_s of work."""
+    """The float32 CPU oracle over one layer of the same workload.
+
+    vsa_reference_f32 (pool, score, top-k, then the per-row block loop: one
+    product against the row's concatenated valid keys, softmax, one product
+    with the values) in torch-CPU ops on the host's cores; map workloads run
+    block_sparse_attention_f32 on the given map.  One head is run first as a
+    warm-up; then the whole layer is timed if the warm-up says it fits in
+    about `budget_s`, else as many whole heads as fit, and the layer time is
+    extrapolated from them (said in `sample`).  value = F_valid of the rows
+    computed (the CPU's own map) / their time.
+    """
     import oracle
-    from threadpoolctl import threadpool_info
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    heads_done, flops, t_total = 0, 0, 0.0
-    while heads_done < wl.heads and t_total < budget_s:
-        h = heads_done
-        qs, ks, vs = (t[:, :, h:h + 1].to(torch.float64).numpy() for t in (q, k, v))
-        t0 = time.perf_counter()
+    threads = torch.get_num_threads()
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, wl.topk)
+
+    def run(heads):
         if wl.topk:
-            ref = oracle.vsa_reference(qs, ks, vs, wl.dit_seq_shape, wl.block_size, wl.topk)
-            rp, ci, plan = ref["row_ptr"], ref["col_idx"], ref["plan"]
-        else:
-            plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
-            rp_all, ci_all, _ = make_tile64_map(wl)
-            nb = plan.num_blocks
-            rp = rp_all[h * nb:(h + 1) * nb + 1] - rp_all[h * nb]
-            ci = ci_all[rp_all[h * nb]:rp_all[(h + 1) * nb]]
-            oracle.block_sparse_attention(qs, ks, vs, plan, rp, ci)
-        t_total += time.perf_counter() - t0
-        flops += oracle.valid_flops(plan, rp, ci, wl.head_dim)
-        heads_done += 1
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{heads_done} of {wl.heads} heads of the same layer, whole hot path "
-                      f"(pool, score, top-k, attention) in float64 numpy; {t_total:.1f} s; "
-                      f"nproc={os.cpu_count()}"}
+            ref = oracle.vsa_reference_f32(q, k, v, wl.dit_seq_shape, wl.block_size, wl.topk,
+                                           heads=heads)
+            return ref["row_ptr"], ref["col_idx"]
+        rp, ci, _ = make_tile64_map(wl)
+        oracle.block_sparse_attention_f32(q, k, v, plan, rp, ci, heads=heads)
+        return rp, ci
+
+    t0 = time.perf_counter()
+    run([0])
+    t_head = time.perf_counter() - t0
+    n = wl.heads if t_head * wl.heads <= budget_s else max(1, int(budget_s / t_head))
+    t0 = time.perf_counter()
+    rp, ci = run(list(range(n)))
+    t = time.perf_counter() - t0
+    nb = plan.num_blocks
+    rows = n * nb   # batch 1: the first n heads' rows
+    rp = np.asarray(rp, np.int64)
+    flops = oracle.valid_flops(plan, rp[:rows + 1], np.asarray(ci, np.int64)[:rp[rows]],
+                               wl.head_dim)
+    s_layer = t * wl.heads / n
+    return {"value": round(flops / t / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "s_per_layer": round(s_layer, 2),
+            "sample": (f"float32 torch-CPU oracle, whole path (pool, score, top-k, block-loop "
+                       f"attention), {'the whole layer' if n == wl.heads else f'{n} of {wl.heads} heads, layer time extrapolated'}"
+                       f" ({wl.name}), {t:.1f} s after a one-head warm-up; {threads} threads"),
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+
+
+def map_check(wl, q, k, col_host):
+    """The step's block ids against the float64 oracle's selection: rows equal
+    bit for bit outside near-ties (k-th vs (k+1)-th score gap < 1e-3), and
+    the number of near-tie rows excluded from that check."""
+    import oracle
+    plan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, wl.topk)
+    q64, k64 = (x.to(torch.float64).numpy() for x in (q, k))
+    sc = oracle.block_scores(oracle.pool_blocks(q64, plan), oracle.pool_blocks(k64, plan))
+    sel, margin = oracle.select_topk(sc, wl.topk)
+    got = col_host.reshape(sel.shape)
+    exact = margin >= 1e-3
+    same = np.all(got == sel, axis=-1)
+    return {"rows": int(exact.size), "bit_exact": int((same & exact).sum()),
+            "near_tie_excluded": int((~exact).sum()),
+            "mismatch_outside_near_ties": int((~same & exact).sum())}
 
 
 def bench_backward(args, wl, plan, elem, dq, dk, dv):
@@ -364,7 +476,7 @@ def main():
                     help="gather-free path: pool Q and K from the raster tensors, score/top-k, "
                          "raster attention writing the raster output (no gather or scatter)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--traffic-json", default=None,
                     help="PMC traffic record of the attention kernel (default: the one in "
                          "profiles/ for the blocked or, with --fused, the raster kernel)")
@@ -534,6 +646,8 @@ def main():
     value = f_valid / (ms_per_step * 1e-3) / 1e12
     traffic = recorded_traffic(args.traffic_json, wl.name, args.dtype,
                                "raster" if args.fused else "blocked")
+    log("[bench] measuring the MFMA loop and the copy bandwidth")
+    den = measure_denominators(dev)
     result = {
         "metric": "effective TFLOP/s (selected blocks) + ms/layer, 27280 tok, topk=64, 1 GPU",
         "value": round(value, 3),
@@ -558,14 +672,23 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": MFMA_16BIT_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / MFMA_16BIT_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     "peak_measured": den["mfma_bf16_tflops"],
+                     "frac_measured": round(attn_tflops / den["mfma_bf16_tflops"], 4),
+                     "clock_ghz": den["mfma_clock_ghz"],
+                     "kernel": "attn_fwd_kernel (balanced launch)" if not args.fixed_order
+                               else "attn_fwd_kernel (fixed order)"},
+        "measured_denominators": den,
         "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in stage_ms.items()},
         "flops_valid": f_valid,
         "flops_nominal": f_nominal,
         "attention_tflops_nominal": round(f_nominal / (t_attn * 1e-3) / 1e12, 2),
     }
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
+        if wl.topk:
+            log("[bench] checking the block ids against the float64 oracle")
+            result["map_check"] = map_check(wl, q, k, col_host)
+        log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
