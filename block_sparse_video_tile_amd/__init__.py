@@ -27,6 +27,7 @@ __all__ = [
     "vsa_forward_fused_workspace_size", "vsa_forward_fused", "vsa_attn_fwd_workspace_size",
     "vsa_block_sparse_attn_fwd_ws", "vsa_block_sparse_attn_fwd_raster_ws", "vsa_status_string",
     "vsa_last_error", "vsa_bench_mfma_peak", "vsa_bench_hbm_copy",
+    "vsa_block_sparse_attn_fwd_noalloc",
 ]
 
 VSA_OK, VSA_ERR_INVALID_ARGUMENT, VSA_ERR_UNSUPPORTED, VSA_ERR_HIP = 0, 1, 2, 3
@@ -93,6 +94,8 @@ _SIGS = {
     "vsa_block_sparse_attn_fwd_raster_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                              ctypes.c_int64, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                              _P], ctypes.c_int),
+    "vsa_block_sparse_attn_fwd_noalloc": ([_P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
+                                           _P, _P, _P], ctypes.c_int),
     "vsa_bench_mfma_peak": ([ctypes.c_int32, ctypes.c_int32, _P, ctypes.POINTER(ctypes.c_int64),
                              _P], ctypes.c_int),
     "vsa_bench_hbm_copy": ([_P, _P, ctypes.c_int64, _P], ctypes.c_int),
@@ -385,6 +388,22 @@ def vsa_block_sparse_attn_fwd_ws(plan: Plan, q_blk, k_blk, v_blk, row_ptr, col_i
         _ptr(o_blk, be, et, "o_blk"),
         _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
         ws_ptr, ws_len, _stream(stream, q_blk, o_blk)))
+
+
+def vsa_block_sparse_attn_fwd_noalloc(plan: Plan, q_blk, k_blk, v_blk, row_ptr, col_idx,
+                                      uniform_k: int, nnz: int, o_blk, lse=None, stream=None):
+    """The balanced launch with its row queues in the library's static device
+    scratch (no workspace, no allocation); calls on one GPU must not overlap."""
+    be = plan.info["blocked_elems"]
+    rows = plan.num_rows()
+    et = plan.torch_dtype()
+    _check(load_library().vsa_block_sparse_attn_fwd_noalloc(
+        plan.handle, _ptr(q_blk, be, et, "q_blk"), _ptr(k_blk, be, et, "k_blk"),
+        _ptr(v_blk, be, et, "v_blk"), _ptr(row_ptr, rows + 1, _i32(), "row_ptr"),
+        _ptr(col_idx, int(nnz), _i32(), "col_idx"), int(uniform_k), int(nnz),
+        _ptr(o_blk, be, et, "o_blk"),
+        _ptr(lse, plan.batch * plan.heads * plan.padded_len, _f32(), "lse"),
+        _stream(stream, q_blk, o_blk)))
 
 
 def vsa_block_sparse_attn_fwd_raster_ws(plan: Plan, q, k, v, row_ptr, col_idx, uniform_k: int,

@@ -77,10 +77,18 @@
 // to -inf.  A row without blocks leaves l = 0 and writes O = 0, LSE = -inf.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
 #include "vsa_internal.h"
+
+// Device scratch of vsa_block_sparse_attn_fwd_noalloc: the row-queue counters
+// of the balanced launch, in a fixed library-owned array (one copy per GPU,
+// held until the process ends) for callers that cannot allocate.  In host
+// code this name only stands for the symbol; kernels receive the device
+// address that vsa::noalloc_scratch looks up per device.
+static __device__ __align__(256) unsigned char scratch[vsa::kNoAllocScratchBytes];
 
 namespace vsa {
 namespace {
@@ -929,6 +937,27 @@ hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void
 }
 
 }  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  // Each device holds its own copy of `scratch` at its own address: look it
+  // up once per device, with that device current, and keep it.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,

@@ -447,6 +447,24 @@ vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t p, const void* q, const void*
                     fn);
 }
 
+vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const void* k,
+                                             const void* v, const int32_t* row_ptr,
+                                             const int32_t* col, int32_t uniform_k, int64_t nnz,
+                                             void* o, float* lse, void* stream) {
+  static const char* fn = "vsa_block_sparse_attn_fwd_noalloc";
+  if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
+  if (vsa_status st = check_lse(fn, lse)) return st;
+  // The scratch holds the 9 row-queue counters of the balanced launch; they
+  // are 32-bit and every plan's row count (at most 2^30) fits them.
+  static_assert(vsa::kAttnQueueBytes <= vsa::kNoAllocScratchBytes, "row queues exceed scratch");
+  void* ws = nullptr;
+  if (hipError_t e = vsa::noalloc_scratch(&ws); e != hipSuccess)
+    return hip_status(e, "vsa_block_sparse_attn_fwd_noalloc: scratch address");
+  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                         static_cast<unsigned int*>(ws), hipStream_t(stream)),
+                    fn);
+}
+
 vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const void* k,
                                             const void* v, const int32_t* row_ptr,
                                             const int32_t* col, int32_t uniform_k, int64_t nnz,

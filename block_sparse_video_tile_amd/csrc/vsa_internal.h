@@ -91,6 +91,10 @@ hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, unsigned int* queues,
                            hipStream_t s);
+// Fixed device scratch of the no-allocation attention entry point (the row
+// queues), and its device address on the current device.
+constexpr size_t kNoAllocScratchBytes = kAttnQueueBytes;
+hipError_t noalloc_scratch(void** ptr);
 // Raster [B,S,NH,D] q, k, v and o; gate (raster) and oc (fp32 [B,NH,nb,D])
 // optional: o = attention + gate * oc[block].
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,

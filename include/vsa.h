@@ -282,6 +282,23 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t plan, const void* q, c
                                                const float* o_coarse, void* o_raster, float* lse,
                                                void* ws, size_t ws_bytes, void* stream);
 
+/* vsa_block_sparse_attn_fwd_ws without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The row-queue counters live in a
+ * library-owned static device array of 256 bytes per GPU, which stays
+ * allocated until the process ends; the call itself allocates nothing and
+ * clears the counters with a small kernel on `stream` (no memset).  Every
+ * call on a GPU shares that GPU's array: calls that may overlap on one GPU
+ * (other streams or threads without ordering between them) race and must be
+ * serialised by the caller.  Arguments, outputs and errors as
+ * vsa_block_sparse_attn_fwd_ws (minus the workspace), plus HIP if the
+ * scratch address cannot be looked up on the current device. */
+vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t plan, const void* q_blk,
+                                             const void* k_blk, const void* v_blk,
+                                             const int32_t* row_ptr, const int32_t* col_idx,
+                                             int32_t uniform_k, int64_t nnz, void* o_blk,
+                                             float* lse, void* stream);
+
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
  * rowsum(dO*O) [B,NH,Npad] fp32, d-major copies of K, Q and dO, and the
  * transposed block map (B*NH*nb*nb + B*NH*nb int32) and the row-queue

@@ -353,3 +353,19 @@ def test_measurement_kernel_checks():
     assert _raw(g, FAKE, FAKE, 40, None) == bad
     assert _raw(g, FAKE + 8, FAKE, 64, None) == bad
     assert "16-byte" in vsa.vsa_last_error()
+
+
+def test_noalloc_attention_checks(plan):
+    """The no-allocation balanced launch: the argument checks of the workspace
+    entry point, before any device call (no workspace argument to check)."""
+    h = plan.handle
+    bad = vsa.VSA_ERR_INVALID_ARGUMENT
+    f = "vsa_block_sparse_attn_fwd_noalloc"
+    # (plan, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, stream)
+    rows = plan.num_rows()
+    assert _raw(f, h, None, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 9, rows * 9, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4 - 1, FAKE, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE + 8, None, None) == bad
+    assert _raw(f, h, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, FAKE + 2, None) == bad
+    assert _raw(f, None, FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None, None) == bad
