@@ -11,12 +11,17 @@
 //   One workgroup per CSR row r = (b*NH + h)*nb + i, i.e. one query block of
 //   V = 32*NW tokens; wave w owns query rows 32w .. 32w+31 (in an 8-wave
 //   block cut by the grid edge to 5 or 6 row groups, waves 4..7 instead share
-//   the last groups by key halves: see the key-half waves below).  Row ids are
+//   the last groups by key halves: see the key-half waves below; a 64-token
+//   block runs 4 waves, two per query group, each group's keys split between
+//   them the same way, so that two workgroups of a CU put two waves on every
+//   SIMD).  Row ids are
 //   remapped so that each of the 8 XCDs (workgroups are dispatched to XCDs
 //   round-robin) works through a contiguous range of rows, i.e. the same
 //   heads, and its L2 serves their shared key/value blocks.  In the balanced
 //   launch the same ranges are queues from which the workgroups claim their
-//   rows at run time (claim_row), so XCDs that run faster take more rows.
+//   rows at run time (claim_row), so XCDs that run faster take more rows;
+//   for a caller's block map the rows of each queue are first sorted longest
+//   first (order_rows_kernel), so that long rows do not start last.
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
 //   loaded).  The workgroup first flattens its CSR entries into a list of
@@ -184,13 +189,16 @@ __device__ inline float tile_max(const f32x16 (&st)[2]) {
 // RASTER = false: q, k, o blocked [B,NH,Npad,D], v blocked-V^T.
 // RASTER = true: q, k, v, o raster [B,S,NH,D]; with `gate` (raster) the
 // output is O + gate * oc[block] (oc fp32 [B,NH,nb,D]), as the gated scatter.
-template <int NW, bool F16, bool RASTER>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
+// NQ: query row groups of 32 per block (block volume 32*NQ); NW: waves, NQ,
+// or 2*NQ for 64-token blocks whose two groups are each split by key halves.
+template <int NW, int NQ, bool F16, bool RASTER>
+__global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
     int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, const uint4* __restrict__ gate,
-    const float* __restrict__ oc, unsigned int* __restrict__ queues, VsaGeom g, float scale_log2,
-    float scale) {
+    const float* __restrict__ oc, unsigned int* __restrict__ queues,
+    const int32_t* __restrict__ order, VsaGeom g, float scale_log2, float scale) {
+  static_assert(NW == NQ || (NQ == 2 && NW == 4), "waves: one per query group, or 4 for 2 groups");
   static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits), "O staging must fit in LDS");
   const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
   // Sub-tile buffers.  K runs one sub-tile ahead of V: while sub-tile n is
@@ -205,26 +213,26 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // sub-tile descriptor list of the current pass over the row, and the
   // per-entry scan that places each entry's descriptors
   constexpr int kThreads = NW * 64;
-  // Two 2-wave workgroups share a CU only if each holds at most half of its
-  // 160 KB of LDS; their list passes are shorter to leave room for the
-  // raster slot table.
-  constexpr int kList = NW == 2 ? 768 : kListEntries;
-  constexpr int kListTiles = kList * (32 * NW / kKvChunk);
+  // Two workgroups of 64-token blocks share a CU only if each holds at most
+  // half of its 160 KB of LDS; their list passes are shorter to leave room
+  // for the raster slot table.
+  constexpr int kList = NQ == 2 ? 768 : kListEntries;
+  constexpr int kListTiles = kList * (32 * NQ / kKvChunk);
   __shared__ int tlist[kListTiles];
   __shared__ int escan[kList];
   __shared__ int ntiles_sh;
-  constexpr int kVol = 32 * NW;
+  constexpr int kVol = 32 * NQ;
   __shared__ uint32_t soff[RASTER ? 8 * kVol : 1];
-  static_assert(NW != 2 || 16 * 2 * (kKUnits + kVUnits) + 4 * (kListTiles + kList) +
+  static_assert(NQ != 2 || 16 * 2 * (kKUnits + kVUnits) + 4 * (kListTiles + kList) +
                                4 * (RASTER ? 8 * kVol : 1) + 64 <= 160 * 1024 / 2,
-                "two 2-wave workgroups must fit in one CU's LDS");
+                "two workgroups of 64-token blocks must fit in one CU's LDS");
 
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   // The row: fixed by the workgroup index (XCD-aware order), or, with
   // `queues`, claimed at start-up (claim_row); a workgroup that finds every
   // row taken leaves at once (workgroup-uniform, before any other barrier).
   __shared__ int64_t row_sh;
-  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh)
+  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh, order)
                                       : xcd_remap(blockIdx.x, nrows);
   if (r < 0) return;
   const int i = int(r % g.nb);
@@ -243,10 +251,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   // online softmax, and the pairs merge before the epilogue.  Waves w and w+4
   // run on the same SIMD, so each SIMD then carries 1.5 waves of matrix work
   // instead of 2 on two SIMDs and 1 on the others.
+  // With 4 waves on a 64-token block (NW = 2*NQ) every group is split:
+  // waves 0 and 2 take group 0, waves 1 and 3 group 1, waves 0 and 1 keys
+  // 0..31 and waves 2 and 3 keys 32..63.
   const int ngroups = (cq + 31) / 32;
-  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
-  const int qgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
-  const int khalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all 64 keys
+  constexpr bool kAllSplit = NW == 2 * NQ;
+  const bool split = kAllSplit || (NW == 8 && (ngroups == 5 || ngroups == 6));  // wg-uniform
+  const int qgroup = kAllSplit ? wave % NQ : (split && wave >= 4 ? 4 + (wave & 1) : wave);
+  const int khalf = kAllSplit ? wave / NQ
+                              : (split && wave >= 4 ? (wave >> 1) & 1 : -1);  // -1: all 64 keys
   const int qrow = qgroup * 32 + l32;    // this lane's query row inside the block
   const bool active = qgroup * 32 < cq;  // wave-uniform
 
@@ -773,18 +786,28 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
     }
   }
   };
-  if (khalf >= 0) passes(std::true_type());
-  else passes(std::false_type());
+  if constexpr (kAllSplit) {
+    passes(std::true_type());
+  } else {
+    if (khalf >= 0) passes(std::true_type());
+    else passes(std::false_type());
+  }
 
   // ---- key-half pairs: the second wave of a pair hands its (m, l, O^T) to
-  // the first through LDS (wave 6's in vbuf1, wave 7's in tlist + escan,
-  // none of which the epilogue's staging uses), which merges them:
+  // the first through LDS (8 waves: wave 6's in vbuf1, wave 7's in tlist +
+  // escan; 4 waves: wave 2's in vbuf1, wave 3's in vbuf0; none of which the
+  // epilogue's staging uses), which merges them:
   // m = max(m_a, m_b), O = O_a 2^((m_a - m)c) + O_b 2^((m_b - m)c), l likewise.
-  const bool own_pad = split && khalf == 1;  // waves 6, 7: their own rows are padding
+  // waves 6, 7 of a split 8-wave block: their own rows are padding (zeroed);
+  // waves 2, 3 of a 64-token block own no rows of it
+  const bool own_pad = split && khalf == 1;
+  const bool owns_rows = wave * 32 < kVol;
   if (split) {
     float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(vbuf1)
-                                        : reinterpret_cast<float*>(tlist);
-    float* const part_ml = (wave & 1) == 0 ? part + 64 * 64 : reinterpret_cast<float*>(escan);
+                                        : (kAllSplit ? reinterpret_cast<float*>(vbuf0)
+                                                     : reinterpret_cast<float*>(tlist));
+    float* const part_ml = (wave & 1) == 0 || kAllSplit ? part + 64 * 64
+                                                        : reinterpret_cast<float*>(escan);
     if (own_pad && active) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -874,7 +897,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         o[at] = val;
       }
     }
-  } else {
+  } else if (owns_rows) {
     uint4* const odst = o + (qk_row0 + wave * 32) * 16;
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
@@ -883,34 +906,97 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
           own_pad ? make_uint4(0u, 0u, 0u, 0u) : srows[rr * kORow + (lane & 15)];
     }
   }
-  if (lse != nullptr && half == 0) {
+  if (lse != nullptr && half == 0 && owns_rows) {
     lse[qk_row0 + (own_pad ? wave * 32 + l32 : qrow)] =
         (row_valid && l_run > 0.f) ? m_run * scale + __logf(l_run) : -INFINITY;
   }
 }
 
-template <int NW, bool F16, bool RASTER>
+// Rows of each of the 8 queue ranges of the balanced launch, longest first,
+// for block maps whose rows differ in length: four classes by the row's
+// entry count against the range's mean (>= 4x, >= 2x, >= 1x, shorter), each
+// class in ascending row order.  order[start .. start + count) of range x is
+// a permutation of those rows; claim_row hands positions out in that order,
+// so a range's long rows start first instead of whenever their position
+// comes up.  One workgroup per range; offsets are sanitised as the
+// attention kernel sanitises them.
+__global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ row_ptr,
+                                                          int64_t nnz, int64_t nrows,
+                                                          int32_t* __restrict__ order) {
+  __shared__ long long wsum[16];
+  __shared__ int wcnt[16];
+  const uint32_t n = uint32_t(nrows), per = n / 8, rem = n % 8, x = blockIdx.x;
+  const uint32_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  const uint32_t count = per + (x < rem ? 1u : 0u);
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  auto len = [&](uint32_t r) -> int64_t {
+    const int64_t beg = min(max(int64_t(row_ptr[r]), int64_t(0)), nnz);
+    const int64_t end = min(max(int64_t(row_ptr[r + 1]), beg), nnz);
+    return end - beg;
+  };
+  // total entries of the range
+  long long part = 0;
+  for (uint32_t t = tid; t < count; t += 1024) part += len(start + t);
+  for (int d = 32; d > 0; d /= 2) part += __shfl_xor(part, d);
+  if (lane == 0) wsum[wave] = part;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) total += wsum[w];
+  // class of a row: len*count compared with k*total (integer arithmetic)
+  auto cls = [&](int64_t l) {
+    const long long lc = (long long)l * (long long)count;
+    return lc >= 4 * total ? 0 : lc >= 2 * total ? 1 : lc >= total ? 2 : 3;
+  };
+  uint32_t base = 0;
+  for (int c = 0; c < 4; ++c) {
+    for (uint32_t chunk = 0; chunk < count; chunk += 1024) {
+      const uint32_t t = chunk + tid;
+      const bool flag = t < count && cls(len(start + t)) == c;
+      const unsigned long long b = __ballot(flag);
+      const int before = __popcll(b & ((1ull << lane) - 1ull));
+      __syncthreads();   // wcnt of the previous chunk has been read by everyone
+      if (lane == 0) wcnt[wave] = __popcll(b);
+      __syncthreads();
+      int woff = 0, ctot = 0;
+      for (int w = 0; w < 16; ++w) {
+        woff += w < wave ? wcnt[w] : 0;
+        ctot += wcnt[w];
+      }
+      if (flag) order[start + base + woff + before] = int32_t(start + t);
+      base += ctot;
+    }
+  }
+}
+
+template <int NW, int NQ, bool F16, bool RASTER>
 hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
                      void* o, float* lse, const void* gate, const float* oc,
-                     unsigned int* queues, hipStream_t s) {
+                     unsigned int* queues, int32_t* order, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * 1.4426950408889634f;
   int64_t grid = rows;
+  const int32_t* claim_order = nullptr;
   if (queues != nullptr) {
     // a quarter more workgroups than rows, so that each XCD can take up to
     // 1.25 times its share; the counters are cleared first on the same stream
     grid = rows + std::max<int64_t>(8, rows / 4);
     hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, queues);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (row_ptr != nullptr && order != nullptr) {
+      hipLaunchKernelGGL(order_rows_kernel, dim3(8), dim3(1024), 0, s, row_ptr, nnz, rows, order);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      claim_order = order;
+    }
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<NW, F16, RASTER>), dim3(unsigned(grid)), dim3(NW * 64), 0,
-                     s, static_cast<const uint4*>(q), static_cast<const uint4*>(k),
+  hipLaunchKernelGGL((attn_fwd_kernel<NW, NQ, F16, RASTER>), dim3(unsigned(grid)), dim3(NW * 64),
+                     0, s, static_cast<const uint4*>(q), static_cast<const uint4*>(k),
                      static_cast<const uint4*>(v), row_ptr, col, uniform_k, nnz,
-                     static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, queues, g,
-                     scale_log2, scale);
+                     static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, queues,
+                     claim_order, g, scale_log2, scale);
   return hipGetLastError();
 }
 
@@ -918,20 +1004,21 @@ template <bool RASTER>
 hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void* v,
                       const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
                       void* o, float* lse, const void* gate, const float* oc,
-                      unsigned int* queues, hipStream_t s) {
-  auto launch = [&](auto nw) {
-    constexpr int NW = decltype(nw)::value;
+                      unsigned int* queues, int32_t* order, hipStream_t s) {
+  auto launch = [&](auto nw, auto nq) {
+    constexpr int NW = decltype(nw)::value, NQ = decltype(nq)::value;
     return g.dtype == VSA_DTYPE_FP16
-               ? launch_nw<NW, true, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                             gate, oc, queues, s)
-               : launch_nw<NW, false, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                              gate, oc, queues, s);
+               ? launch_nw<NW, NQ, true, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o,
+                                                 lse, gate, oc, queues, order, s)
+               : launch_nw<NW, NQ, false, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o,
+                                                  lse, gate, oc, queues, order, s);
   };
+  using std::integral_constant;
   switch (g.vol / 32) {
-    case 2: return launch(std::integral_constant<int, 2>());
-    case 4: return launch(std::integral_constant<int, 4>());
-    case 6: return launch(std::integral_constant<int, 6>());
-    case 8: return launch(std::integral_constant<int, 8>());
+    case 2: return launch(integral_constant<int, 4>(), integral_constant<int, 2>());
+    case 4: return launch(integral_constant<int, 4>(), integral_constant<int, 4>());
+    case 6: return launch(integral_constant<int, 6>(), integral_constant<int, 6>());
+    case 8: return launch(integral_constant<int, 8>(), integral_constant<int, 8>());
     default: return hipErrorInvalidValue;
   }
 }
@@ -962,16 +1049,18 @@ hipError_t noalloc_scratch(void** ptr) {
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, unsigned int* queues,
-                           hipStream_t s) {
+                           int32_t* order, hipStream_t s) {
   return launch_any<false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, nullptr, nullptr,
-                           queues, s);
+                           queues, order, s);
 }
 
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
                                   const int32_t* row_ptr, const int32_t* col, int uniform_k,
                                   int64_t nnz, void* o, float* lse, const void* gate,
-                                  const float* oc, unsigned int* queues, hipStream_t s) {
-  return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, queues, s);
+                                  const float* oc, unsigned int* queues, int32_t* order,
+                                  hipStream_t s) {
+  return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, queues,
+                          order, s);
 }
 
 }  // namespace vsa

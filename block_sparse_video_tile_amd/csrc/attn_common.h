@@ -108,9 +108,11 @@ __device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
 // rows.  A ticket holder always finds a row: a queue it finds empty stays
 // empty, and if all 8 were empty every row would already be held by one of
 // the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
-// reaches the workgroup through LDS.
+// reaches the workgroup through LDS.  With `order` (block maps of their own
+// row lengths), position p of the queues is row order[p] instead of the
+// cost order above: the rows of each queue range sorted longest first.
 __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const VsaGeom& g,
-                                    int64_t* row_sh) {
+                                    int64_t* row_sh, const int32_t* order = nullptr) {
   if (threadIdx.x == 0) {
     int64_t row = -1;
     // rows number at most 2^30 (the plan's limit): 32-bit arithmetic
@@ -126,7 +128,14 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const V
         if (t < count) {
           const uint32_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
           const uint32_t nb = uint32_t(g.nb);
-          row = int64_t(pos / nb) * nb + block_in_cost_order(g, int(pos % nb));
+          if (order != nullptr) {
+            // a permutation of the rows; anything else leaves the row undone
+            // rather than addressing memory outside the tensors
+            const int32_t o = order[pos];
+            row = (o >= 0 && uint32_t(o) < n) ? int64_t(o) : -1;
+          } else {
+            row = int64_t(pos / nb) * nb + block_in_cost_order(g, int(pos % nb));
+          }
           break;
         }
       }

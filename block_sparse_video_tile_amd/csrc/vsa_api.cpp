@@ -401,12 +401,17 @@ vsa_status check_raster_args(const char* fn, vsa_plan_t p, const void* gate, con
   return ok();
 }
 
-// The row-queue counters of the balanced attention launch.
-vsa_status check_queue_workspace(const char* fn, void* ws, size_t ws_bytes) {
+// Workspace of the balanced attention launches: the row-queue counters, then
+// one int32 per row for the longest-first order of a block map.
+size_t attn_ws_bytes(const VsaGeom& g) {
+  return vsa::kAttnQueueBytes + align256(size_t(g.batch) * g.heads * g.nb * 4);
+}
+
+vsa_status check_queue_workspace(const char* fn, vsa_plan_t p, void* ws, size_t ws_bytes) {
   if (!ws) return fail(VSA_ERR_INVALID_ARGUMENT, "%s: null workspace", fn);
-  if (ws_bytes < vsa::kAttnQueueBytes)
+  if (ws_bytes < attn_ws_bytes(p->g))
     return fail(VSA_ERR_INVALID_ARGUMENT, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes,
-                vsa::kAttnQueueBytes);
+                attn_ws_bytes(p->g));
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
     return fail(VSA_ERR_INVALID_ARGUMENT, "%s: workspace not 256-byte aligned", fn);
   return ok();
@@ -424,13 +429,13 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k,
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                         nullptr, hipStream_t(stream)),
+                                         nullptr, nullptr, hipStream_t(stream)),
                     fn);
 }
 
 vsa_status vsa_attn_fwd_workspace_size(vsa_plan_t p, size_t* bytes) {
   if (!p || !bytes) return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_attn_fwd_workspace_size: null");
-  *bytes = vsa::kAttnQueueBytes;
+  *bytes = attn_ws_bytes(p->g);
   return ok();
 }
 
@@ -441,10 +446,13 @@ vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t p, const void* q, const void*
   static const char* fn = "vsa_block_sparse_attn_fwd_ws";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
-  if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
-  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                         static_cast<unsigned int*>(ws), hipStream_t(stream)),
-                    fn);
+  if (vsa_status st = check_queue_workspace(fn, p, ws, ws_bytes)) return st;
+  return hip_status(
+      vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                           static_cast<unsigned int*>(ws),
+                           reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
+                           hipStream_t(stream)),
+      fn);
 }
 
 vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const void* k,
@@ -454,15 +462,24 @@ vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const 
   static const char* fn = "vsa_block_sparse_attn_fwd_noalloc";
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
-  // The scratch holds the 9 row-queue counters of the balanced launch; they
-  // are 32-bit and every plan's row count (at most 2^30) fits them.
-  static_assert(vsa::kAttnQueueBytes <= vsa::kNoAllocScratchBytes, "row queues exceed scratch");
+  // The scratch holds the 9 row-queue counters of the balanced launch (32-bit:
+  // every plan's row count, at most 2^30, fits them) and, for a block map,
+  // the longest-first order of at most kNoAllocMaxMapRows rows.
+  const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
+  if (row_ptr != nullptr && rows > vsa::kNoAllocMaxMapRows)
+    return fail(VSA_ERR_UNSUPPORTED,
+                "%s: a block map of %lld rows exceeds the %lld rows of the fixed scratch "
+                "(use vsa_block_sparse_attn_fwd_ws with a workspace)",
+                fn, (long long)rows, (long long)vsa::kNoAllocMaxMapRows);
   void* ws = nullptr;
   if (hipError_t e = vsa::noalloc_scratch(&ws); e != hipSuccess)
     return hip_status(e, "vsa_block_sparse_attn_fwd_noalloc: scratch address");
-  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                         static_cast<unsigned int*>(ws), hipStream_t(stream)),
-                    fn);
+  return hip_status(
+      vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                           static_cast<unsigned int*>(ws),
+                           reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
+                           hipStream_t(stream)),
+      fn);
 }
 
 vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const void* k,
@@ -475,7 +492,8 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const v
   if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
-                                                lse, gate, oc, nullptr, hipStream_t(stream)),
+                                                lse, gate, oc, nullptr, nullptr,
+                                                hipStream_t(stream)),
                     fn);
 }
 
@@ -489,11 +507,14 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t p, const void* q, cons
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
-  if (vsa_status st = check_queue_workspace(fn, ws, ws_bytes)) return st;
-  return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
-                                                lse, gate, oc, static_cast<unsigned int*>(ws),
-                                                hipStream_t(stream)),
-                    fn);
+  if (vsa_status st = check_queue_workspace(fn, p, ws, ws_bytes)) return st;
+  return hip_status(
+      vsa::launch_attn_fwd_raster(
+          p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc,
+          static_cast<unsigned int*>(ws),
+          reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
+          hipStream_t(stream)),
+      fn);
 }
 
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t p, size_t* bytes) {
@@ -600,7 +621,8 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
   if ((e = vsa::launch_score_topk(g, qp, kp, p->topk, col, nullptr, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: score/top-k");
   unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
-  if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, queues, s)) !=
+  if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, queues,
+                                nullptr, s)) !=
       hipSuccess)
     return hip_status(e, "vsa_forward: attention");
   if (gate && (e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
@@ -663,7 +685,7 @@ vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const v
   }
   unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
   if ((e = vsa::launch_attn_fwd_raster(g, q, k, v, nullptr, col, p->topk, nnz, out, lse, gate,
-                                       gate ? oc : nullptr, queues, s)) != hipSuccess)
+                                       gate ? oc : nullptr, queues, nullptr, s)) != hipSuccess)
     return hip_status(e, "vsa_forward_fused: attention");
   return ok();
 }

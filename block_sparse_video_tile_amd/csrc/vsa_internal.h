@@ -85,22 +85,27 @@ hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp,
                              int32_t* col, float* scores, hipStream_t s);
 // queues == nullptr: one workgroup per row in a fixed order; otherwise 9
 // device counters (kAttnQueueBytes of workspace) from which the workgroups
-// of a larger launch claim their rows.
+// of a larger launch claim their rows.  order: with queues and a block map
+// (row_ptr), an int32 buffer of one entry per row that receives the rows of
+// each queue sorted longest first (nullptr: claims in plain order).
 constexpr size_t kAttnQueueBytes = 256;
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, unsigned int* queues,
-                           hipStream_t s);
-// Fixed device scratch of the no-allocation attention entry point (the row
-// queues), and its device address on the current device.
-constexpr size_t kNoAllocScratchBytes = kAttnQueueBytes;
+                           int32_t* order, hipStream_t s);
+// Fixed device scratch of the no-allocation attention entry point: the row
+// queues, then the longest-first row order of a block map of at most
+// kNoAllocMaxMapRows rows; and its device address on the current device.
+constexpr int64_t kNoAllocMaxMapRows = int64_t(1) << 16;
+constexpr size_t kNoAllocScratchBytes = kAttnQueueBytes + size_t(kNoAllocMaxMapRows) * 4;
 hipError_t noalloc_scratch(void** ptr);
 // Raster [B,S,NH,D] q, k, v and o; gate (raster) and oc (fp32 [B,NH,nb,D])
 // optional: o = attention + gate * oc[block].
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
                                   const int32_t* row_ptr, const int32_t* col, int uniform_k,
                                   int64_t nnz, void* o, float* lse, const void* gate,
-                                  const float* oc, unsigned int* queues, hipStream_t s);
+                                  const float* oc, unsigned int* queues, int32_t* order,
+                                  hipStream_t s);
 
 // Measurement kernels (microbench.hip): `timing` holds 4 uint64 per wave.
 hipError_t launch_mfma_peak(int num_workgroups, int iters, uint64_t* timing, hipStream_t s);

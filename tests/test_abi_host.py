@@ -252,12 +252,14 @@ def test_balanced_attention_workspace_checks(plan):
     h = plan.handle
     bad = vsa.VSA_ERR_INVALID_ARGUMENT
     need = vsa.vsa_attn_fwd_workspace_size(plan)
-    assert need == 256
+    # 9 row-queue counters (256 bytes), then one int32 per row for the
+    # longest-first order of a block map, 256-byte aligned
+    rows = plan.num_rows()
+    assert need == 256 + (rows * 4 + 255) // 256 * 256
     big = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), batch=1, num_heads=24, topk=64)
-    assert vsa.vsa_attn_fwd_workspace_size(big) == need
+    assert vsa.vsa_attn_fwd_workspace_size(big) == 256 + 2880 * 4   # 11520 = 45 * 256
     f = "vsa_block_sparse_attn_fwd_ws"
     # (plan, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, ws, ws_bytes, stream)
-    rows = plan.num_rows()
     ok_args = (FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None)
     assert _raw(f, h, *ok_args, None, need, None) == bad
     assert "null workspace" in vsa.vsa_last_error()
@@ -272,7 +274,7 @@ def test_balanced_attention_workspace_checks(plan):
     # (plan, q, k, v, row_ptr, col, uniform_k, nnz, gate, o_coarse, o, lse, ws, ws_bytes, stream)
     r_args = (FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4)
     assert _raw(g, h, *r_args, None, None, FAKE, None, None, need, None) == bad
-    assert _raw(g, h, *r_args, None, None, FAKE, None, FAKE, need - 256, None) == bad
+    assert _raw(g, h, *r_args, None, None, FAKE, None, FAKE, need - 4, None) == bad
     assert _raw(g, h, *r_args, FAKE, None, FAKE, None, FAKE, need, None) == bad
     assert "gate and o_coarse" in vsa.vsa_last_error()
     # the layer entry points carry the queues in their own workspaces
@@ -353,6 +355,20 @@ def test_measurement_kernel_checks():
     assert _raw(g, FAKE, FAKE, 40, None) == bad
     assert _raw(g, FAKE + 8, FAKE, 64, None) == bad
     assert "16-byte" in vsa.vsa_last_error()
+
+
+def test_noalloc_attention_map_rows_limit():
+    """The fixed scratch holds the longest-first order of at most 2^16 rows of
+    a block map: a larger map-mode plan is UNSUPPORTED (uniform rows need no
+    order and have no such limit)."""
+    bad = vsa.VSA_ERR_UNSUPPORTED
+    f = "vsa_block_sparse_attn_fwd_noalloc"
+    big = vsa.vsa_plan(33280, (1, 1, 33280), (1, 1, 64), batch=1, num_heads=127, topk=0)
+    assert big.num_rows() == 127 * 520 > 65536
+    assert _raw(f, big.handle, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 10, FAKE, None, None) == bad
+    assert "65536" in vsa.vsa_last_error()
+    ok = vsa.vsa_plan(33280, (1, 1, 33280), (1, 1, 64), batch=1, num_heads=126, topk=0)
+    assert ok.num_rows() == 65520 <= 65536
 
 
 def test_noalloc_attention_checks(plan):
