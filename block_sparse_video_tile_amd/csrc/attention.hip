@@ -21,7 +21,10 @@
 //   launch the same ranges are queues from which the workgroups claim their
 //   rows at run time (claim_row), so XCDs that run faster take more rows;
 //   for a caller's block map the rows of each queue are first sorted longest
-//   first (order_rows_kernel), so that long rows do not start last.
+//   first (order_rows_kernel), so that long rows do not start last; for a
+//   layer whose heads' key/value blocks outgrow the memory-side cache when
+//   the XCDs work on 8 different heads, the queues interleave the heads
+//   instead (claim_row_strided).
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
 //   loaded).  The workgroup first flattens its CSR entries into a list of
@@ -232,8 +235,10 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   // `queues`, claimed at start-up (claim_row); a workgroup that finds every
   // row taken leaves at once (workgroup-uniform, before any other barrier).
   __shared__ int64_t row_sh;
-  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh, order)
-                                      : xcd_remap(blockIdx.x, nrows);
+  const int64_t r = queues == nullptr ? xcd_remap(blockIdx.x, nrows)
+                    : (row_ptr == nullptr && g.head_interleave)
+                        ? claim_row_strided(queues, nrows, g, &row_sh)
+                        : claim_row(queues, nrows, g, &row_sh, order);
   if (r < 0) return;
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;

@@ -146,6 +146,39 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const V
   return *row_sh;
 }
 
+// claim_row with the heads interleaved over the queues (uniform rows of a
+// layer whose key/value blocks outgrow the memory-side cache when the 8 XCDs
+// each work on a different head): queue x holds, for every head in turn, the
+// blocks at positions x, x+8, x+16, ... of the head's cost order, so all
+// XCDs work on the same one or two heads at a time and the blocks they
+// stream stay cached.  Same tickets, stealing and exit rule as claim_row.
+__device__ inline int64_t claim_row_strided(unsigned int* queues, int64_t nrows,
+                                            const VsaGeom& g, int64_t* row_sh) {
+  if (threadIdx.x == 0) {
+    int64_t row = -1;
+    const uint32_t n = uint32_t(nrows);
+    const uint32_t nb = uint32_t(g.nb), heads = n / nb;
+    if (atomicAdd(&queues[8], 1u) < n) {
+      const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t x = (home + j) & 7;
+        const uint32_t cx = nb / 8 + (x < nb % 8 ? 1u : 0u);   // positions of x per head
+        const uint32_t count = cx * heads;
+        if (count == 0) continue;
+        const uint32_t t = atomicAdd(&queues[x], 1u);
+        if (t < count) {
+          const uint32_t head = t / cx, p = (t % cx) * 8 + x;
+          row = int64_t(head) * nb + block_in_cost_order(g, int(p));
+          break;
+        }
+      }
+    }
+    *row_sh = row;
+  }
+  __syncthreads();
+  return *row_sh;
+}
+
 // LDS row holding key `key` of a K sub-tile: swap bits 2 and 3.
 __device__ inline int kappa(int key) {
   return (key & ~0xc) | ((key & 4) << 1) | ((key & 8) >> 1);

@@ -225,6 +225,11 @@ vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
   g.npad = npad;
   g.dtype = d->dtype;
   fill_cost_order(g);
+  // K and V of one head: Npad tokens x D x 2 bytes, twice; the 8 XCDs of the
+  // balanced launch each work on one head unless that outgrows the 256 MB
+  // memory-side (Infinity) cache.
+  const int64_t kv_head_bytes = npad * d->head_dim * 2 * 2;
+  g.head_interleave = 8 * kv_head_bytes > (int64_t(256) << 20) ? 1 : 0;
   p->topk = d->topk;
   p->dtype = d->dtype;
   *out = p;

@@ -27,6 +27,11 @@ struct VsaGeom {
   // the k-th class, cstart[k] the position of its first block.
   int32_t corder[8];
   int32_t cstart[8];
+  // Balanced forward launches with uniform rows: 1 when the K and V of the 8
+  // heads the XCDs would work on at once (8 * Npad * D * 2 bytes * 2) exceed
+  // the 256 MB memory-side cache; the queues then interleave the heads'
+  // blocks so that every XCD works on the same head (claim_row_strided).
+  int32_t head_interleave;
 };
 
 struct vsa_plan_s {
