@@ -39,7 +39,9 @@ _HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "vsa.h")
 
 
 def lib_path() -> str:
-    return os.path.join(_PKG_DIR, "libvsa_amd.so")
+    """The library to load: libvsa_amd.so of this package, or the file named by
+    VSA_LIBRARY (the host-sanitizer build of the host-only tests)."""
+    return os.environ.get("VSA_LIBRARY") or os.path.join(_PKG_DIR, "libvsa_amd.so")
 
 
 class VsaError(RuntimeError):
