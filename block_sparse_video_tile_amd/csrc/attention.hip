@@ -9,7 +9,7 @@
 //
 // Work decomposition
 //   One workgroup per CSR row r = (b*NH + h)*nb + i, i.e. one query block of
-//   V = 32*NW tokens; wave w owns query rows 32w .. 32w+31 (in an 8-wave
+//   V = 32*NQ tokens; wave w owns query rows 32w .. 32w+31 (in an 8-wave
 //   block cut by the grid edge to 5 or 6 row groups, waves 4..7 instead share
 //   the last groups by key halves: see the key-half waves below; a 64-token
 //   block runs 4 waves, two per query group, each group's keys split between
@@ -33,9 +33,10 @@
 //   is read from LDS while the current one is being computed.
 //   K (64 x 128) and V^T (128 x 64) sub-tiles are copied HBM/L2 -> LDS
 //   directly (global_load_lds_dwordx4, no VGPR staging), double-buffered, one
-//   barrier per sub-tile.  The copies are issued from inside the MFMA slots
-//   (K in the QK^T half, V in the PV half) rather than as one burst, and
-//   unconditionally, so the slots stay a single basic block.  K runs one
+//   barrier per sub-tile.  With 8 or 6 waves the copies are issued from
+//   inside the MFMA slots (K in the QK^T half, V in the PV half) rather than
+//   as one burst; the 4-wave kernels, whose 64-key steps are too short to
+//   hide them that way, issue theirs at the top of each step.  K runs one
 //   sub-tile ahead of V so that the next sub-tile's QK^T can run on the
 //   matrix cores while this sub-tile's softmax runs on the VALU (software
 //   pipeline inside each wave).
@@ -105,7 +106,7 @@ using namespace tile;
 
 
 // A row's CSR entries are flattened, up to kListEntries at a time (768 in the
-// 2-wave kernel), into a list
+// 64-token kernel), into a list
 // of 64-key sub-tile descriptors in LDS:
 //   (64-token chunk index of the sub-tile within its head) << 7 | (valid keys - 1)
 // K rows of chunk c start at token row 64c of the head and V^T chunk c is the
@@ -359,8 +360,8 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
 #pragma unroll
     for (int x = 0; x < kMaxV; ++x) vo[x] = RASTER ? soff[tb + vrow[x]] + voff[x] : voff[x];
   };
-  // The predicate is evaluated per lane (exec mask) rather than as a branch,
-  // so copies can sit inside the scheduled slots without splitting them.
+  // The predicate is wave-uniform (whether this wave owns chunk x of the
+  // sub-tile); the slot fences keep each copy in its slot either way.
   auto copy_k = [&](const uint4* src, uint32_t off, int x, uint4* dst) {
     if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, off, dst + (wave + x * NW) * 64);
   };
