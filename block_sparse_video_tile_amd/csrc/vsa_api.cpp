@@ -184,14 +184,23 @@ vsa_status vsa_plan(const vsa_plan_desc* d, vsa_plan_t* out) {
   if (d->batch < 1 || d->num_heads < 1 || d->head_dim < 1)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: batch, num_heads, head_dim must be >= 1");
   const int64_t T = d->dit_seq_shape[0], H = d->dit_seq_shape[1], W = d->dit_seq_shape[2];
-  if (d->seq_len != T * H * W)
+  // products of three int32 extents can exceed int64: checked multiplication
+  auto mul3 = [](int64_t a, int64_t b, int64_t c, int64_t* r) {
+    return !__builtin_mul_overflow(a, b, r) && !__builtin_mul_overflow(*r, c, r);
+  };
+  int64_t thw = 0;
+  if (!mul3(T, H, W, &thw))
+    return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: T*H*W overflows 64 bits");
+  if (d->seq_len != thw)
     return fail(VSA_ERR_INVALID_ARGUMENT, "vsa_plan: seq_len %lld != T*H*W = %lld",
-                (long long)d->seq_len, (long long)(T * H * W));
+                (long long)d->seq_len, (long long)thw);
   const int64_t nbt = (T + d->block_size[0] - 1) / d->block_size[0];
   const int64_t nbh = (H + d->block_size[1] - 1) / d->block_size[1];
   const int64_t nbw = (W + d->block_size[2] - 1) / d->block_size[2];
-  const int64_t nb = nbt * nbh * nbw;
-  const int64_t vol = int64_t(d->block_size[0]) * d->block_size[1] * d->block_size[2];
+  int64_t nb = 0, vol = 0;
+  if (!mul3(nbt, nbh, nbw, &nb) ||
+      !mul3(d->block_size[0], d->block_size[1], d->block_size[2], &vol))
+    return fail(VSA_ERR_UNSUPPORTED, "vsa_plan: problem too large for this implementation");
   if (d->topk < 0 || d->topk > nb)
     return fail(VSA_ERR_INVALID_ARGUMENT,
                 "vsa_plan: topk %d outside [1, num_blocks=%lld] (0 selects map mode)", d->topk,

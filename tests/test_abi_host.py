@@ -85,6 +85,8 @@ def test_plan_geometry_agrees_with_oracle(shape, block):
     (dict(dtype=2), vsa.VSA_ERR_UNSUPPORTED),                        # neither bf16 nor fp16
     (dict(block_size=(2, 4, 4)), vsa.VSA_ERR_UNSUPPORTED),           # V = 32
     (dict(block_size=(4, 8, 16)), vsa.VSA_ERR_UNSUPPORTED),          # V = 512
+    (dict(dit_seq_shape=(2**31 - 1,) * 3, seq_len=1), vsa.VSA_ERR_INVALID_ARGUMENT),  # T*H*W > 2^63
+    (dict(block_size=(2**31 - 1,) * 3), vsa.VSA_ERR_UNSUPPORTED),    # block volume > 2^63
 ])
 def test_plan_rejects(kwargs, status):
     args = dict(seq_len=27280, dit_seq_shape=(31, 22, 40), block_size=(4, 8, 8), batch=1,
