@@ -11,10 +11,14 @@
 //   One workgroup per CSR row r = (b*NH + h)*nb + i, i.e. one query block of
 //   V = 32*NQ tokens; wave w owns query rows 32w .. 32w+31 (in an 8-wave
 //   block cut by the grid edge to 5 or 6 row groups, waves 4..7 instead share
-//   the last groups by key halves: see the key-half waves below; a 64-token
-//   block runs 4 waves, two per query group, each group's keys split between
-//   them the same way, so that two workgroups of a CU put two waves on every
-//   SIMD).  Row ids are
+//   the last groups by key halves, and with at most 4 groups waves w and w+4
+//   share group w: see the key-half waves below; a 64-token block runs 4
+//   waves, two per query group, each group's keys split between them the same
+//   way, so that two workgroups of a CU put two waves on every SIMD).  The
+//   8-wave blocked kernel runs the alternating pipeline described at
+//   pp_pipeline (waves 0..3 and 4..7 take turns on the matrix cores, rings of
+//   four K and three V sub-tiles); the others the interleaved step below.
+//   Row ids are
 //   remapped so that each of the 8 XCDs (workgroups are dispatched to XCDs
 //   round-robin) works through a contiguous range of rows, i.e. the same
 //   heads, and its L2 serves their shared key/value blocks.  In the balanced
@@ -32,8 +36,9 @@
 //   divisions and no global index loads; the descriptor three sub-tiles ahead
 //   is read from LDS while the current one is being computed.
 //   K (64 x 128) and V^T (128 x 64) sub-tiles are copied HBM/L2 -> LDS
-//   directly (global_load_lds_dwordx4, no VGPR staging), double-buffered, one
-//   barrier per sub-tile.  With 8 or 6 waves the copies are issued from
+//   directly (global_load_lds_dwordx4, no VGPR staging).  In the interleaved
+//   step they are double-buffered, one barrier per sub-tile; with 8 or 6
+//   waves (the raster kernel) the copies are issued from
 //   inside the MFMA slots (K in the QK^T half, V in the PV half) rather than
 //   as one burst; the 4-wave kernels, whose 64-key steps are too short to
 //   hide them that way, issue theirs at the top of each step.  K runs one
@@ -203,17 +208,23 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     const float* __restrict__ oc, unsigned int* __restrict__ queues,
     const int32_t* __restrict__ order, VsaGeom g, float scale_log2, float scale) {
   static_assert(NW == NQ || (NQ == 2 && NW == 4), "waves: one per query group, or 4 for 2 groups");
-  static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits), "O staging must fit in LDS");
+  static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits) && 8 * 32 * kORow <= 4 * kKUnits,
+                "O staging must fit in LDS");
   const float rescale_thr = 8.0f / scale_log2;  // raw-score growth that triggers a rescale
-  // Sub-tile buffers.  K runs one sub-tile ahead of V: while sub-tile n is
-  // finished, K buffer (n+1)%2 holds K_{n+1} (read) and K buffer n%2 receives
-  // K_{n+2}; V buffer n%2 holds V_n (read) and V buffer (n+1)%2 receives
-  // V_{n+1}.  Four separate arrays let the compiler see that the in-flight
-  // copies never alias the buffers being read.
-  __shared__ __align__(16) uint4 kbuf0[kKUnits];
-  __shared__ __align__(16) uint4 kbuf1[kKUnits];
-  __shared__ __align__(16) uint4 vbuf0[kVUnits];
-  __shared__ __align__(16) uint4 vbuf1[kVUnits];
+  // Sub-tile buffers of the 4- and 6-wave kernels.  K runs one sub-tile
+  // ahead of V: while sub-tile n is finished, K buffer (n+1)%2 holds K_{n+1}
+  // (read) and K buffer n%2 receives K_{n+2}; V buffer n%2 holds V_n (read)
+  // and V buffer (n+1)%2 receives V_{n+1}.  Four separate arrays let the
+  // compiler see that the in-flight copies never alias the buffers being read.
+  // The 8-wave kernel's alternating pipeline (below) keeps rings of four K
+  // and three V sub-tiles instead.
+  constexpr bool kPP = NW == 8 && !RASTER;
+  __shared__ __align__(16) uint4 kbuf0[kPP ? 1 : kKUnits];
+  __shared__ __align__(16) uint4 kbuf1[kPP ? 1 : kKUnits];
+  __shared__ __align__(16) uint4 vbuf0[kPP ? 1 : kVUnits];
+  __shared__ __align__(16) uint4 vbuf1[kPP ? 1 : kVUnits];
+  __shared__ __align__(16) uint4 kring[kPP ? 4 * kKUnits : 1];
+  __shared__ __align__(16) uint4 vring[kPP ? 3 * kVUnits : 1];
   // sub-tile descriptor list of the current pass over the row, and the
   // per-entry scan that places each entry's descriptors
   constexpr int kThreads = NW * 64;
@@ -249,22 +260,27 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   const int lane = tid % 64;
   const int half = lane / 32;
   const int l32 = lane & 31;
-  // Query row groups.  Normally wave w owns rows 32w .. 32w+31.  With 8
-  // waves and 5 or 6 groups holding valid rows (a block cut by the grid
-  // edge), waves 4..7 share the last groups by keys instead: waves 4 and 6
-  // take group 4, waves 5 and 7 group 5; the first of each pair takes keys
-  // 0..31 of every sub-tile and the second keys 32..63, each with its own
-  // online softmax, and the pairs merge before the epilogue.  Waves w and w+4
-  // run on the same SIMD, so each SIMD then carries 1.5 waves of matrix work
-  // instead of 2 on two SIMDs and 1 on the others.
+  // Query row groups.  Normally wave w owns rows 32w .. 32w+31.  The 8-wave
+  // kernel runs the alternating pipeline below, in which waves w and w+4
+  // (always on the same SIMD) take turns on the matrix cores, so each SIMD
+  // needs work for both: with 5 or 6 groups holding valid rows (a block cut
+  // by the grid edge), waves 4..7 share the last groups by keys: waves 4 and
+  // 6 take group 4, waves 5 and 7 group 5; with at most 4 groups, waves w and
+  // w+4 share group w.  In such a pair the first wave takes keys 0..31 of
+  // every sub-tile and the second keys 32..63, each with its own online
+  // softmax, and the pair merges before the epilogue.
   // With 4 waves on a 64-token block (NW = 2*NQ) every group is split:
   // waves 0 and 2 take group 0, waves 1 and 3 group 1, waves 0 and 1 keys
   // 0..31 and waves 2 and 3 keys 32..63.
   const int ngroups = (cq + 31) / 32;
   constexpr bool kAllSplit = NW == 2 * NQ;
   const bool split = kAllSplit || (NW == 8 && (ngroups == 5 || ngroups == 6));  // wg-uniform
-  const int qgroup = kAllSplit ? wave % NQ : (split && wave >= 4 ? 4 + (wave & 1) : wave);
+  const bool split4 = kPP && ngroups <= 4;                                      // wg-uniform
+  const int qgroup = kAllSplit ? wave % NQ
+                     : split4  ? wave & 3
+                               : (split && wave >= 4 ? 4 + (wave & 1) : wave);
   const int khalf = kAllSplit ? wave / NQ
+                    : split4  ? wave >> 2
                               : (split && wave >= 4 ? (wave >> 1) & 1 : -1);  // -1: all 64 keys
   const int qrow = qgroup * 32 + l32;    // this lane's query row inside the block
   const bool active = qgroup * 32 < cq;  // wave-uniform
@@ -380,6 +396,25 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
 #pragma unroll
     for (int x = 0; x < kMaxV; ++x) copy_v(src_of(vbase, desc), vo[x], x, dst);
   };
+  // the same copies issued from inline asm (wave_copy_to_lds_async)
+  auto load_k_async = [&](int desc, uint4* dst) {
+    uint32_t ko[kMaxK];
+    k_offsets(desc, ko);
+#pragma unroll
+    for (int x = 0; x < kMaxK; ++x)
+      if (tid / 64 + x * NW < kKChunks)
+        wave_copy_to_lds_async(src_of(kbase, desc), ko[x] * 16u,
+                               lds_addr(dst + (wave + x * NW) * 64));
+  };
+  auto load_v_async = [&](int desc, uint4* dst) {
+    uint32_t vo[kMaxV];
+    v_offsets(desc, vo);
+#pragma unroll
+    for (int x = 0; x < kMaxV; ++x)
+      if (tid / 64 + x * NW < kVChunks)
+        wave_copy_to_lds_async(src_of(vbase, desc), vo[x] * 16u,
+                               lds_addr(dst + (wave + x * NW) * 64));
+  };
   auto wait_loads = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // per-lane operand bases: K row l32 (+ half unit), V^T row l32 (+ half unit)
@@ -394,18 +429,291 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   const int kread_h = kread + kh * 32 * kKRow;
   const int vread_h = vread + kh * 4;
   const int vtr_h = vtr + kh * 32 * (kRasterVRow * 16);
-  // The passes over the row (list building, prologue, pipelined steps) are
-  // compiled twice, for full waves (HV = false) and for key-half waves, each
-  // with its own register allocation; a wave runs one of them.
-  auto passes = [&](auto hv) __attribute__((always_inline)) {
-  constexpr bool HV = decltype(hv)::value;
-  f32x16 sa[2], sb[2];
-  float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
 
-  for (int e0 = 0; e0 < len; e0 += kList) {
+  // ---- Alternating pipeline of the 8-wave kernel.  Waves 0..3 (group A)
+  // and 4..7 (group B) put one wave on each SIMD each and take turns: while
+  // one wave of a SIMD runs the matrix phase of a sub-tile (M: S_{n+1} =
+  // K_{n+1} Q^T and O^T += V^T_n P^T_n, MFMAs and their LDS operand reads) the
+  // other runs its softmax phase (S: mask, row max exchange, rescale,
+  // exponentials, row sums, rounding of P, and the wave's share of the
+  // global->LDS copies).  A wave issues in order, so with both kinds of work
+  // interleaved in every wave's stream the older wave of a SIMD held the
+  // matrix cores while the younger one waited behind its own MFMAs with its
+  // softmax work unissued.
+  //   Phases are separated by workgroup barriers.  Group A runs QK_0 | S_0 |
+  // M_0 | S_1 | M_1 | ..., group B the same one phase later: in phase 2n
+  // group A runs M_n while group B runs S_n, in phase 2n+1 A runs S_{n+1}
+  // while B runs M_n.  K_j lives in K ring slot j % 4, V_j in V ring slot j % 3.
+  // In S_j group A copies K_{j+3} (into the slot of K_{j-1}, last read by
+  // M_{j-2}) and group B copies V_{j+2} (into the slot of V_{j-1}, last read
+  // by M_{j-1}); at the end of its next M phase each wave waits for all but
+  // the copies of its latest S phase, so a copy has three phases to land
+  // before the barrier ahead of its first reader (the S phase that reads the
+  // first K operands of the M phase using it, or that M phase for V).
+  // The copies are issued from inline asm: their destinations are computed
+  // at run time, and the compiler, unable to place them, would otherwise
+  // wait for all of them before every LDS read.
+  auto pp_pipeline = [&](auto hv, auto gbt, auto comp, int T, auto desc_at)
+      __attribute__((always_inline)) {
+    constexpr bool HV = decltype(hv)::value;          // key-half wave
+    constexpr bool GB = decltype(gbt)::value;         // group B (waves 4..7)
+    constexpr bool kCompute = decltype(comp)::value;  // the wave holds query rows
+    static_assert(!RASTER, "the alternating pipeline serves the blocked layout");
+    constexpr int NQK = HV ? 8 : 16;                  // QK^T MFMAs per sub-tile
+    constexpr int NPV = HV ? 8 : 16;                  // PV MFMAs per sub-tile
+    constexpr int NE = HV ? 8 : 16;                   // exponential pairs per sub-tile
+    // group A copies the 17 chunks of a K sub-tile, group B the 18 of a V
+    // sub-tile; wave gw of a group copies chunks gw, gw+4, gw+8, ...
+    constexpr int kChunks = GB ? kVChunks : kKChunks;
+    constexpr int NCP = (kChunks + 3) / 4;
+    const int gw = wave & 3;
+    const bool last_copy = gw + 4 * (NCP - 1) < kChunks;  // wave-uniform: NCP copies, else NCP-1
+    f32x16 sacc[2];
+    float mx_pre = -INFINITY;
+    uint32_t pw[4][4];
+    ev8 op[8];
+    // this lane's source byte offsets within a sub-tile
+    uint32_t cofs[NCP];
+#pragma unroll
+    for (int x = 0; x < NCP; ++x) {
+      const int c = min(gw + 4 * x, kChunks - 1);
+      const int pos = c * 64 + lane;
+      if constexpr (!GB) {
+        const int row = pos / kKRow, unit = pos % kKRow;
+        cofs[x] = (kappa(row) * 16 + (unit < 16 ? unit : 0)) * 16;
+      } else {
+        const int row = pos / kVRow, unit = pos % kVRow;
+        cofs[x] = (row * 8 + (unit < 8 ? unit : 0)) * 16;
+      }
+    }
+    constexpr uint32_t kSlotBytes = (GB ? kVUnits : kKUnits) * 16;
+    const uint32_t ring0 = lds_addr(GB ? vring : kring) + uint32_t(gw) * 1024u;
+    // copy x of this wave: its chunk of sub-tile `desc` into ring slot `slot`
+    auto copy_one = [&](int x, const char* src, uint32_t dst) __attribute__((always_inline)) {
+      if (x < NCP - 1 || last_copy) wave_copy_to_lds_async(src, cofs[x], dst + uint32_t(x) * 4096u);
+    };
+    // all but this wave's latest batch of copies have landed
+    auto wait_older = [&]() __attribute__((always_inline)) {
+      if (last_copy) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCP) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCP - 1) : "memory");
+    };
+    // Phase barrier.  A fence would make the compiler wait for every load in
+    // flight; an empty asm with a memory clobber keeps it from moving LDS
+    // accesses across the barrier instead.  No LDS read of a wave can still
+    // be pending on a slot that a copy issued after the barrier overwrites:
+    // every M-phase read feeds an MFMA of the same phase, and the reads an S
+    // phase leaves in flight (the next M phase's first K operands, the
+    // descriptors) address slots and lists that stay untouched for several
+    // phases.
+    auto barrier = []() __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    };
+    // operand of M-phase slot s: K rows for the QK^T slots, V^T rows for PV
+    auto operand = [&](const uint4* kn, const uint4* vn, int s) __attribute__((always_inline)) -> ev8 {
+      if (s < NQK) {
+        if constexpr (HV) return as_ev8(kn[kread_h + 2 * s]);
+        else return as_ev8(kn[kread + (s % 2) * 32 * kKRow + 2 * (s / 2)]);
+      }
+      const int w = s - NQK, cc = w / 4, dt = w % 4;
+      return as_ev8(vn[(HV ? vread_h : vread) + dt * 32 * kVRow + 2 * cc]);
+    };
+    // M phase: S_{n+1} = K_{n+1} Q^T into sacc (kn) and, with PV, O^T += V^T_n
+    // P^T_n (vn, pw).  op[0..3] hold the operands of slots 0..3.  The row max
+    // of the new scores is taken in the last slots, after its MFMAs.
+    auto m_phase = [&](const uint4* kn, const uint4* vn, auto withpv) __attribute__((always_inline)) {
+      constexpr bool PV = decltype(withpv)::value;
+      constexpr int NS = PV ? NQK + NPV : NQK;
+      constexpr int MX0 = NS - (HV ? 4 : 8);  // first slot of the row max
+#pragma unroll
+      for (int mt = 0; mt < (HV ? 1 : 2); ++mt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[mt][j] = 0.f;
+      float mxn = -INFINITY;
+      slot_fence();
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        if (s % 4 == 0) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (s + 4 + x < NS) op[(s + 4 + x) % 8] = operand(kn, vn, s + 4 + x);
+        }
+        if (s < NQK) {
+          if constexpr (HV) sacc[0] = mfma_32x32x16<F16>(op[s % 8], qf[s], sacc[0]);
+          else sacc[s % 2] = mfma_32x32x16<F16>(op[s % 8], qf[s / 2], sacc[s % 2]);
+        } else {
+          const int w = s - NQK, cc = w / 4, dt = w % 4;
+          const ev8 pb =
+              __builtin_bit_cast(ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
+          oacc[dt] = mfma_32x32x16<F16>(op[s % 8], pb, oacc[dt]);
+        }
+        if (PV && s >= MX0) {
+          const int mt = HV ? 0 : (s - MX0) / 4, j0 = ((s - MX0) % 4) * 4;
+          mxn = fmaxf(fmaxf(mxn, sacc[mt][j0]), sacc[mt][j0 + 1]);
+          mxn = fmaxf(fmaxf(mxn, sacc[mt][j0 + 2]), sacc[mt][j0 + 3]);
+          pin(mxn);
+        }
+        slot_fence();
+      }
+      if constexpr (PV) mx_pre = mxn;
+      else mx_pre = HV ? tile_max1(sacc[0]) : tile_max(sacc);
+    };
+    // S phase of sub-tile j (descriptor dj, scores in sacc): P_j into pw, the
+    // running max / sum updated; kpre holds K_{j+1}, whose first operands the
+    // next M phase reads (issued last).  cp(e) issues the copies placed after pair e and
+    // tells whether there were any.
+    auto s_phase = [&](int dj, const uint4* kpre, auto&& cp) __attribute__((always_inline)) {
+      float mx = mx_pre;
+      const int valid = (dj & 127) + 1;
+      if (valid < kKvChunk) {
+        // key of register j: (32 mt or 32 kh) + 16 (j/8) + 8 half + j%8; the
+        // comparison is against valid - 8 half - 32 kh so that every key
+        // offset is an immediate
+        const int vh = valid - 8 * half - (HV ? 32 * kh : 0);
+#pragma unroll
+        for (int mt = 0; mt < (HV ? 1 : 2); ++mt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if ((HV ? 0 : mt * 32) + 16 * (j / 8) + (j % 8) >= vh) sacc[mt][j] = -INFINITY;
+        mx = HV ? tile_max1(sacc[0]) : tile_max(sacc);
+      }
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                         false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      if (__ballot(mx > m_run + rescale_thr) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+        m_run = m_new;
+        l_run *= alpha;
+        // in place: O keeps its registers through the (rare) rescale
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            float t = oacc[dt][j];
+            asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t) : "v"(alpha));
+            oacc[dt][j] = t;
+          }
+      }
+      // a key half may have seen only masked keys so far (m_run = -inf); any
+      // finite reference then gives p = 0 for them
+      const float mb = (HV && m_run == -INFINITY) ? 0.f : m_run * scale_log2;
+      // four row-sum accumulators (pairs e % 2 and both lanes of a pair), so
+      // the additions do not form one long dependent chain
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int cc = e / 4, t = 2 * (e % 4);
+        const float s0 = HV ? sacc[0][8 * cc + t] : sacc[cc / 2][8 * (cc % 2) + t];
+        const float s1 = HV ? sacc[0][8 * cc + t + 1] : sacc[cc / 2][8 * (cc % 2) + t + 1];
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, scale_log2, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s1, scale_log2, -mb));
+        rs[2 * (e % 2)] += p0;
+        rs[2 * (e % 2) + 1] += p1;
+        pw[cc][t / 2] = pack2<F16>(p0, p1);
+        // the wave's copies stay spread over the phase (issued together, the
+        // four SIMDs' copies queue behind each other at the CU's vector
+        // memory unit); between copies the scheduler may overlap the pairs
+        if (cp(e)) {
+          pin(rs[2 * (e % 2)]);
+          pin(rs[2 * (e % 2) + 1]);
+          pin(pw[cc][t / 2]);
+          slot_fence();
+        }
+      }
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      // the next M phase's first operands, left in flight across the barrier
+#pragma unroll
+      for (int x = 0; x < 4; ++x) op[x] = operand(kpre, nullptr, x);
+    };
+    auto kslot = [&](int sl) __attribute__((always_inline)) { return kring + sl * kKUnits; };
+    auto vslot = [&](int sl) __attribute__((always_inline)) { return vring + sl * kVUnits; };
+    // S phase of sub-tile j (descriptor dj): the softmax (with rows) and this
+    // wave's copies of sub-tile dc (group A: K_{j+3} into K slot cslot; group
+    // B: V_{j+2} into V slot cslot)
+    auto s_full = [&](int dj, int dc, int kpre_slot, int cslot) __attribute__((always_inline)) {
+      const char* const src = reinterpret_cast<const char*>(src_of(GB ? vbase : kbase, dc));
+      const uint32_t dst = ring0 + uint32_t(cslot) * kSlotBytes;
+      if constexpr (kCompute) {
+        // copy x after exponential pair x * NE / NCP
+        s_phase(dj, kslot(kpre_slot), [&](int e) __attribute__((always_inline)) {
+          bool any = false;
+#pragma unroll
+          for (int x = 0; x < NCP; ++x)
+            if (e == (x * NE) / NCP) {
+              copy_one(x, src, dst);
+              any = true;
+            }
+          return any;
+        });
+      } else {
+#pragma unroll
+        for (int x = 0; x < NCP; ++x) copy_one(x, src, dst);
+      }
+    };
+    auto rfl = [](int x) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(x); };
+
+    // prologue: K_0, K_1, K_2 and V_0, V_1 by all waves
+    const int d0 = __builtin_amdgcn_readfirstlane(desc_at(0));
+    load_k_async(d0, kslot(0));
+    load_k_async(__builtin_amdgcn_readfirstlane(desc_at(1)), kslot(1));
+    load_k_async(__builtin_amdgcn_readfirstlane(desc_at(2)), kslot(2));
+    load_v_async(d0, vslot(0));
+    load_v_async(__builtin_amdgcn_readfirstlane(desc_at(1)), vslot(1));
+    wait_loads();
+    barrier();
+    auto qk0 = [&]() __attribute__((always_inline)) {
+      if constexpr (kCompute) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) op[x] = operand(kslot(0), nullptr, x);
+        m_phase(kslot(0), nullptr, std::false_type());
+      }
+    };
+    if constexpr (!GB) {
+      qk0();  // phase -2 (group B: nothing)
+      barrier();
+      s_full(d0, rfl(desc_at(3)), 1, 3);  // phase -1: S_0, K_3 into slot 3 (group B: QK_0)
+      barrier();
+    } else {
+      barrier();  // phase -2
+      qk0();      // phase -1
+      barrier();
+      s_full(d0, rfl(desc_at(2)), 1, 2);  // phase 0: S_0, V_2 into slot 2 (group A: M_0)
+      barrier();
+    }
+    // iteration n: M_n (K_{n+1} in slot k1, V_n in slot v0), the wait for
+    // this wave's copies of S_{n-1} (those of S_n stay in flight), barrier,
+    // S_{n+1} (first operands of K_{n+2}; group A copies K_{n+4} into the slot
+    // of K_n, group B V_{n+3} into the slot of V_n), barrier.  A copy thus has
+    // three phases to land before the barrier ahead of its first reader.
+    int k1 = 1, v0 = 0;
+    for (int n = 0; n < T; ++n) {
+      // descriptors of S_{n+1}, read before M_n so that it hides their latency
+      const int dj = desc_at(n + 1), dc = desc_at(GB ? n + 3 : n + 4);
+      if constexpr (kCompute) m_phase(kslot(k1), vslot(v0), std::true_type());
+      wait_older();
+      barrier();
+      if (n + 1 < T) s_full(rfl(dj), rfl(dc), (k1 + 1) & 3, GB ? v0 : (k1 + 3) & 3);
+      barrier();
+      k1 = (k1 + 1) & 3;
+      v0 = v0 == 2 ? 0 : v0 + 1;
+    }
+    // group A's last phase: group B runs M_{T-1}
+    if constexpr (!GB) barrier();
+    wait_loads();
+    __syncthreads();
+  };
+
+  // Flatten row entries e0 .. e0+m-1 (m = min(kList, len - e0)) into the
+  // sub-tile list: per-entry sub-tile counts, an exclusive scan of them, then
+  // the descriptors.  Returns the number of sub-tiles (wave-uniform).
+  auto build_list = [&](int e0) __attribute__((always_inline)) -> int {
     const int m = min(kList, len - e0);
-    // ---- flatten entries e0 .. e0+m-1 into the sub-tile list: per-entry
-    // sub-tile counts, an exclusive scan of them, then the descriptors
     for (int e = tid; e < m; e += kThreads) {
       const int j = rcol[e0 + e];
       escan[e] = (j >= 0 && j < g.nb) ? (block_count(g, j) + kKvChunk - 1) / kKvChunk : 0;
@@ -456,7 +764,19 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
       }
     }
     __syncthreads();
-    const int T = __builtin_amdgcn_readfirstlane(ntiles_sh);  // uniform
+    return __builtin_amdgcn_readfirstlane(ntiles_sh);
+  };
+  // The passes over the row (list building, prologue, pipelined steps) of
+  // the 4- and 6-wave kernels are compiled twice, for full waves (HV = false)
+  // and for key-half waves, each with its own register allocation; a wave
+  // runs one of them.
+  auto passes = [&](auto hv) __attribute__((always_inline)) {
+  constexpr bool HV = decltype(hv)::value;
+  f32x16 sa[2], sb[2];
+  float mx_pre = -INFINITY;  // unmasked row max of the scores of sub-tile n
+
+  for (int e0 = 0; e0 < len; e0 += kList) {
+    const int T = build_list(e0);
     if (T == 0) continue;
     // descriptor of sub-tile n; past the end it repeats the last one, whose
     // copies then land in a buffer that is not read again
@@ -792,7 +1112,37 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     }
   }
   };
-  if constexpr (kAllSplit) {
+  // The 8-wave kernel: one instantiation of the alternating pipeline per
+  // wave role (group, key-half or full wave, with or without query rows);
+  // a wave's role is fixed for the row, so each keeps its own registers.
+  auto pp_rows = [&](auto hv, auto gbt, auto comp) __attribute__((always_inline)) {
+    for (int e0 = 0; e0 < len; e0 += kList) {
+      const int T = build_list(e0);
+      if (T == 0) continue;
+      // every global load so far (the Q fragments, the row's column
+      // indices) has landed; said in a form the compiler tracks, since it
+      // does not count the pipeline's copies and would otherwise wait for
+      // them where Q is first used
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+      // descriptor of sub-tile n; past the end it repeats the last one, whose
+      // copies then land in buffers that are not read again
+      auto desc_at = [&](int n) __attribute__((always_inline)) { return tlist[min(n, T - 1)]; };
+      pp_pipeline(hv, gbt, comp, T, desc_at);
+    }
+  };
+  if constexpr (kPP) {
+    using F = std::false_type;
+    using Tr = std::true_type;
+    if (wave < 4) {
+      if (!active) pp_rows(F(), F(), F());
+      else if (split4) pp_rows(Tr(), F(), Tr());
+      else pp_rows(F(), F(), Tr());
+    } else {
+      if (!active) pp_rows(F(), Tr(), F());
+      else if (khalf >= 0) pp_rows(Tr(), Tr(), Tr());
+      else pp_rows(F(), Tr(), Tr());
+    }
+  } else if constexpr (kAllSplit) {
     passes(std::true_type());
   } else {
     if (khalf >= 0) passes(std::true_type());
@@ -800,20 +1150,29 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   }
 
   // ---- key-half pairs: the second wave of a pair hands its (m, l, O^T) to
-  // the first through LDS (8 waves: wave 6's in vbuf1, wave 7's in tlist +
-  // escan; 4 waves: wave 2's in vbuf1, wave 3's in vbuf0; none of which the
-  // epilogue's staging uses), which merges them:
+  // the first through LDS, which merges them:
   // m = max(m_a, m_b), O = O_a 2^((m_a - m)c) + O_b 2^((m_b - m)c), l likewise.
-  // waves 6, 7 of a split 8-wave block: their own rows are padding (zeroed);
-  // waves 2, 3 of a 64-token block own no rows of it
-  const bool own_pad = split && khalf == 1;
+  // Alternating pipeline: wave 4+x's in V ring slot x (x < 3) or K ring slot
+  // 3; 8 waves otherwise: wave 6's in vbuf1, wave 7's in tlist + escan; 4
+  // waves: wave 2's in vbuf1, wave 3's in vbuf0 (none of which the epilogue's
+  // staging of the rows' owners uses).  The second waves of the pairs own
+  // padding rows (zeroed): waves 6, 7 of a 5-6 group block, waves 4..7 of a
+  // block of at most 4 groups; waves 2, 3 of a 64-token block own no rows.
+  const bool own_pad = (split || split4) && khalf == 1;
   const bool owns_rows = wave * 32 < kVol;
-  if (split) {
-    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(vbuf1)
-                                        : (kAllSplit ? reinterpret_cast<float*>(vbuf0)
-                                                     : reinterpret_cast<float*>(tlist));
-    float* const part_ml = (wave & 1) == 0 || kAllSplit ? part + 64 * 64
-                                                        : reinterpret_cast<float*>(escan);
+  if (split || split4) {
+    float* part;
+    if constexpr (kPP) {
+      const int pidx = khalf == 1 ? wave - 4 : (split4 ? wave : wave - 2);
+      part = reinterpret_cast<float*>(pidx < 3 ? vring + pidx * kVUnits : kring + 3 * kKUnits);
+    } else {
+      part = (wave & 1) == 0 ? reinterpret_cast<float*>(vbuf1)
+                             : (kAllSplit ? reinterpret_cast<float*>(vbuf0)
+                                          : reinterpret_cast<float*>(tlist));
+    }
+    float* const part_ml = kPP || (wave & 1) == 0 || kAllSplit ? part + 64 * 64
+                                                               : reinterpret_cast<float*>(escan);
+    static_assert(4 * (64 * 64 + 128) <= 16 * kKUnits, "a merge buffer fits a K tile buffer");
     if (own_pad && active) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -848,7 +1207,8 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   const bool row_valid = active && !own_pad && qrow < cq;
   const float inv = (row_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
   // staging area of 32 rows x 272 B per wave: two waves per buffer
-  uint4* const sbase = wave < 2 ? kbuf0 : (wave < 4 ? kbuf1 : (wave < 6 ? vbuf0 : vbuf1));
+  uint4* const sbase = kPP ? kring + (wave / 2) * kKUnits
+                            : (wave < 2 ? kbuf0 : (wave < 4 ? kbuf1 : (wave < 6 ? vbuf0 : vbuf1)));
   uint4* const srows = sbase + (wave % 2) * 32 * kORow;
   uint2* const ostage = reinterpret_cast<uint2*>(srows);
 #pragma unroll

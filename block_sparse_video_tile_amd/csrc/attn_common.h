@@ -214,5 +214,25 @@ __device__ inline void wave_copy_to_lds(const uint4* src, uint32_t off, uint4* d
       0, 0);
 }
 
+// The same copy issued from inline asm, to the LDS byte address `lds`
+// (wave-uniform) from `src` + `bytes` (per lane).  The compiler then does not
+// see an LDS write in flight, so it inserts no waits for it before LDS reads
+// (it cannot tell which buffer a copy whose destination is computed at run
+// time targets, and would wait for every copy before every read): the caller
+// waits for these copies itself (s_waitcnt vmcnt) before the barrier that
+// publishes them.
+__device__ inline void wave_copy_to_lds_async(const void* src, uint32_t bytes, uint32_t lds) {
+  // s_nop: one wait state between the write of M0 and the copy that reads it
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(bytes), "s"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<void*>(p))));
+}
+
 }  // namespace tile
 }  // namespace vsa

@@ -2,10 +2,14 @@
 attention on raster [B,S,NH,D] tensors (tokens located by block index
 arithmetic inside the kernel, O written straight to raster rows) and the fused
 forward (block means read from the raster tensors; no gather or scatter
-pass).  The raster kernel forms the same products in the same order as the
-blocked kernel, so besides the oracle comparison (same tolerances as the other
-parity tests) its output is compared bit for bit with the blocked kernel
-followed by the scatter.
+pass).  Besides the oracle comparison (same tolerances as the other parity
+tests) the raster output is compared with the blocked kernel followed by the
+scatter: bit for bit for block volumes below 256, where both run the same
+interleaved step and form the same products in the same order; for 256-token
+blocks the blocked kernel runs the alternating (two-group) pipeline, whose
+row sums and key halves of blocks with at most 4 query groups are added in
+another order, so there the two agree to within rounding of the last bit of
+the element type (and the LSE to 1e-4).
 """
 import numpy as np
 import pytest
@@ -54,6 +58,22 @@ def _blocked_then_scatter(plan, q, k, v, row_ptr, col_idx, uniform_k):
     return out.cpu(), lse.cpu()
 
 
+def _same_as_blocked(plan, out, o2, lse=None, l2=None):
+    """Raster vs blocked + scatter: bitwise below 256-token blocks, else to the
+    last bit of the element type (relative 2^-7 of max(1, |x|)) and LSE 1e-4."""
+    if plan.info["block_volume"] < 256:
+        assert torch.equal(out, o2)
+        if lse is not None:
+            assert torch.equal(lse, l2)
+        return
+    a, b = out.double(), o2.double()
+    assert torch.all((a - b).abs() <= 2.0 ** -7 * torch.clamp(b.abs(), min=1.0))
+    if lse is not None:
+        assert torch.equal(torch.isinf(lse), torch.isinf(l2))
+        fin = torch.isfinite(l2)
+        assert torch.all((lse[fin] - l2[fin]).abs() <= 1e-4)
+
+
 def _check_oracle(oplan, out, lse, ref_out, ref_lse, label):
     err = np.abs(out.double().numpy() - ref_out)
     vol = oplan.block_volume
@@ -84,7 +104,7 @@ def test_raster_attention(name, k, dtype):
     out, lse = out.cpu(), lse.cpu()
     _check_oracle(ref["plan"], out, lse, ref["out"], ref["lse"], f"{name} k{k} {dtype}")
     o2, l2 = _blocked_then_scatter(plan, q, kk, v, None, ref["col_idx"], k)
-    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    _same_as_blocked(plan, out, o2, lse, l2)
 
 
 @pytest.mark.parametrize("name,dtype", [("padded_tiny", torch.bfloat16),
@@ -105,7 +125,7 @@ def test_raster_attention_gated_epilogue_equals_gated_scatter(name, dtype):
     out2 = torch.empty(plan.raster_shape(), dtype=dtype, device=DEV)
     vsa.vsa_scatter_gated(plan, ob, oc, gate, out2)
     torch.cuda.synchronize()
-    assert torch.equal(out.cpu(), out2.cpu())
+    _same_as_blocked(plan, out.cpu(), out2.cpu())
 
 
 def test_raster_attention_csr_with_zero_rows():
@@ -122,7 +142,7 @@ def test_raster_attention_csr_with_zero_rows():
     # rows without blocks: O = 0, LSE = -inf
     _check_oracle(oplan, out, lse, np.nan_to_num(ref_o), ref_l, "tile64_tiny CSR")
     o2, l2 = _blocked_then_scatter(plan, q, kk, v, rp, ci, 0)
-    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    _same_as_blocked(plan, out, o2, lse, l2)
 
 
 def test_raster_attention_full_size_csr_map():
@@ -133,7 +153,7 @@ def test_raster_attention_full_size_csr_map():
     plan = _plan(wl)
     out, lse = _raster_attend(plan, q, kk, v, rp, ci, 0)
     o2, l2 = _blocked_then_scatter(plan, q, kk, v, rp, ci, 0)
-    assert torch.equal(out.cpu(), o2) and torch.equal(lse.cpu(), l2)
+    _same_as_blocked(plan, out.cpu(), o2, lse.cpu(), l2)
     # sampled rows against the oracle
     oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size)
     nb = oplan.num_blocks
@@ -177,9 +197,11 @@ def test_fused_forward(name):
     assert exact.all()
     assert np.array_equal(col.reshape(ref["sel"].shape), ref["sel"])
     _check_oracle(ref["plan"], out, lse, ref["out"], ref["lse"], f"fused {name}")
-    # the means are the gather's, so the map and the output are the unfused path's
+    # the means are the gather's, so the map is the unfused path's, and the
+    # output too (to the last bit for 256-token blocks, as above)
     o2, c2, l2 = _forward(plan, q, kk, v, fused=False)
-    assert np.array_equal(col, c2) and torch.equal(out, o2) and torch.equal(lse, l2)
+    assert np.array_equal(col, c2)
+    _same_as_blocked(plan, out, o2, lse, l2)
 
 
 @pytest.mark.parametrize("name,dtype", [("tiny", torch.bfloat16), ("padded_tiny", torch.bfloat16),
