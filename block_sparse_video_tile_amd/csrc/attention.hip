@@ -471,7 +471,8 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     f32x16 sacc[2];
     float mx_pre = -INFINITY;
     uint32_t pw[4][4];
-    ev8 op[8];
+    ev8 op[8];  // operand ring of the M phase
+    constexpr int kPre = 4;  // operand reads in flight ahead of their MFMA
     // this lane's source byte offsets within a sub-tile
     uint32_t cofs[NCP];
 #pragma unroll
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
       return as_ev8(vn[(HV ? vread_h : vread) + dt * 32 * kVRow + 2 * cc]);
     };
     // M phase: S_{n+1} = K_{n+1} Q^T into sacc (kn) and, with PV, O^T += V^T_n
-    // P^T_n (vn, pw).  op[0..3] hold the operands of slots 0..3.  The row max
+    // P^T_n (vn, pw).  op[0..kPre-1] hold the operands of the first slots.  The row max
     // of the new scores is taken in the last slots, after its MFMAs.
     auto m_phase = [&](const uint4* kn, const uint4* vn, auto withpv) __attribute__((always_inline)) {
       constexpr bool PV = decltype(withpv)::value;
@@ -536,11 +537,9 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
       slot_fence();
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        if (s % 4 == 0) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            if (s + 4 + x < NS) op[(s + 4 + x) % 8] = operand(kn, vn, s + 4 + x);
-        }
+        // one operand read per slot, kPre slots ahead, so that the wave keeps
+        // about kPre reads in flight instead of bursts of four
+        if (s + kPre < NS) op[(s + kPre) % 8] = operand(kn, vn, s + kPre);
         if (s < NQK) {
           if constexpr (HV) sacc[0] = mfma_32x32x16<F16>(op[s % 8], qf[s], sacc[0]);
           else sacc[s % 2] = mfma_32x32x16<F16>(op[s % 8], qf[s / 2], sacc[s % 2]);
@@ -558,15 +557,19 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
         }
         slot_fence();
       }
-      if constexpr (PV) mx_pre = mxn;
-      else mx_pre = HV ? tile_max1(sacc[0]) : tile_max(sacc);
+      if constexpr (!PV) mxn = HV ? tile_max1(sacc[0]) : tile_max(sacc);
+      // row max including the partner lane's keys (l ^ 32), taken here so that
+      // its latency overlaps the last MFMAs instead of opening the S phase
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxn), __float_as_uint(mxn),
+                                                       false, false);
+      mx_pre = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     };
     // S phase of sub-tile j (descriptor dj, scores in sacc): P_j into pw, the
     // running max / sum updated; kpre holds K_{j+1}, whose first operands the
     // next M phase reads (issued last).  cp(e) issues the copies placed after pair e and
     // tells whether there were any.
     auto s_phase = [&](int dj, const uint4* kpre, auto&& cp) __attribute__((always_inline)) {
-      float mx = mx_pre;
+      float mx = mx_pre;  // the row max over both lane halves (unmasked)
       const int valid = (dj & 127) + 1;
       if (valid < kKvChunk) {
         // key of register j: (32 mt or 32 kh) + 16 (j/8) + 8 half + j%8; the
@@ -579,8 +582,6 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
           for (int j = 0; j < 16; ++j)
             if ((HV ? 0 : mt * 32) + 16 * (j / 8) + (j % 8) >= vh) sacc[mt][j] = -INFINITY;
         mx = HV ? tile_max1(sacc[0]) : tile_max(sacc);
-      }
-      {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                          false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
       l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
       // the next M phase's first operands, left in flight across the barrier
 #pragma unroll
-      for (int x = 0; x < 4; ++x) op[x] = operand(kpre, nullptr, x);
+      for (int x = 0; x < kPre; ++x) op[x] = operand(kpre, nullptr, x);
     };
     auto kslot = [&](int sl) __attribute__((always_inline)) { return kring + sl * kKUnits; };
     auto vslot = [&](int sl) __attribute__((always_inline)) { return vring + sl * kVUnits; };
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     auto qk0 = [&]() __attribute__((always_inline)) {
       if constexpr (kCompute) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) op[x] = operand(kslot(0), nullptr, x);
+        for (int x = 0; x < kPre; ++x) op[x] = operand(kslot(0), nullptr, x);
         m_phase(kslot(0), nullptr, std::false_type());
       }
     };
