@@ -24,8 +24,10 @@
 //   heads, and its L2 serves their shared key/value blocks.  In the balanced
 //   launch the same ranges are queues from which the workgroups claim their
 //   rows at run time (claim_row), so XCDs that run faster take more rows;
-//   for a caller's block map the rows of each queue are first sorted longest
-//   first (order_rows_kernel), so that long rows do not start last; for a
+//   for a caller's block map the rows of each queue are first put in claim
+//   order (order_rows_kernel: long rows first, then head by head by entry
+//   count, so that the workgroups of an XCD stream a head's key blocks in
+//   step and share them in L2); for a
 //   layer whose heads' key/value blocks outgrow the memory-side cache when
 //   the XCDs work on 8 different heads, the queues interleave the heads
 //   instead (claim_row_strided).
@@ -1279,19 +1281,28 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   }
 }
 
-// Rows of each of the 8 queue ranges of the balanced launch, longest first,
-// for block maps whose rows differ in length: four classes by the row's
-// entry count against the range's mean (>= 4x, >= 2x, >= 1x, shorter), each
-// class in ascending row order.  order[start .. start + count) of range x is
-// a permutation of those rows; claim_row hands positions out in that order,
-// so a range's long rows start first instead of whenever their position
-// comes up.  One workgroup per range; offsets are sanitised as the
-// attention kernel sanitises them.
+// Rows of each of the 8 queue ranges of the balanced launch in claim order,
+// for block maps whose rows differ in length.  First the range's long rows
+// (entry count >= 4x the range's mean), in ascending row order, so that none
+// of them starts late; then the other rows head by head (a head is a run of
+// nb consecutive rows), within a head by entry count, largest first, equal
+// counts in ascending row order.  The workgroups running at once on an XCD
+// then hold rows of one head with about the same number of key blocks, and as
+// every row's column list is streamed in ascending order they move through
+// the head's key blocks in step and share them in the XCD's L2: the key and
+// value blocks of one head of a random map are several times the L2, and
+// rows at different points of their lists would each miss.
+// order[start .. start + count) of range x is a permutation of the range's
+// rows; claim_row hands positions out in that order.  One workgroup per
+// range; offsets are sanitised as the attention kernel sanitises them.
 __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ row_ptr,
-                                                          int64_t nnz, int64_t nrows,
+                                                          int64_t nnz, int64_t nrows, int nb,
                                                           int32_t* __restrict__ order) {
+  constexpr int kBins = 2048;  // entry counts >= kBins - 1 share the first bin
   __shared__ long long wsum[16];
   __shared__ int wcnt[16];
+  __shared__ int bin_at[kBins];  // count, then first position, of each bin of a head
+  __shared__ __align__(16) int keys[1024];
   const uint32_t n = uint32_t(nrows), per = n / 8, rem = n % 8, x = blockIdx.x;
   const uint32_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   const uint32_t count = per + (x < rem ? 1u : 0u);
@@ -1309,29 +1320,87 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
   __syncthreads();
   long long total = 0;
   for (int w = 0; w < 16; ++w) total += wsum[w];
-  // class of a row: len*count compared with k*total (integer arithmetic)
-  auto cls = [&](int64_t l) {
-    const long long lc = (long long)l * (long long)count;
-    return lc >= 4 * total ? 0 : lc >= 2 * total ? 1 : lc >= total ? 2 : 3;
-  };
+  // long row: len*count >= 4*total (integer arithmetic)
+  auto is_long = [&](int64_t l) { return (long long)l * (long long)count >= 4 * total; };
+  // bin of a row that is not long: 0 for the largest counts
+  auto bin_of = [&](int64_t l) { return kBins - 1 - int(min(l, int64_t(kBins - 1))); };
+
+  // the long rows, ascending (ballot compaction, 1024 rows at a time)
   uint32_t base = 0;
-  for (int c = 0; c < 4; ++c) {
-    for (uint32_t chunk = 0; chunk < count; chunk += 1024) {
-      const uint32_t t = chunk + tid;
-      const bool flag = t < count && cls(len(start + t)) == c;
-      const unsigned long long b = __ballot(flag);
-      const int before = __popcll(b & ((1ull << lane) - 1ull));
-      __syncthreads();   // wcnt of the previous chunk has been read by everyone
-      if (lane == 0) wcnt[wave] = __popcll(b);
-      __syncthreads();
-      int woff = 0, ctot = 0;
-      for (int w = 0; w < 16; ++w) {
-        woff += w < wave ? wcnt[w] : 0;
-        ctot += wcnt[w];
-      }
-      if (flag) order[start + base + woff + before] = int32_t(start + t);
-      base += ctot;
+  for (uint32_t chunk = 0; chunk < count; chunk += 1024) {
+    const uint32_t t = chunk + tid;
+    const bool flag = t < count && is_long(len(start + t));
+    const unsigned long long b = __ballot(flag);
+    const int before = __popcll(b & ((1ull << lane) - 1ull));
+    __syncthreads();  // wcnt of the previous chunk has been read by everyone
+    if (lane == 0) wcnt[wave] = __popcll(b);
+    __syncthreads();
+    int woff = 0, ctot = 0;
+    for (int w = 0; w < 16; ++w) {
+      woff += w < wave ? wcnt[w] : 0;
+      ctot += wcnt[w];
     }
+    if (flag) order[start + base + woff + before] = int32_t(start + t);
+    base += ctot;
+  }
+  if (count == 0 || nb <= 0) return;
+
+  // the other rows, head by head: a counting sort by bin
+  const uint32_t last = start + count;
+  for (uint32_t h0 = start - start % uint32_t(nb); h0 < last; h0 += uint32_t(nb)) {
+    const uint32_t s0 = max(h0, start), s1 = min(h0 + uint32_t(nb), last);
+    for (int b = tid; b < kBins; b += 1024) bin_at[b] = 0;
+    __syncthreads();
+    for (uint32_t t = s0 + tid; t < s1; t += 1024) {
+      const int64_t l = len(t);
+      if (!is_long(l)) atomicAdd(&bin_at[bin_of(l)], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the bin counts (two bins per thread)
+    const int c0 = bin_at[2 * tid], c1 = bin_at[2 * tid + 1];
+    int incl = c0 + c1;
+    for (int d = 1; d < 64; d *= 2) {
+      const int up = __shfl_up(incl, d);
+      if (lane >= d) incl += up;
+    }
+    __syncthreads();  // wcnt of the long-row pass or the previous head has been read
+    if (lane == 63) wcnt[wave] = incl;
+    __syncthreads();
+    int woff = 0, htot = 0;
+    for (int w = 0; w < 16; ++w) {
+      woff += w < wave ? wcnt[w] : 0;
+      htot += wcnt[w];
+    }
+    const int excl = woff + incl - (c0 + c1);
+    bin_at[2 * tid] = excl;
+    bin_at[2 * tid + 1] = excl + c0;
+    __syncthreads();
+    // place the head's rows 1024 at a time: a row's position is its bin's
+    // next free position plus the rows of the same bin before it in the chunk
+    for (uint32_t chunk = s0; chunk < s1; chunk += 1024) {
+      const uint32_t t = chunk + tid;
+      int key = -1;
+      if (t < s1) {
+        const int64_t l = len(t);
+        if (!is_long(l)) key = bin_of(l);
+      }
+      keys[tid] = key;
+      __syncthreads();
+      int same = 0;
+      if (key >= 0) {
+        const int4* k4 = reinterpret_cast<const int4*>(keys);
+        for (int j = 0; j < tid / 4; ++j) {
+          const int4 kk = k4[j];
+          same += (kk.x == key) + (kk.y == key) + (kk.z == key) + (kk.w == key);
+        }
+        for (int j = tid & ~3; j < tid; ++j) same += keys[j] == key;
+        order[start + base + bin_at[key] + same] = int32_t(t);
+      }
+      __syncthreads();  // every row of the chunk has read bin_at
+      if (key >= 0) atomicAdd(&bin_at[key], 1);
+      __syncthreads();
+    }
+    base += uint32_t(htot);
   }
 }
 
@@ -1353,7 +1422,8 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (row_ptr != nullptr && order != nullptr) {
-      hipLaunchKernelGGL(order_rows_kernel, dim3(8), dim3(1024), 0, s, row_ptr, nnz, rows, order);
+      hipLaunchKernelGGL(order_rows_kernel, dim3(8), dim3(1024), 0, s, row_ptr, nnz, rows, g.nb,
+                         order);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       claim_order = order;

@@ -110,7 +110,8 @@ __device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
 // the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
 // reaches the workgroup through LDS.  With `order` (block maps of their own
 // row lengths), position p of the queues is row order[p] instead of the
-// cost order above: the rows of each queue range sorted longest first.
+// cost order above: the rows of each queue range in the claim order of a
+// block map (order_rows_kernel).
 __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const VsaGeom& g,
                                     int64_t* row_sh, const int32_t* order = nullptr) {
   if (threadIdx.x == 0) {

@@ -416,7 +416,7 @@ vsa_status check_raster_args(const char* fn, vsa_plan_t p, const void* gate, con
 }
 
 // Workspace of the balanced attention launches: the row-queue counters, then
-// one int32 per row for the longest-first order of a block map.
+// one int32 per row for the claim order of a block map's rows.
 size_t attn_ws_bytes(const VsaGeom& g) {
   return vsa::kAttnQueueBytes + align256(size_t(g.batch) * g.heads * g.nb * 4);
 }
@@ -478,7 +478,7 @@ vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const 
   if (vsa_status st = check_lse(fn, lse)) return st;
   // The scratch holds the 9 row-queue counters of the balanced launch (32-bit:
   // every plan's row count, at most 2^30, fits them) and, for a block map,
-  // the longest-first order of at most kNoAllocMaxMapRows rows.
+  // the claim order of at most kNoAllocMaxMapRows rows.
   const int64_t rows = int64_t(p->g.batch) * p->g.heads * p->g.nb;
   if (row_ptr != nullptr && rows > vsa::kNoAllocMaxMapRows)
     return fail(VSA_ERR_UNSUPPORTED,

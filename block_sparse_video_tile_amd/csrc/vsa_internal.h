@@ -92,14 +92,15 @@ hipError_t launch_score_topk(const VsaGeom& g, const float* qp, const float* kp,
 // device counters (kAttnQueueBytes of workspace) from which the workgroups
 // of a larger launch claim their rows.  order: with queues and a block map
 // (row_ptr), an int32 buffer of one entry per row that receives the rows of
-// each queue sorted longest first (nullptr: claims in plain order).
+// each queue in claim order (long rows first, then head by head by entry
+// count; nullptr: claims in plain order).
 constexpr size_t kAttnQueueBytes = 256;
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, unsigned int* queues,
                            int32_t* order, hipStream_t s);
 // Fixed device scratch of the no-allocation attention entry point: the row
-// queues, then the longest-first row order of a block map of at most
+// queues, then the claim order of the rows of a block map of at most
 // kNoAllocMaxMapRows rows; and its device address on the current device.
 constexpr int64_t kNoAllocMaxMapRows = int64_t(1) << 16;
 constexpr size_t kNoAllocScratchBytes = kAttnQueueBytes + size_t(kNoAllocMaxMapRows) * 4;

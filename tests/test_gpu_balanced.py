@@ -55,6 +55,44 @@ def _both_blocked(plan, qb, kb, vb, rp, col, uk, ws):
     return outs
 
 
+# Byte offset of the claim order in the balanced launch's workspace (after
+# the 256 bytes of row-queue counters).
+_ORDER_OFFSET = 256
+
+
+def _expected_claim_order(rp_h, nb):
+    """The claim order of a block map's rows, written from its rule: the rows
+    cut into 8 ranges as the queues cut them; in each range first the long
+    rows (entry count times the range's row count at least 4 times the
+    range's entries) in ascending order, then the others head by head (nb
+    rows per head), by entry count descending (counts of 2047 and more count
+    as 2047), equal counts ascending."""
+    lens = np.diff(np.asarray(rp_h, np.int64))
+    n = len(lens)
+    per, rem = n // 8, n % 8
+    out = []
+    for x in range(8):
+        start = x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per
+        count = per + (1 if x < rem else 0)
+        rows = np.arange(start, start + count)
+        total = int(lens[rows].sum()) if count else 0
+        is_long = lens[rows] * count >= 4 * total
+        out += [int(r) for r in rows[is_long]]
+        rest = rows[~is_long]
+        out += sorted((int(r) for r in rest), key=lambda r: (r // nb, -min(lens[r], 2047), r))
+    return np.array(out, np.int64)
+
+
+def _check_claim_order(ws, rp_h, nb, what):
+    rows = len(rp_h) - 1
+    got = ws[_ORDER_OFFSET:_ORDER_OFFSET + 4 * rows].cpu().view(torch.int32).numpy()
+    exp = _expected_claim_order(rp_h, nb)
+    assert np.array_equal(np.sort(got), np.arange(rows)), f"{what}: claim order is no permutation"
+    bad = np.flatnonzero(got != exp)
+    assert bad.size == 0, f"{what}: claim order differs at {bad.size} positions, first {bad[:5]}"
+    _say(f"    {what}: claim order of {rows} rows as expected")
+
+
 def _assert_same(a, b, what):
     assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)), f"{what}: O differs"
     assert torch.equal(a[1], b[1]), f"{what}: LSE differs"
@@ -106,8 +144,10 @@ def test_csr_maps_with_empty_rows(name):
     rp_h, ci_h, _ = make_tile64_map(wl)
     rp = torch.as_tensor(rp_h, dtype=torch.int32).to(DEV)
     col = torch.as_tensor(ci_h, dtype=torch.int32).to(DEV)
-    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, _junk_workspace(plan))
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
     _assert_same(plain, bal, name)
+    _check_claim_order(ws, rp_h, plan.info["num_blocks"], name)
 
 
 def test_rows_longer_than_one_list_pass():
@@ -123,8 +163,34 @@ def test_rows_longer_than_one_list_pass():
     qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
     rp = torch.as_tensor(rp_h.astype(np.int32)).to(DEV)
     col = torch.as_tensor(np.array(sum(lists, []), np.int32)).to(DEV)
-    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, _junk_workspace(plan))
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
     _assert_same(plain, bal, "long rows")
+    _check_claim_order(ws, rp_h, nt, "long rows")
+
+
+def test_claim_order_across_heads():
+    """Queue ranges that start and end inside heads (5 heads of 300 tiles
+    over 8 ranges), rows of every length from 0 to 300 in random order."""
+    nt, heads = 300, 5
+    wl = Workload("order_heads", (1, 1, nt * 64), (1, 1, 64), 1, heads, 128, None, seed=22)
+    rng = np.random.default_rng(22)
+    lists = []
+    for h in range(heads):
+        for i in range(nt):
+            k = int(rng.integers(0, nt + 1))
+            lists.append(sorted(rng.choice(nt, size=k, replace=False).tolist()))
+    rp_h = np.zeros(len(lists) + 1, np.int64)
+    rp_h[1:] = np.cumsum([len(x) for x in lists])
+    plan = _plan(wl)
+    q, kk, v = make_qkv(wl)
+    qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
+    rp = torch.as_tensor(rp_h.astype(np.int32)).to(DEV)
+    col = torch.as_tensor(np.array(sum(lists, []), np.int32)).to(DEV)
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
+    _assert_same(plain, bal, "order across heads")
+    _check_claim_order(ws, rp_h, nt, "order across heads")
 
 
 @pytest.mark.parametrize("gated", [False, True])
