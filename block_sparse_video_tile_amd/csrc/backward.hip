@@ -12,8 +12,8 @@
 //
 // Kernels
 //   rowdot    D_q for every blocked row.
-//   transpose blocked token-major -> d-major 64-token chunks (the layout the
-//             forward uses for V^T), for K, Q and dO.
+//   transpose blocked token-major K -> d-major 64-token chunks (the layout
+//             the forward uses for V^T), the A operand of dQ^T += K^T dS^T.
 //   tmap      per key block j, the query blocks i whose row lists j, with the
 //             multiplicity, ascending i (one thread per column, no atomics).
 //   dq        one workgroup per query block, wave w owns 32 query rows:
@@ -21,22 +21,20 @@
 //             staged kappa-permuted, so dS^T comes out in exactly the register
 //             layout of the B operand of dQ^T += K^T dS^T (the forward's PV
 //             arrangement with K^T in place of V^T).
-//   dv, dk    one workgroup per key block, wave w owns 32 keys, streaming the
+//   dkv       one workgroup per key block, wave w owns 32 keys, streaming the
 //             64-query sub-tiles of the query blocks that selected the block:
 //             S = Q K^T and dP = dO V^T with the query rows staged
 //             kappa-permuted, so P and dS feed dV^T += dO^T P and
-//             dK^T += Q^T dS as B operands.  dV and dK are separate kernels so
-//             that each stays within 256 VGPRs per lane.
-// dv runs the forward kernel's software pipeline (S of the next sub-tile on
-// the matrix cores while this sub-tile's P is formed, 32 fenced MFMA slots per
-// sub-tile).  dq and dk keep S and dP of one sub-tile at a time (their
-// operands leave no room for a second set), with the sub-tile copies
-// double-buffered; dk lays each sub-tile out in 48 fenced slots so that the
-// dS pairs of one query tile run beside the matrix products of the next (for
-// dq, with a single lse per lane, the compiler's own order measured faster).
-// All three take their query block or key block from per-XCD queues at run
-// time (claim_row, counters in the workspace), as the forward's balanced
-// launch does; the results do not depend on which workgroup takes which.
+//             dK^T += Q^T dS as B operands; the A operands Q^T and dO^T are
+//             read from the same row-major tiles with the transposing LDS
+//             read.  S and dP are formed once for both gradients.
+// dq keeps S and dP of one sub-tile at a time, with the sub-tile copies
+// double-buffered (for dq, with a single lse per lane, the compiler's own
+// order measured faster than fenced slots); dkv lays each 32-query half of a
+// sub-tile out in 32 fenced MFMA slots.  Both take their query block or key
+// block from per-XCD queues at run time (claim_row, counters in the
+// workspace), as the forward's balanced launch does; the results do not
+// depend on which workgroup takes which.
 
 #include <algorithm>
 #include <type_traits>
@@ -206,7 +204,8 @@ __device__ inline void store_rows(const f32x16 (&acc)[4], float mul, uint4* rows
 
 // Each workgroup flattens its work (the CSR row for dQ, the key block's list
 // of query blocks for dK/dV) into a list of 64-token sub-tile descriptors in
-// LDS, kPassEntries entries at a time:
+// LDS, kPassEntries entries at a time (half as many in dkv, whose LDS holds
+// the key block's V rows as well):
 //   (64-token chunk index within the head) << 7 | (valid tokens - 1)
 // and then streams the sub-tiles double-buffered: the copies of sub-tile n+1
 // are in flight while sub-tile n is computed, one wait and one barrier per
@@ -495,337 +494,98 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
                   half);
 }
 
-// ------------------------------------------------------------------ dV, dK
+// ------------------------------------------------------------------ dK and dV together
 
-// Per 64-query sub-tile the workgroup stages lse (log2 units, +inf for pad
-// query rows) and D; register jj of query tile mt holds query
-// 32mt + 16(jj/8) + 8*half + jj%8 (query rows staged kappa-permuted).
-__device__ inline int query_of(int mt, int jj, int half) {
-  return 32 * mt + 16 * (jj / 8) + 8 * half + jj % 8;
+// Query sub-tiles of the fused dK/dV kernel: 64 query rows, kappa-permuted,
+// of 16 data units and 2 pad units (288 B).  They are read as rows
+// (ds_read_b128: the A operands of S = Q K^T and dP = dO V^T) and as columns
+// (ds_read_b64_tr_b16: the A operands of dK^T += Q^T dS and dV^T += dO^T P);
+// with 288-byte rows both kinds of read fall on distinct banks.
+constexpr int kQRow = 18;
+constexpr int kQUnits = 64 * kQRow;    // 1152 16-byte units (18 KB)
+constexpr int kQChunks = kQUnits / 64;  // 18 wave-loads of 1 KB
+
+// Source unit (within a 64-token sub-tile) of LDS position pos of a query
+// sub-tile; a pad unit re-reads a unit of its row.
+__device__ inline uint32_t qtile_off(int pos) {
+  const int row = pos / kQRow, unit = pos % kQRow;
+  return kappa(row) * 16 + (unit < 16 ? unit : unit - 16);
 }
 
-template <int NW, bool F16>
-__global__ __launch_bounds__(NW * 64) void dk_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ qt, const uint4* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ dsum,
-    const int32_t* __restrict__ tlist, const int32_t* __restrict__ tcount,
-    uint4* __restrict__ grad, unsigned int* __restrict__ queues, VsaGeom g, float scale_log2,
-    float scale) {
-  constexpr int kThreads = NW * 64;
-  constexpr int kPassTiles = kPassEntries * (NW / 2);
-  // two buffer sets.  A operand of the first product(s): query rows (Q, and
-  // dO for dK); A of the accumulation: d rows (dO^T for dV, Q^T for dK)
-  __shared__ __align__(16) uint4 qs0[kKUnits];
-  __shared__ __align__(16) uint4 ds0[kKUnits];
-  __shared__ __align__(16) uint4 ts0[kVUnits];
-  __shared__ __align__(16) uint4 qs1[kKUnits];
-  __shared__ __align__(16) uint4 ds1[kKUnits];
-  __shared__ __align__(16) uint4 ts1[kVUnits];
-  __shared__ __align__(16) float lse_sh[2][kKvChunk];
-  __shared__ __align__(16) float d_sh[2][kKvChunk];
-  __shared__ int tl[kPassTiles];
-  __shared__ float tm[kPassTiles];  // multiplicity of each sub-tile's query block
-  __shared__ int esc[kPassEntries];
-  __shared__ int ntl;
-  const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
-  __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
-  const int64_t c = queues != nullptr ? claim_row(queues, ncols, g, &col_sh)
-                                      : xcd_remap(blockIdx.x, ncols);
-  if (c < 0) return;
-  const int j = int(c % g.nb);
-  const int64_t bh = c / g.nb;
-  const int cj = block_count(g, j);
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
-  // Query-half waves for edge key blocks: with 8 waves and 5 or 6 groups of
-  // valid keys, waves 4 and 6 share key group 4 and waves 5 and 7 group 5,
-  // the first of each pair taking queries 0..31 of every query sub-tile and
-  // the second queries 32..63; the second's partial dK is added to the
-  // first's before the store.  Waves w and w+4 share a SIMD.
-  const int ngroups = (cj + 31) / 32;
-  const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
-  const int kgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
-  const int qhalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all queries
-  const int qh = qhalf > 0 ? 1 : 0;
-  const int key = kgroup * 32 + l32;
-  const bool active = kgroup * 32 < cj;
-  const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-  ev8 kf[8], vf[8];
-  if (active) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      kf[s] = as_ev8(k[(key0 + key) * 16 + 2 * s + half]);
-      vf[s] = as_ev8(v[(key0 + key) * 16 + 2 * s + half]);
-    }
-  }
-  f32x16 acc[4];
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i%4 of the 8-byte segments addressed by lanes 4e + i/4, e = 0..3.
+__device__ inline v4i16 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+}
+
+// Store a 32 x 128 accumulator tile whose MFMA row m of tile dt holds column
+// d = 64(m/16) + 16dt + m%16 (the order the transposing reads produce), times
+// `mul`, as element rows: register j of lane l holds key l%32 and
+// d = 64(j/8) + 16dt + 8((j/4)%2) + 4(l/32) + j%4.
+template <bool F16>
+__device__ inline void store_rows_perm(const f32x16 (&acc)[4], float mul, uint4* rows_base,
+                                       int l32, int half) {
+  uint2* dst = reinterpret_cast<uint2*>(rows_base + int64_t(l32) * 16);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
-
-  const uint4* const qbase = q + bh * g.npad * 16;
-  const uint4* const dbase = dout + bh * g.npad * 16;
-  const uint4* const tbase = qt + bh * (g.npad / kKvChunk) * kUnits;
-  const int cpb = g.vol / kKvChunk;
-  const int qread = l32 * kKRow + half, tread = l32 * kVRow + half;
-
-  // copies of one query sub-tile and its lse / D (threads 0..63, plain loads)
-  auto issue = [&](int d, uint4* qsb, uint4* dsb, uint4* tsb, int set) {
-    const int64_t chunk = d >> 7;
-    copy_tile<NW, kKChunks>(qbase + chunk * kUnits, qsb, wave, lane, true);
-    copy_tile<NW, kKChunks>(dbase + chunk * kUnits, dsb, wave, lane, true);
-    copy_tile<NW, kVChunks>(tbase + chunk * kUnits, tsb, wave, lane, false);
-    if (tid < kKvChunk) {
-      const int64_t row = bh * g.npad + chunk * kKvChunk + tid;
-      const bool ok = tid <= (d & 127);
-      lse_sh[set][tid] = ok ? lse[row] * kLog2e : INFINITY;
-      d_sh[set][tid] = ok ? dsum[row] : 0.f;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 64 * (jj / 2) + 16 * dt + 8 * (jj % 2) + 4 * half;
+      dst[d0 / 4] = make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
+                               pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
     }
-  };
-  // One query sub-tile in 48 fenced MFMA slots: S and dP of query tile 0
-  // (16), those of tile 1 (16) with the dS pairs of tile 0 on the VALU, dK^T
-  // for queries 0..31 (8) with the dS pairs of tile 1, dK^T for queries
-  // 32..63 (8).  Operands are read from LDS three slots ahead, the lse and D
-  // of a pair two pairs ahead.
-  auto compute = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
-    if (!active) return;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) s[mt][jj] = dp[mt][jj] = 0.f;
-    uint32_t bw[4][4];  // dS pairs: B operands of the 4 dK^T steps
-    // pad keys of this block take no part (their rows are also stored as 0):
-    // their K rows are zero, so P is finite there and the factor 0 removes it
-    const float mlane = key < cj ? mult : 0.f;
-    // pair k (0..15): query tile mt = k/8, step cc = 2mt + (k%8)/4, queries
-    // t, t+1 of it with t = 2(k%4), i.e. rows 16cc + 8*half + t (kappa-staged)
-    float2 lsep[3], dp2[3];
-    auto read_pair = [&](int k) {
-      const int cc = 2 * (k / 8) + (k % 8) / 4, t = 2 * (k % 4);
-      const int qi = 16 * cc + 8 * half + t;
-      lsep[k % 3] = *reinterpret_cast<const float2*>(&lse_sh[set][qi]);
-      dp2[k % 3] = *reinterpret_cast<const float2*>(&d_sh[set][qi]);
-    };
-    auto ds_pair = [&](int k) {
-      const int mt = k / 8, cc = 2 * mt + (k % 8) / 4, t = 2 * (k % 4);
-      const float2 l = lsep[k % 3], dd = dp2[k % 3];
-      const int jj = 8 * (cc % 2) + t;
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[mt][jj], scale_log2, -l.x)) * mlane;
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[mt][jj + 1], scale_log2, -l.y)) * mlane;
-      bw[cc][t / 2] = pack2<F16>(p0 * (dp[mt][jj] - dd.x), p1 * (dp[mt][jj + 1] - dd.y));
-      pin_v(bw[cc][t / 2]);
-    };
-    ev8 op[4];
-    auto read_op = [&](int i) {
-      if (i < 32) {
-        const int mt = i / 16, st = (i % 16) / 2;
-        const uint4* b = (i % 2 == 0) ? qsb : dsb;
-        op[i % 4] = as_ev8(b[qread + mt * 32 * kKRow + 2 * st]);
-      } else {
-        const int x = i - 32, cc = x / 4, dt = x % 4;
-        op[i % 4] = as_ev8(tsb[tread + dt * 32 * kVRow + 2 * cc]);
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < 3; ++i) read_op(i);
-    read_pair(0);
-    read_pair(1);
-    slot_fence();
-#pragma unroll
-    for (int i = 0; i < 48; ++i) {
-      if (i + 3 < 48) read_op(i + 3);
-      if (i < 32) {
-        const int mt = i / 16, st = (i % 16) / 2;
-        if (i % 2 == 0) s[mt] = mfma_32x32x16<F16>(op[i % 4], kf[st], s[mt]);
-        else dp[mt] = mfma_32x32x16<F16>(op[i % 4], vf[st], dp[mt]);
-        if (i >= 16 && i % 2 == 1) {
-          const int k = (i - 16) / 2;
-          if (k + 2 < 16) read_pair(k + 2);
-          ds_pair(k);
-        }
-      } else {
-        const int x = i - 32, cc = x / 4, dt = x % 4;
-        const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
-                                                         bw[cc][3]));
-        acc[dt] = mfma_32x32x16<F16>(op[i % 4], b, acc[dt]);
-        if (x < 8) {
-          const int k = 8 + x;
-          if (k + 2 < 16) read_pair(k + 2);
-          ds_pair(k);
-        }
-      }
-      slot_fence();
-    }
-  };
-
-  // query-half wave: one 32-query tile (queries 32qh..) of S and dP, dK^T
-  // from the matching two 16-query steps
-  const int qread_h = qread + qh * 32 * kKRow, tread_h = tread + 4 * qh;
-  auto compute_half = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb,
-                          int set) {
-    if (!active) return;
-    f32x16 s1, dp1;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) s1[jj] = dp1[jj] = 0.f;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      s1 = mfma_32x32x16<F16>(as_ev8(qsb[qread_h + 2 * st]), kf[st], s1);
-      dp1 = mfma_32x32x16<F16>(as_ev8(dsb[qread_h + 2 * st]), vf[st], dp1);
-    }
-    const float mlane = key < cj ? mult : 0.f;
-    uint32_t bw[2][4];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      // queries 32qh + 16cc + 8*half + 0..7
-      const int q0 = 32 * qh + 16 * cc + 8 * half;
-      float lq[8], dq8[8];
-      *reinterpret_cast<float4*>(&lq[0]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0]);
-      *reinterpret_cast<float4*>(&lq[4]) = *reinterpret_cast<const float4*>(&lse_sh[set][q0 + 4]);
-      *reinterpret_cast<float4*>(&dq8[0]) = *reinterpret_cast<const float4*>(&d_sh[set][q0]);
-      *reinterpret_cast<float4*>(&dq8[4]) = *reinterpret_cast<const float4*>(&d_sh[set][q0 + 4]);
-#pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        float x2[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int jj = 8 * cc + t + u;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s1[jj], scale_log2, -lq[t + u])) * mlane;
-          x2[u] = p * (dp1[jj] - dq8[t + u]);
-        }
-        bw[cc][t / 2] = pack2<F16>(x2[0], x2[1]);
-      }
-    }
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const ev8 b = __builtin_bit_cast(ev8, make_uint4(bw[cc][0], bw[cc][1], bw[cc][2],
-                                                       bw[cc][3]));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma_32x32x16<F16>(as_ev8(tsb[tread_h + dt * 32 * kVRow + 2 * cc]), b,
-                                     acc[dt]);
-    }
-  };
-
-  const int nent = tcount[c];
-  const int32_t* list = tlist + c * int64_t(g.nb);
-  // the passes are compiled twice (full and query-half waves), each with its
-  // own register allocation
-  auto passes = [&](auto hv) __attribute__((always_inline)) {
-  constexpr bool HV = decltype(hv)::value;
-  auto work = [&](float mult, const uint4* qsb, const uint4* dsb, const uint4* tsb, int set) {
-    if constexpr (HV) compute_half(mult, qsb, dsb, tsb, set);
-    else compute(mult, qsb, dsb, tsb, set);
-  };
-  for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
-    const int m = min(kPassEntries, nent - e0);
-    for (int x = tid; x < m; x += kThreads)
-      esc[x] = (block_count(g, list[e0 + x] & 0xffff) + kKvChunk - 1) / kKvChunk;
-    __syncthreads();
-    scan_counts(esc, m, &ntl, wave, lane);
-    __syncthreads();
-    for (int x = tid; x < m; x += kThreads) {
-      const int32_t ent = list[e0 + x];
-      const int qi = ent & 0xffff;
-      const float mult = float(uint32_t(ent) >> 16);
-      const int cq = block_count(g, qi);
-      for (int sub = 0; sub * kKvChunk < cq; ++sub) {
-        tl[esc[x] + sub] = ((qi * cpb + sub) << 7) | (min(kKvChunk, cq - sub * kKvChunk) - 1);
-        tm[esc[x] + sub] = mult;
-      }
-    }
-    __syncthreads();
-    const int T = __builtin_amdgcn_readfirstlane(ntl);
-    if (T == 0) continue;
-    issue(__builtin_amdgcn_readfirstlane(tl[0]), qs0, ds0, ts0, 0);
-    wait_copies();
-    __syncthreads();
-    for (int n = 0; n < T; n += 2) {
-      const float m0 = tm[n];
-      const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
-      const float m1 = tm[min(n + 1, T - 1)];
-      if (n + 1 < T) issue(d1, qs1, ds1, ts1, 1);
-      work(m0, qs0, ds0, ts0, 0);
-      wait_copies();
-      __syncthreads();
-      if (n + 1 >= T) break;
-      if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), qs0, ds0, ts0, 0);
-      work(m1, qs1, ds1, ts1, 1);
-      wait_copies();
-      __syncthreads();
-    }
-  }
-  };
-  if (qhalf >= 0) passes(std::true_type());
-  else passes(std::false_type());
-  // query-half pairs: the second wave's partial dK^T (wave 6's in qs1, wave
-  // 7's in ds1, both free after the last barrier) is added to the first's
-  const bool own_pad = split && qhalf == 1;  // waves 6, 7: their own rows are padding
-  if (split) {
-    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(qs1)
-                                        : reinterpret_cast<float*>(ds1);
-    if (own_pad && active) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) part[(dt * 16 + jj) * 64 + lane] = acc[dt][jj];
-    }
-    __syncthreads();
-    if (qhalf == 0 && active) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] += part[(dt * 16 + jj) * 64 + lane];
-    }
-    if (own_pad) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
-    }
-  }
-  // rows of this wave's own keys; pad key rows are written as zero
-  store_rows<F16>(acc, key < cj && !own_pad ? scale : 0.f, grad + (key0 + wave * 32) * 16,
-                  l32, half);
 }
 
-// ------------------------------------------------------------------ dV, pipelined
-
-// dV with the forward kernel's software pipeline.  One workgroup per key
-// block, wave w owns keys 32w .. 32w+31 (their K fragments stay in VGPRs).
-// The 64-query sub-tiles of the query blocks whose rows list the block stream
-// through LDS, Q one sub-tile ahead of dO^T, so that while
-//   P_n = 2^(S_n log2(e)/sqrt(D) - lse log2(e) + log2(multiplicity))
-// feeds dV^T += dO^T_n P_n the matrix cores already compute
-// S_{n+1} = Q_{n+1} K^T.  32 MFMA slots per sub-tile (16 for S_{n+1}, then 16
-// for dV), the 16 exponential pairs of P_n spread over them.  Pad query rows
-// carry lse = +inf in LDS (P = 0); pad key rows are stored as zero.
+// dK and dV of one key block in one pass over the query sub-tiles that
+// selected it.  One workgroup per key block, wave w owns keys 32w .. 32w+31:
+// their K fragments stay in VGPRs, the block's V rows are staged in LDS once.
+// Each 64-query sub-tile (Q and dO rows, kappa-permuted, and the queries' lse
+// and D) is copied into LDS once, double-buffered, and every wave takes it in
+// two 32-query halves of 32 fenced MFMA slots:
+//   slots  0.. 7  S   = Q K^T    (A: Q rows, B: K fragments)
+//   slots  8..15  dP  = dO V^T   (A: dO rows, B: V rows), with the 8
+//                 exponential pairs P = 2^(S log2(e)/sqrt(D) - lse log2(e)) x
+//                 multiplicity in slots 10..17
+//   slots 16..23  dV^T += dO^T P (A: dO columns), with the 8 pairs
+//                 dS = P (dP - D) in slots 18..25
+//   slots 24..31  dK^T += Q^T dS (A: Q columns)
+// so S and dP are formed once for both gradients.  The registers of S, dP,
+// P and dS of one half, the two accumulator sets and the K fragments fit the
+// 256 of two waves per SIMD; V, the largest operand held per wave otherwise,
+// is read from LDS.  Pad query rows carry lse = +inf (P = 0) and D = 0; pad
+// keys (zero K and V rows) take the factor 0 and their rows are stored as 0.
+// Edge key blocks of 5 or 6 key groups split waves 4..7 by query halves, as
+// the separate kernels did.
 template <int NW, bool F16>
-__global__ __launch_bounds__(NW * 64) void dv_kernel(
-    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ dot,
-    const float* __restrict__ lse, const int32_t* __restrict__ tlist,
-    const int32_t* __restrict__ tcount, uint4* __restrict__ dv, unsigned int* __restrict__ queues,
-    VsaGeom g, float scale_log2) {
+__global__ __launch_bounds__(NW * 64) void dkv_kernel(
+    const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
+    const uint4* __restrict__ dout, const float* __restrict__ lse,
+    const float* __restrict__ dsum, const int32_t* __restrict__ tlist,
+    const int32_t* __restrict__ tcount, uint4* __restrict__ dk, uint4* __restrict__ dv,
+    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale) {
   constexpr int kThreads = NW * 64;
-  constexpr int kPassTiles = kPassEntries * (NW / 2);
-  // Q sub-tiles (kappa rows, the "K" role of the forward) and dO^T sub-tiles
-  // (d rows, the "V^T" role); four arrays so the compiler sees that copies in
-  // flight never alias the buffers being read
-  __shared__ __align__(16) uint4 kbuf0[kKUnits];
-  __shared__ __align__(16) uint4 kbuf1[kKUnits];
-  __shared__ __align__(16) uint4 vbuf0[kVUnits];
-  __shared__ __align__(16) uint4 vbuf1[kVUnits];
-  __shared__ __align__(16) float lbuf[2][kKvChunk];
-  __shared__ int tl[kPassTiles];
-  __shared__ float tm[kPassTiles];
-  __shared__ int esc[kPassEntries];
+  constexpr int kEntries = kPassEntries / 2;       // query blocks per pass
+  constexpr int kTiles = kEntries * (NW / 2);      // <= vol/64 sub-tiles per query block
+  constexpr int kVRows = NW * 32 * kKRow;          // the key block's V rows, padded
+  __shared__ __align__(16) uint4 vrows[kVRows];
+  __shared__ __align__(16) uint4 qs0[kQUnits];
+  __shared__ __align__(16) uint4 ds0[kQUnits];
+  __shared__ __align__(16) uint4 qs1[kQUnits];
+  __shared__ __align__(16) uint4 ds1[kQUnits];
+  __shared__ __align__(16) float lse_sh[2][kKvChunk];
+  __shared__ __align__(16) float d_sh[2][kKvChunk];
+  __shared__ int tl[kTiles];
+  __shared__ uint16_t tm[kTiles];  // multiplicity of each sub-tile's query block
+  __shared__ int esc[kEntries];
   __shared__ int ntl;
+  static_assert(kVRows * 16 + 4 * kQUnits * 16 + 4 * kKvChunk * 4 + kTiles * 6 + kEntries * 4 +
+                        64 <= 160 * 1024,
+                "the fused kernel's LDS must fit one CU");
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
-  __shared__ int64_t col_sh;   // column claimed from the queues (balanced launch)
+  __shared__ int64_t col_sh;  // column claimed from the queues (balanced launch)
   const int64_t c = queues != nullptr ? claim_row(queues, ncols, g, &col_sh)
                                       : xcd_remap(blockIdx.x, ncols);
   if (c < 0) return;
@@ -835,73 +595,182 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, half = lane / 32, l32 = lane & 31;
-  // query-half waves for edge key blocks, as in the dK kernel
   const int ngroups = (cj + 31) / 32;
   const bool split = NW == 8 && (ngroups == 5 || ngroups == 6);  // workgroup-uniform
   const int kgroup = split && wave >= 4 ? 4 + (wave & 1) : wave;
   const int qhalf = split && wave >= 4 ? (wave >> 1) & 1 : -1;   // -1: all queries
-  const int qh = qhalf > 0 ? 1 : 0;
   const int key = kgroup * 32 + l32;
   const bool active = kgroup * 32 < cj;
   const int64_t key0 = bh * g.npad + int64_t(j) * g.vol;
+  // 32-query halves of every sub-tile this wave takes (wave-uniform)
+  const int hs_lo = qhalf > 0 ? 1 : 0, hs_hi = qhalf == 0 ? 0 : 1;
 
+  // the key block's V rows (keys in order, 17-unit rows), all waves
+#pragma unroll
+  for (int x = 0; x < (kVRows / 64 + NW - 1) / NW; ++x) {
+    const int ch = wave + x * NW;
+    if (ch < kVRows / 64) {
+      const int pos = ch * 64 + lane;
+      const int row = pos / kKRow, unit = pos % kKRow;
+      wave_copy_to_lds(v + key0 * 16, uint32_t(row * 16 + (unit < 16 ? unit : 0)),
+                       vrows + ch * 64);
+    }
+  }
   ev8 kf[8];
   if (active) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) kf[s] = as_ev8(k[(key0 + key) * 16 + 2 * s + half]);
   }
-  f32x16 acc[4];
+  f32x16 accv[4], acck[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+    for (int jj = 0; jj < 16; ++jj) accv[dt][jj] = acck[dt][jj] = 0.f;
 
   const uint4* const qbase = q + bh * g.npad * 16;
-  const uint4* const tbase = dot + bh * (g.npad / kKvChunk) * kUnits;
+  const uint4* const dbase = dout + bh * g.npad * 16;
   const float* const lbase = lse + bh * g.npad;
+  const float* const dsbase = dsum + bh * g.npad;
   const int cpb = g.vol / kKvChunk;
-  constexpr int kMaxK = (kKChunks + NW - 1) / NW, kMaxV = (kVChunks + NW - 1) / NW;
-  constexpr bool kSlotCopies = kMaxK + kMaxV <= 6;
-  uint32_t koff[kMaxK], voff[kMaxV];
+  constexpr int kMaxC = (kQChunks + NW - 1) / NW;
+  uint32_t qoff[kMaxC];
 #pragma unroll
-  for (int x = 0; x < kMaxK; ++x) koff[x] = row_tile_off((wave + x * NW) * 64 + lane);
+  for (int x = 0; x < kMaxC; ++x) qoff[x] = qtile_off(min((wave + x * NW) * 64 + lane, kQUnits - 1));
+  // copies of query sub-tile d (Q and dO rows) into one buffer set
+  auto issue = [&](int d, uint4* qsb, uint4* dsb) {
+    const int64_t chunk = d >> 7;
 #pragma unroll
-  for (int x = 0; x < kMaxV; ++x) voff[x] = col_tile_off((wave + x * NW) * 64 + lane);
-  auto src_of = [](const uint4* base, int d) { return base + int64_t(d >> 7) * kUnits; };
-  auto copy_k = [&](const uint4* src, int x, uint4* dst) {
-    if (tid / 64 + x * NW < kKChunks) wave_copy_to_lds(src, koff[x], dst + (wave + x * NW) * 64);
+    for (int x = 0; x < kMaxC; ++x)
+      if (wave + x * NW < kQChunks) {
+        wave_copy_to_lds(qbase + chunk * kUnits, qoff[x], qsb + (wave + x * NW) * 64);
+        wave_copy_to_lds(dbase + chunk * kUnits, qoff[x], dsb + (wave + x * NW) * 64);
+      }
   };
-  auto copy_v = [&](const uint4* src, int x, uint4* dst) {
-    if (tid / 64 + x * NW < kVChunks) wave_copy_to_lds(src, voff[x], dst + (wave + x * NW) * 64);
+  // lse (log2 units) and D of the sub-tile's 64 queries, staged by wave 0:
+  // plain loads issued early, the LDS writes after the copies' wait
+  struct Raw { float l, d; };
+  auto raw_of = [&](int d) -> Raw {
+    if (wave != 0) return {0.f, 0.f};
+    const int64_t row = int64_t(d >> 7) * kKvChunk + lane;
+    return {lbase[row], dsbase[row]};
   };
-  auto load_k = [&](int d, uint4* dst) {
+  auto put = [&](Raw r, int d, int set) {
+    if (wave == 0) {
+      const bool ok = lane <= (d & 127);
+      lse_sh[set][lane] = ok ? r.l * kLog2e : INFINITY;
+      d_sh[set][lane] = ok ? r.d : 0.f;
+    }
+  };
+
+  // per-lane operand bases: row reads (query row l32, unit half), V row of
+  // this lane's key, and the byte offset of the transposing reads (query rows
+  // 4*half + (lane%16)/4 of a 16-query step, kappa-placed; d columns
+  // 64*((lane/16)%2) + 4*(lane%4))
+  const int qread = l32 * kQRow + half;
+  const int vread = key * kKRow + half;
+  const int trb = (4 * half + (lane & 15) / 4) * (kQRow * 16) + 128 * ((lane >> 4) & 1) +
+                  8 * (lane & 3);
+
+  // one 32-query half hs of a sub-tile held in (qsb, dsb), lse / D in set
+  auto half_tile = [&](int hs, const uint4* qsb, const uint4* dsb, int set, float mlane)
+      __attribute__((always_inline)) {
+    f32x16 s, dp;
 #pragma unroll
-    for (int x = 0; x < kMaxK; ++x) copy_k(src_of(qbase, d), x, dst);
-  };
-  auto load_v = [&](int d, uint4* dst) {
+    for (int jj = 0; jj < 16; ++jj) s[jj] = dp[jj] = 0.f;
+    uint32_t pw[2][4], dsw[2][4];
+    const int rbase = qread + hs * 32 * kQRow;
+    const char* const tbq = reinterpret_cast<const char*>(qsb) + trb + hs * 32 * (kQRow * 16);
+    const char* const tbd = reinterpret_cast<const char*>(dsb) + trb + hs * 32 * (kQRow * 16);
+    // A operand of a transposed product, 16-query step cc, d tile dt: the
+    // first read takes queries 8*half + 0..3 of the step, the second 4..7
+    // (their rows lie 8 further on: kappa swaps bits 2 and 3)
+    auto tr_op = [&](const char* b, int cc, int dt) -> ev8 {
+      const char* p = b + cc * 16 * (kQRow * 16) + 32 * dt;
+      const v4i16 lo = lds_read_tr16(p);
+      const v4i16 hi = lds_read_tr16(p + 8 * (kQRow * 16));
+      return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // A operand of slot i, read 2 slots ahead (the V operands of slots 8..15
+    // are read in their own slot: a longer lead spills at 256 registers)
+    ev8 opa[3];
+    auto read_op = [&](int i) {
+      if (i < 8) {
+        opa[i % 3] = as_ev8(qsb[rbase + 2 * i]);
+      } else if (i < 16) {
+        opa[i % 3] = as_ev8(dsb[rbase + 2 * (i - 8)]);
+      } else if (i < 24) {
+        const int x = i - 16;
+        opa[i % 3] = tr_op(tbd, x / 4, x % 4);
+      } else {
+        const int x = i - 24;
+        opa[i % 3] = tr_op(tbq, x / 4, x % 4);
+      }
+    };
+    // pair e holds registers 2e, 2e+1: queries 32hs + 16(e/4) + 8*half +
+    // 2(e%4) and the next one; lse of the pairs two ahead of the
+    // exponentials, D two ahead of the dS pairs
+    float2 lq[3], dq2[3];
+    auto q_of = [&](int e) { return 32 * hs + 16 * (e / 4) + 8 * half + 2 * (e % 4); };
+    auto read_l = [&](int e) {
+      lq[e % 3] = *reinterpret_cast<const float2*>(&lse_sh[set][q_of(e)]);
+    };
+    auto read_d = [&](int e) {
+      dq2[e % 3] = *reinterpret_cast<const float2*>(&d_sh[set][q_of(e)]);
+    };
 #pragma unroll
-    for (int x = 0; x < kMaxV; ++x) copy_v(src_of(tbase, d), x, dst);
+    for (int i = 0; i < 2; ++i) read_op(i);
+    slot_fence();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (i + 2 < 32) read_op(i + 2);
+      if (i == 6) read_l(0);
+      if (i == 7) read_l(1);
+      if (i == 14) read_d(0);
+      if (i == 15) read_d(1);
+      if (i < 8) {
+        s = mfma_32x32x16<F16>(opa[i % 3], kf[i], s);
+      } else if (i < 16) {
+        dp = mfma_32x32x16<F16>(opa[i % 3], as_ev8(vrows[vread + 2 * (i - 8)]), dp);
+      } else if (i < 24) {
+        const int x = i - 16, cc = x / 4, dt = x % 4;
+        const ev8 b = __builtin_bit_cast(ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2],
+                                                         pw[cc][3]));
+        accv[dt] = mfma_32x32x16<F16>(opa[i % 3], b, accv[dt]);
+      } else {
+        const int x = i - 24, cc = x / 4, dt = x % 4;
+        const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
+                                                         dsw[cc][3]));
+        acck[dt] = mfma_32x32x16<F16>(opa[i % 3], b, acck[dt]);
+      }
+      if (i >= 10 && i < 18) {  // exponential pair e: P, kept in fp32 in s
+        const int e = i - 10, jj = 2 * e;
+        const float2 l = lq[e % 3];
+        if (e + 2 < 8) read_l(e + 2);
+        s[jj] = __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -l.x)) * mlane;
+        s[jj + 1] = __builtin_amdgcn_exp2f(fmaf(s[jj + 1], scale_log2, -l.y)) * mlane;
+        pw[e / 4][e % 4] = pack2<F16>(s[jj], s[jj + 1]);
+        pin_v(pw[e / 4][e % 4]);
+      }
+      if (i >= 18 && i < 26) {  // dS pair e
+        const int e = i - 18, jj = 2 * e;
+        const float2 dd = dq2[e % 3];
+        if (e + 2 < 8) read_d(e + 2);
+        dsw[e / 4][e % 4] = pack2<F16>(s[jj] * (dp[jj] - dd.x), s[jj + 1] * (dp[jj + 1] - dd.y));
+        pin_v(dsw[e / 4][e % 4]);
+      }
+      slot_fence();
+    }
   };
-  // lse of the 64 query rows of sub-tile d, staged by wave 0: a plain load
-  // issued early, the LDS write late
-  auto lse_raw = [&](int d) { return wave == 0 ? lbase[int64_t(d >> 7) * kKvChunk + lane] : 0.f; };
-  auto lse_put = [&](float raw, int d, float mult, float* dst) {
-    if (wave == 0) dst[lane] = lane <= (d & 127) ? raw * kLog2e - __log2f(mult) : INFINITY;
+  auto work = [&](float mult, const uint4* qsb, const uint4* dsb, int set) {
+    if (!active) return;
+    const float mlane = key < cj ? mult : 0.f;
+    for (int hs = hs_lo; hs <= hs_hi; ++hs) half_tile(hs, qsb, dsb, set, mlane);
   };
-  const int kread = l32 * kKRow + half;
-  const int vread = l32 * kVRow + half;
-  // operand bases of a query-half wave: queries 32qh .. 32qh+31 of each sub-tile
-  const int kread_h = kread + qh * 32 * kKRow, vread_h = vread + 4 * qh;
 
   const int nent = tcount[c];
   const int32_t* list = tlist + c * int64_t(g.nb);
-  // the passes are compiled twice (full and query-half waves), each with its
-  // own register allocation
-  auto passes = [&](auto hv) __attribute__((always_inline)) {
-  constexpr bool HV = decltype(hv)::value;
-  f32x16 sa[2], sb[2];
-  for (int e0 = 0; e0 < nent; e0 += kPassEntries) {
-    const int m = min(kPassEntries, nent - e0);
+  for (int e0 = 0; e0 < nent; e0 += kEntries) {
+    const int m = min(kEntries, nent - e0);
     for (int x = tid; x < m; x += kThreads)
       esc[x] = (block_count(g, list[e0 + x] & 0xffff) + kKvChunk - 1) / kKvChunk;
     __syncthreads();
@@ -910,258 +779,82 @@ __global__ __launch_bounds__(NW * 64) void dv_kernel(
     for (int x = tid; x < m; x += kThreads) {
       const int32_t ent = list[e0 + x];
       const int qi = ent & 0xffff;
-      const float mult = float(uint32_t(ent) >> 16);
       const int cq = block_count(g, qi);
       for (int sub = 0; sub * kKvChunk < cq; ++sub) {
         tl[esc[x] + sub] = ((qi * cpb + sub) << 7) | (min(kKvChunk, cq - sub * kKvChunk) - 1);
-        tm[esc[x] + sub] = mult;
+        tm[esc[x] + sub] = uint16_t(uint32_t(ent) >> 16);
       }
     }
     __syncthreads();
     const int T = __builtin_amdgcn_readfirstlane(ntl);
     if (T == 0) continue;
-    // descriptor / multiplicity of sub-tile n; past the end the last one
-    // repeats (its copies land in buffers that are not read again)
-    auto desc_at = [&](int n) { return tl[min(n, T - 1)]; };
-    auto mult_at = [&](int n) { return tm[min(n, T - 1)]; };
-
-    int n = 0;
-    int d0 = __builtin_amdgcn_readfirstlane(desc_at(0));
-    int d1 = __builtin_amdgcn_readfirstlane(desc_at(1));
-    int d2 = __builtin_amdgcn_readfirstlane(desc_at(2));
-    load_k(d0, kbuf0);
-    load_v(d0, vbuf0);
-    load_k(d1, kbuf1);
     {
-      const float raw = lse_raw(d0);
-      wait_copies();
-      lse_put(raw, d0, mult_at(0), lbuf[0]);
+      const int d0 = __builtin_amdgcn_readfirstlane(tl[0]);
+      issue(d0, qs0, ds0);
+      const Raw r0 = raw_of(d0);
+      wait_copies();  // also the V rows of the first pass
+      put(r0, d0, 0);
     }
     __syncthreads();
-    if (active && !HV) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) sa[mt][jj] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          sa[mt] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread + mt * 32 * kKRow + 2 * s]), kf[s],
-                                      sa[mt]);
-    } else if (active) {
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) sa[0][jj] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        sa[0] = mfma_32x32x16<F16>(as_ev8(kbuf0[kread_h + 2 * s]), kf[s], sa[0]);
-    }
-    // the first step copies Q_2 into kbuf0: every wave must be done with Q_0
-    __syncthreads();
-
-    // Finish sub-tile n (S_n in `cur`, lse_n in lcur) and compute S_{n+1}
-    // into `nxt`.  kn: Q_{n+1}; kw receives Q_{n+2}; vn: dO^T_n; vw receives
-    // dO^T_{n+1}; lnx receives lse_{n+1}.
-    auto step = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const uint4* kn, uint4* kw,
-                    const uint4* vn, uint4* vw, const float* lcur, float* lnx) {
-      const uint4* const sk = src_of(qbase, d2);
-      const uint4* const sv = src_of(tbase, d1);
-      const int d3 = desc_at(n + 3);  // LDS read; made uniform after the barrier
-      const float m1 = mult_at(n + 1);
-      const float raw = lse_raw(d1);
-      if constexpr (!kSlotCopies) {
-        load_k(d2, kw);
-        load_v(d1, vw);
+    for (int n = 0; n < T; n += 2) {
+      const float m0 = float(tm[n]);
+      const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
+      const float m1 = float(tm[min(n + 1, T - 1)]);
+      Raw r1 = {0.f, 0.f};
+      if (n + 1 < T) {
+        issue(d1, qs1, ds1);
+        r1 = raw_of(d1);
       }
-      if (HV && active) {
-        // query-half wave: one 32-query S tile, 8 + 8 MFMA slots
-        uint32_t pw[2][4];
-        ev8 opk[8], opv[8];
-        float4 lq[2][2];
-        auto read_k = [&](int u) { opk[u % 8] = as_ev8(kn[kread_h + 2 * u]); };
-        auto read_v = [&](int w) {
-          opv[w % 8] = as_ev8(vn[vread_h + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
-        };
-        auto read_l = [&](int cc) {  // queries 32qh + 16cc + 8*half + 0..7
-          lq[cc][0] = *reinterpret_cast<const float4*>(lcur + 32 * qh + 16 * cc + 8 * half);
-          lq[cc][1] = *reinterpret_cast<const float4*>(lcur + 32 * qh + 16 * cc + 8 * half + 4);
-        };
-        read_l(0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) read_k(u);
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) nxt[0][jj] = 0.f;
-        slot_fence();
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if constexpr (kSlotCopies) {
-#pragma unroll
-            for (int x = 0; x < kMaxK; ++x)
-              if (u == 1 + (x * 8) / kMaxK) copy_k(sk, x, kw);
-#pragma unroll
-            for (int x = 0; x < kMaxV; ++x)
-              if (u == 9 + (x * 8) / kMaxV) copy_v(sv, x, vw);
-          }
-          if (u == 1) read_l(1);
-          if (u < 8) {
-            if (u % 4 == 0) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) {
-                if (u + 4 < 8) read_k(u + 4 + x);
-                else read_v(x);
-              }
-            }
-            nxt[0] = mfma_32x32x16<F16>(opk[u % 8], kf[u], nxt[0]);
-            // exponential pair u: queries t, t+1 of step u/4
-            const int cc = u / 4, t = 2 * (u % 4);
-            const float4 l4 = lq[cc][t / 4];
-            const float la = (t % 4 == 0) ? l4.x : l4.z;
-            const float lb = (t % 4 == 0) ? l4.y : l4.w;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[0][8 * cc + t], scale_log2, -la));
-            const float p1 =
-                __builtin_amdgcn_exp2f(fmaf(cur[0][8 * cc + t + 1], scale_log2, -lb));
-            pw[cc][t / 2] = pack2<F16>(p0, p1);
-            pin_v(pw[cc][t / 2]);
-          } else {
-            const int w = u - 8, cc = w / 4, dt = w % 4;
-            if (w == 0) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) read_v(4 + x);
-            }
-            const ev8 pb = __builtin_bit_cast(
-                ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
-            acc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, acc[dt]);
-          }
-          slot_fence();
-        }
-      } else if (!HV && active) {
-        uint32_t pw[4][4];  // bf16 pairs of P: B operands of the 4 dV steps
-        ev8 opk[8], opv[8];
-        float4 lq[4][2];    // lse of the 8 queries of each dV step
-        auto read_k = [&](int u) {
-          opk[u % 8] = as_ev8(kn[kread + (u % 2) * 32 * kKRow + 2 * (u / 2)]);
-        };
-        auto read_v = [&](int w) {
-          opv[w % 8] = as_ev8(vn[vread + (w % 4) * 32 * kVRow + 2 * (w / 4)]);
-        };
-        // queries of step cc: 16cc + 8*half + 0..7 (kappa-staged rows)
-        auto read_l = [&](int cc) {
-          lq[cc][0] = *reinterpret_cast<const float4*>(lcur + 16 * cc + 8 * half);
-          lq[cc][1] = *reinterpret_cast<const float4*>(lcur + 16 * cc + 8 * half + 4);
-        };
-        read_l(0);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) read_k(u);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) nxt[mt][jj] = 0.f;
-        slot_fence();
-#pragma unroll
-        for (int u = 0; u < 32; ++u) {
-          if constexpr (kSlotCopies) {
-#pragma unroll
-            for (int x = 0; x < kMaxK; ++x)
-              if (u == 1 + (x * 16) / kMaxK) copy_k(sk, x, kw);
-#pragma unroll
-            for (int x = 0; x < kMaxV; ++x)
-              if (u == 17 + (x * 16) / kMaxV) copy_v(sv, x, vw);
-          }
-          // lse of dV step cc read two steps' worth of slots ahead of its pairs
-          if (u == 2) read_l(1);
-          if (u == 10) read_l(2);
-          if (u == 18) read_l(3);
-          if (u < 16) {
-            const int s = u / 2, mt = u % 2;
-            if (u % 4 == 0) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) {
-                if (u + 4 < 16) read_k(u + 4 + x);
-                else read_v(x);
-              }
-            }
-            nxt[mt] = mfma_32x32x16<F16>(opk[u % 8], kf[s], nxt[mt]);
-          } else {
-            const int w = u - 16, cc = w / 4, dt = w % 4;
-            if (w % 4 == 0 && w + 4 < 16) {
-#pragma unroll
-              for (int x = 0; x < 4; ++x) read_v(w + 4 + x);
-            }
-            const ev8 pb = __builtin_bit_cast(
-                ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2], pw[cc][3]));
-            acc[dt] = mfma_32x32x16<F16>(opv[w % 8], pb, acc[dt]);
-          }
-          // exponential pair e (queries 2e%8, +1 of step e/4): pairs 0..11 in
-          // even slots 0..22, pairs 12..15 in slots 24..27
-          const int e = (u < 24) ? ((u % 2 == 0) ? u / 2 : -1) : ((u < 28) ? u - 12 : -1);
-          if (e >= 0) {
-            const int cc = e / 4, t = 2 * (e % 4);
-            const float4 l4 = lq[cc][t / 4];
-            const float la = (t % 4 == 0) ? l4.x : l4.z;
-            const float lb = (t % 4 == 0) ? l4.y : l4.w;
-            const float p0 =
-                __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t], scale_log2, -la));
-            const float p1 =
-                __builtin_amdgcn_exp2f(fmaf(cur[cc / 2][8 * (cc % 2) + t + 1], scale_log2, -lb));
-            pw[cc][t / 2] = pack2<F16>(p0, p1);
-            pin_v(pw[cc][t / 2]);
-          }
-          slot_fence();
-        }
-      } else if constexpr (kSlotCopies) {
-#pragma unroll
-        for (int x = 0; x < kMaxK; ++x) copy_k(sk, x, kw);
-#pragma unroll
-        for (int x = 0; x < kMaxV; ++x) copy_v(sv, x, vw);
-      }
+      work(m0, qs0, ds0, 0);
       wait_copies();
-      lse_put(raw, d1, m1, lnx);
+      if (n + 1 < T) put(r1, d1, 1);
       __syncthreads();
-      ++n;
-      d0 = d1;
-      d1 = d2;
-      d2 = __builtin_amdgcn_readfirstlane(d3);
-    };
-
-    while (true) {
-      step(sa, sb, kbuf1, kbuf0, vbuf0, vbuf1, lbuf[0], lbuf[1]);
-      if (n >= T) break;
-      step(sb, sa, kbuf0, kbuf1, vbuf1, vbuf0, lbuf[1], lbuf[0]);
-      if (n >= T) break;
+      if (n + 1 >= T) break;
+      const int d2 = __builtin_amdgcn_readfirstlane(tl[min(n + 2, T - 1)]);
+      Raw r2 = {0.f, 0.f};
+      if (n + 2 < T) {
+        issue(d2, qs0, ds0);
+        r2 = raw_of(d2);
+      }
+      work(m1, qs1, ds1, 1);
+      wait_copies();
+      if (n + 2 < T) put(r2, d2, 0);
+      __syncthreads();
     }
   }
-  };
-  if (qhalf >= 0) passes(std::true_type());
-  else passes(std::false_type());
-  // query-half pairs: the second wave's partial dV^T (wave 6's in kbuf1, wave
-  // 7's in vbuf1, both free after the last barrier) is added to the first's
+  wait_copies();  // the V rows, when no pass ran
+  __syncthreads();
+  // query-half pairs: the second wave's partial dV^T and dK^T (wave 6's in
+  // qs0/qs1, wave 7's in ds0/ds1, free after the last barrier) are added to
+  // the first's
   const bool own_pad = split && qhalf == 1;  // waves 6, 7: their own rows are padding
   if (split) {
-    float* const part = (wave & 1) == 0 ? reinterpret_cast<float*>(kbuf1)
-                                        : reinterpret_cast<float*>(vbuf1);
+    float* const pv = reinterpret_cast<float*>((wave & 1) == 0 ? qs0 : ds0);
+    float* const pk = reinterpret_cast<float*>((wave & 1) == 0 ? qs1 : ds1);
     if (own_pad && active) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) part[(dt * 16 + jj) * 64 + lane] = acc[dt][jj];
+        for (int jj = 0; jj < 16; ++jj) {
+          pv[(dt * 16 + jj) * 64 + lane] = accv[dt][jj];
+          pk[(dt * 16 + jj) * 64 + lane] = acck[dt][jj];
+        }
     }
     __syncthreads();
     if (qhalf == 0 && active) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] += part[(dt * 16 + jj) * 64 + lane];
-    }
-    if (own_pad) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[dt][jj] = 0.f;
+        for (int jj = 0; jj < 16; ++jj) {
+          accv[dt][jj] += pv[(dt * 16 + jj) * 64 + lane];
+          acck[dt][jj] += pk[(dt * 16 + jj) * 64 + lane];
+        }
     }
   }
-  // rows of this wave's own keys; pad key rows are written as zero
-  store_rows<F16>(acc, key < cj && !own_pad ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32,
-                  half);
+  // rows of this wave's own keys; pad key rows (and waves 6, 7) write zeros
+  const bool keep = key < cj && !own_pad;
+  store_rows_perm<F16>(accv, keep ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32, half);
+  store_rows_perm<F16>(acck, keep ? scale : 0.f, dk + (key0 + wave * 32) * 16, l32, half);
 }
 
 template <int NW, bool F16>
@@ -1186,16 +879,11 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
                      a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), a.queues, g, scale_log2,
                      scale);
   if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dv_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((dkv_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.dot), a.lse, a.tlist, a.tcount,
-                     static_cast<uint4*>(a.dv), a.queues, g, scale_log2);
-  if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dk_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
-                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.qt),
-                     static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.tlist, a.tcount,
-                     static_cast<uint4*>(a.dk), a.queues, g, scale_log2, scale);
+                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse,
+                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk),
+                     static_cast<uint4*>(a.dv), a.queues, g, scale_log2, scale);
   return hipGetLastError();
 }
 
@@ -1220,13 +908,9 @@ hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
                        a.dsum, blocked_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned chunks = unsigned(blocked_rows / kKvChunk);
-  const void* srcs[3] = {a.k, a.q, a.dout};
-  void* dsts[3] = {a.kt, a.qt, a.dot};
-  for (int t = 0; t < 3; ++t) {
-    hipLaunchKernelGGL(transpose_kernel, dim3(chunks), dim3(256), 0, s,
-                       static_cast<const uint4*>(srcs[t]), static_cast<uint4*>(dsts[t]));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  hipLaunchKernelGGL(transpose_kernel, dim3(chunks), dim3(256), 0, s,
+                     static_cast<const uint4*>(a.k), static_cast<uint4*>(a.kt));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(tmap_kernel, dim3(unsigned((int64_t(g.batch) * g.heads * g.nb + 3) / 4)),
                      dim3(256), 0, s, a.row_ptr, a.col, a.uniform_k, a.nnz, a.tlist, a.tcount, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
