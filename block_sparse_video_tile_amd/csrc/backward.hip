@@ -497,19 +497,23 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 // ------------------------------------------------------------------ dK and dV together
 
 // Query sub-tiles of the fused dK/dV kernel: 64 query rows, kappa-permuted,
-// of 16 data units and 2 pad units (288 B).  They are read as rows
-// (ds_read_b128: the A operands of S = Q K^T and dP = dO V^T) and as columns
-// (ds_read_b64_tr_b16: the A operands of dK^T += Q^T dS and dV^T += dO^T P);
-// with 288-byte rows both kinds of read fall on distinct banks.
-constexpr int kQRow = 18;
-constexpr int kQUnits = 64 * kQRow;    // 1152 16-byte units (18 KB)
-constexpr int kQChunks = kQUnits / 64;  // 18 wave-loads of 1 KB
+// of 16 data units and 1 pad unit (272 B), as the forward's K tiles.  They
+// are read as rows (ds_read_b128: the A operands of S = Q K^T and
+// dP = dO V^T; 8 consecutive rows at the same unit fall on distinct banks)
+// and as columns (ds_read_b64_tr_b16: the A operands of dK^T += Q^T dS and
+// dV^T += dO^T P).  In a column read the 16 lanes of a group address 4 rows
+// (68 dwords apart) and 4 segments of 8 bytes; the segments are taken at byte
+// offsets 0, 8, 64, 72 of a 128-byte window, so that the 16 two-dword spans
+// 4e + {0, 2, 16, 18} (mod 32) cover every bank once.
+constexpr int kQRow = kKRow;
+constexpr int kQUnits = 64 * kQRow;    // 1088 16-byte units (17 KB)
+constexpr int kQChunks = kQUnits / 64;  // 17 wave-loads of 1 KB
 
 // Source unit (within a 64-token sub-tile) of LDS position pos of a query
-// sub-tile; a pad unit re-reads a unit of its row.
+// sub-tile; the pad unit re-reads unit 0 of its row.
 __device__ inline uint32_t qtile_off(int pos) {
   const int row = pos / kQRow, unit = pos % kQRow;
-  return kappa(row) * 16 + (unit < 16 ? unit : unit - 16);
+  return kappa(row) * 16 + (unit < 16 ? unit : 0);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -522,9 +526,9 @@ __device__ inline v4i16 lds_read_tr16(const void* p) {
 }
 
 // Store a 32 x 128 accumulator tile whose MFMA row m of tile dt holds column
-// d = 64(m/16) + 16dt + m%16 (the order the transposing reads produce), times
-// `mul`, as element rows: register j of lane l holds key l%32 and
-// d = 64(j/8) + 16dt + 8((j/4)%2) + 4(l/32) + j%4.
+// d = 64(m/16) + 8dt + 32((m%16)/8) + 4((m/4)%2) + m%4 (the order the
+// transposing reads produce), times `mul`, as element rows: register j of
+// lane l holds key l%32 and d = 64(j/8) + 8dt + 32((j/4)%2) + 4(l/32) + j%4.
 template <bool F16>
 __device__ inline void store_rows_perm(const f32x16 (&acc)[4], float mul, uint4* rows_base,
                                        int l32, int half) {
@@ -533,7 +537,7 @@ __device__ inline void store_rows_perm(const f32x16 (&acc)[4], float mul, uint4*
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int d0 = 64 * (jj / 2) + 16 * dt + 8 * (jj % 2) + 4 * half;
+      const int d0 = 64 * (jj / 2) + 8 * dt + 32 * (jj % 2) + 4 * half;
       dst[d0 / 4] = make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
                                pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
     }
@@ -663,13 +667,13 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   };
 
   // per-lane operand bases: row reads (query row l32, unit half), V row of
-  // this lane's key, and the byte offset of the transposing reads (query rows
-  // 4*half + (lane%16)/4 of a 16-query step, kappa-placed; d columns
-  // 64*((lane/16)%2) + 4*(lane%4))
+  // this lane's key, and the byte offset of the transposing reads (query row
+  // 4*half + (lane%16)/4 of a 16-query step, kappa-placed; the segment of d
+  // columns 64*((lane/16)%2) + 32*((lane%4)/2) + 4*(lane%2) .. +3, plus 8dt)
   const int qread = l32 * kQRow + half;
   const int vread = key * kKRow + half;
   const int trb = (4 * half + (lane & 15) / 4) * (kQRow * 16) + 128 * ((lane >> 4) & 1) +
-                  8 * (lane & 3);
+                  64 * ((lane & 3) >> 1) + 8 * (lane & 1);
 
   // one 32-query half hs of a sub-tile held in (qsb, dsb), lse / D in set
   auto half_tile = [&](int hs, const uint4* qsb, const uint4* dsb, int set, float mlane)
@@ -685,14 +689,14 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     // first read takes queries 8*half + 0..3 of the step, the second 4..7
     // (their rows lie 8 further on: kappa swaps bits 2 and 3)
     auto tr_op = [&](const char* b, int cc, int dt) -> ev8 {
-      const char* p = b + cc * 16 * (kQRow * 16) + 32 * dt;
+      const char* p = b + cc * 16 * (kQRow * 16) + 16 * dt;
       const v4i16 lo = lds_read_tr16(p);
       const v4i16 hi = lds_read_tr16(p + 8 * (kQRow * 16));
       return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // A operand of slot i, read 2 slots ahead (the V operands of slots 8..15
-    // are read in their own slot: a longer lead spills at 256 registers)
-    ev8 opa[3];
+    // A operand of slot i, read 2 slots ahead, and the V operand of slots
+    // 8..15 one slot ahead (longer leads spill at 256 registers)
+    ev8 opa[3], opv[2];
     auto read_op = [&](int i) {
       if (i < 8) {
         opa[i % 3] = as_ev8(qsb[rbase + 2 * i]);
@@ -723,6 +727,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       if (i + 2 < 32) read_op(i + 2);
+      if (i >= 7 && i < 15) opv[(i + 1) % 2] = as_ev8(vrows[vread + 2 * (i + 1 - 8)]);
       if (i == 6) read_l(0);
       if (i == 7) read_l(1);
       if (i == 14) read_d(0);
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
       if (i < 8) {
         s = mfma_32x32x16<F16>(opa[i % 3], kf[i], s);
       } else if (i < 16) {
-        dp = mfma_32x32x16<F16>(opa[i % 3], as_ev8(vrows[vread + 2 * (i - 8)]), dp);
+        dp = mfma_32x32x16<F16>(opa[i % 3], opv[i % 2], dp);
       } else if (i < 24) {
         const int x = i - 16, cc = x / 4, dt = x % 4;
         const ev8 b = __builtin_bit_cast(ev8, make_uint4(pw[cc][0], pw[cc][1], pw[cc][2],
