@@ -12,15 +12,14 @@
 //
 // Kernels
 //   rowdot    D_q for every blocked row.
-//   transpose blocked token-major K -> d-major 64-token chunks (the layout
-//             the forward uses for V^T), the A operand of dQ^T += K^T dS^T.
 //   tmap      per key block j, the query blocks i whose row lists j, with the
 //             multiplicity, ascending i (one thread per column, no atomics).
 //   dq        one workgroup per query block, wave w owns 32 query rows:
 //             S^T = K Q^T and dP^T = V dO^T with the key rows of K and V
 //             staged kappa-permuted, so dS^T comes out in exactly the register
 //             layout of the B operand of dQ^T += K^T dS^T (the forward's PV
-//             arrangement with K^T in place of V^T).
+//             arrangement with K^T in place of V^T); K^T is read from the K
+//             rows with the transposing LDS read.
 //   dkv       one workgroup per key block, wave w owns 32 keys, streaming the
 //             64-query sub-tiles of the query blocks that selected the block:
 //             S = Q K^T and dP = dO V^T with the query rows staged
@@ -84,32 +83,6 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint4* __restrict__ o
   if (row < rows && unit == 0) dsum[row] = acc;
 }
 
-// Blocked token-major [B,NH,Npad,D] -> [B,NH,Npad/64,D,64]: one workgroup per
-// 64-token chunk, transposed through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint4* __restrict__ x,
-                                                        uint4* __restrict__ xt) {
-  __shared__ __align__(16) uint16_t t[64][kHeadDim + 8];
-  const int64_t c = blockIdx.x;  // chunk over B*NH*Npad/64
-  const uint4* src = x + c * 64 * 16;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int idx = threadIdx.x + p * 256;
-    *reinterpret_cast<uint4*>(&t[idx / 16][(idx % 16) * 8]) = src[idx];
-  }
-  __syncthreads();
-  uint4* dst = xt + c * kHeadDim * 8;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int idx = threadIdx.x + p * 256;
-    const int d = idx % kHeadDim, ku = idx / kHeadDim;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = uint32_t(t[ku * 8 + 2 * e][d]) | (uint32_t(t[ku * 8 + 2 * e + 1][d]) << 16);
-    dst[d * 8 + ku] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
 // Bounds of CSR row r, sanitised exactly as the forward does.
 __device__ inline void row_bounds(const int32_t* row_ptr, int uniform_k, int64_t nnz, int64_t r,
                                   int64_t& beg, int64_t& end) {
@@ -155,50 +128,27 @@ __global__ __launch_bounds__(256) void tmap_kernel(const int32_t* __restrict__ r
   if (lane == 0) tcount[task] = cnt;
 }
 
-// Per-lane copy offsets (16-byte units inside one 64-token sub-tile) of the
-// padded LDS layouts: "row" tiles (64 token rows, kappa-permuted, 17 units
-// per row) and "column" tiles (128 d rows of 64 tokens, 9 units per row).
-// Positions past the buffer are clamped; their copies are not issued.
+// Per-lane copy offset (16-byte units inside one 64-token sub-tile) of the
+// padded row tiles: 64 token rows, kappa-permuted, 17 units per row (the pad
+// unit re-reads unit 0).  Positions past the buffer are clamped; their copies
+// are not issued.
 __device__ inline uint32_t row_tile_off(int pos) {
   pos = min(pos, kKUnits - 1);
   const int row = pos / kKRow, unit = pos % kKRow;
   return kappa(row) * 16 + (unit < 16 ? unit : 0);
 }
-__device__ inline uint32_t col_tile_off(int pos) {
-  pos = min(pos, kVUnits - 1);
-  const int row = pos / kVRow, unit = pos % kVRow;
-  return row * 8 + (unit < 8 ? unit : 0);
-}
 
-// Copy one sub-tile with all NW waves of the workgroup.
-template <int NW, int CHUNKS>
-__device__ inline void copy_tile(const uint4* src, uint4* dst, int wave, int lane, bool row_tile) {
+// Copy one row tile with all NW waves of the workgroup.
+template <int NW>
+__device__ inline void copy_tile(const uint4* src, uint4* dst, int wave, int lane) {
 #pragma unroll
-  for (int x = 0; x < (CHUNKS + NW - 1) / NW; ++x) {
+  for (int x = 0; x < (kKChunks + NW - 1) / NW; ++x) {
     const int c = wave + x * NW;
-    if (c < CHUNKS) {
-      const int pos = c * 64 + lane;
-      wave_copy_to_lds(src, row_tile ? row_tile_off(pos) : col_tile_off(pos), dst + c * 64);
-    }
+    if (c < kKChunks) wave_copy_to_lds(src, row_tile_off(c * 64 + lane), dst + c * 64);
   }
 }
 
 __device__ inline void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Store one wave's 32 x 128 accumulator tile (acc[dt] register j holds row
-// l%32, column 32dt + 8(j/4) + 4(l/32) + j%4) times `mul` as element rows.
-template <bool F16>
-__device__ inline void store_rows(const f32x16 (&acc)[4], float mul, uint4* rows_base, int l32,
-                                  int half) {
-  uint2* dst = reinterpret_cast<uint2*>(rows_base + int64_t(l32) * 16);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      dst[(dt * 32 + 8 * jj + 4 * half) / 4] =
-          make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
-                     pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
-}
 
 // ------------------------------------------------------------------ work lists
 
@@ -249,24 +199,74 @@ __global__ void bwd_queue_reset_kernel(unsigned int* queues) {
   if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i%4 of the 8-byte segments addressed by lanes 4e + i/4, e = 0..3.
+__device__ inline v4i16 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+}
+
+// Store a 32 x 128 accumulator tile whose MFMA row m of tile dt holds column
+// d = 64(m/16) + 8dt + 32((m%16)/8) + 4((m/4)%2) + m%4 (the order the
+// transposing reads produce), times `mul`, as element rows: register j of
+// lane l holds key l%32 and d = 64(j/8) + 8dt + 32((j/4)%2) + 4(l/32) + j%4.
+template <bool F16>
+__device__ inline void store_rows_perm(const f32x16 (&acc)[4], float mul, uint4* rows_base,
+                                       int l32, int half) {
+  uint2* dst = reinterpret_cast<uint2*>(rows_base + int64_t(l32) * 16);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d0 = 64 * (jj / 2) + 8 * dt + 32 * (jj % 2) + 4 * half;
+      dst[d0 / 4] = make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
+                               pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
+    }
+}
+
+// Column operand of a kappa-permuted 64-row tile of 17-unit rows (the K
+// tiles of dq, the Q and dO tiles of dkv), read with two transposing reads:
+// lane l gets the 8 consecutive rows' (keys' or queries') elements of one
+// column for the 16-row step starting at the tile byte offset `base`; `trb`
+// is the lane's part of the address (tr_lane_base), dt selects the d tile.
+// Within a group of 16 lanes the reads address 4 rows (68 dwords apart) and 4
+// segments of 8 bytes at byte offsets 0, 8, 64, 72 of a 128-byte window, so
+// the 16 two-dword spans 4e + {0, 2, 16, 18} (mod 32) cover every bank once.
+// MFMA row m of the product then holds column
+// d = 64(m/16) + 8dt + 32((m%16)/8) + 4((m/4)%2) + m%4 (store_rows_perm).
+__device__ inline int tr_lane_base(int lane) {
+  const int half = lane / 32;
+  return (4 * half + (lane & 15) / 4) * (kKRow * 16) + 128 * ((lane >> 4) & 1) +
+         64 * ((lane & 3) >> 1) + 8 * (lane & 1);
+}
+// The operand at tile byte offset trb + base + 16dt: the first read takes rows
+// 8*half + 0..3 of the step, the second 4..7 (kappa places them 8 rows on).
+__device__ inline ev8 tr_operand(const uint4* tile, int off) {
+  const char* p = reinterpret_cast<const char*>(tile) + off;
+  const v4i16 lo = lds_read_tr16(p);
+  const v4i16 hi = lds_read_tr16(p + 8 * (kKRow * 16));
+  return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // ------------------------------------------------------------------ dQ
 
 template <int NW, bool F16>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
-    const uint4* __restrict__ kt, const uint4* __restrict__ dout, const float* __restrict__ lse,
+    const uint4* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, int uniform_k, int64_t nnz, uint4* __restrict__ dq,
     unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale) {
   constexpr int kThreads = NW * 64;
   constexpr int kPassTiles = kPassEntries * (NW / 2);  // <= vol/64 sub-tiles per block
-  // two buffer sets: K rows, V rows (kappa, padded), K^T (d-major, padded)
+  // two buffer sets: K rows and V rows (kappa, padded); K^T is read from the
+  // K rows with the transposing read
   __shared__ __align__(16) uint4 ks0[kKUnits];
   __shared__ __align__(16) uint4 vs0[kKUnits];
-  __shared__ __align__(16) uint4 kts0[kVUnits];
   __shared__ __align__(16) uint4 ks1[kKUnits];
   __shared__ __align__(16) uint4 vs1[kKUnits];
-  __shared__ __align__(16) uint4 kts1[kVUnits];
   __shared__ int tl[kPassTiles];
   __shared__ int esc[kPassEntries];
   __shared__ int ntl;
@@ -319,20 +319,18 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 
   const uint4* const kbase = k + bh * g.npad * 16;
   const uint4* const vbase = v + bh * g.npad * 16;
-  const uint4* const ktbase = kt + bh * (g.npad / kKvChunk) * kUnits;
   const int cpb = g.vol / kKvChunk;
-  const int kread = l32 * kKRow + half, ktread = l32 * kVRow + half;
+  const int kread = l32 * kKRow + half, trb = tr_lane_base(lane);
 
-  auto issue = [&](int d, uint4* ksb, uint4* vsb, uint4* ktsb) {
+  auto issue = [&](int d, uint4* ksb, uint4* vsb) {
     const int64_t chunk = d >> 7;
-    copy_tile<NW, kKChunks>(kbase + chunk * kUnits, ksb, wave, lane, true);
-    copy_tile<NW, kKChunks>(vbase + chunk * kUnits, vsb, wave, lane, true);
-    copy_tile<NW, kVChunks>(ktbase + chunk * kUnits, ktsb, wave, lane, false);
+    copy_tile<NW>(kbase + chunk * kUnits, ksb, wave, lane);
+    copy_tile<NW>(vbase + chunk * kUnits, vsb, wave, lane);
   };
   // key-half wave: one 32-key tile (keys 32kh..) of S^T and dP^T, dQ^T from
   // the matching two 16-key steps
-  const int kread_h = kread + kh * 32 * kKRow, ktread_h = ktread + 4 * kh;
-  auto compute_half = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
+  const int kread_h = kread + kh * 32 * kKRow, trb_h = trb + kh * 32 * (kKRow * 16);
+  auto compute_half = [&](int d, const uint4* ksb, const uint4* vsb) {
     if (!active) return;
     f32x16 s, dp;
 #pragma unroll
@@ -366,11 +364,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
                                                        dsw[cc][3]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma_32x32x16<F16>(as_ev8(ktsb[ktread_h + dt * 32 * kVRow + 2 * cc]), b,
-                                     acc[dt]);
+        acc[dt] = mfma_32x32x16<F16>(tr_operand(ksb, trb_h + cc * 16 * (kKRow * 16) + 16 * dt),
+                                     b, acc[dt]);
     }
   };
-  auto compute = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
+  auto compute = [&](int d, const uint4* ksb, const uint4* vsb) {
     if (!active) return;
     f32x16 s[2], dp[2];
 #pragma unroll
@@ -409,7 +407,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
                                                        dsw[cc][3]));
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = mfma_32x32x16<F16>(as_ev8(ktsb[ktread + dt * 32 * kVRow + 2 * cc]), b, acc[dt]);
+        acc[dt] = mfma_32x32x16<F16>(tr_operand(ksb, trb + cc * 16 * (kKRow * 16) + 16 * dt), b,
+                                     acc[dt]);
     }
   };
 
@@ -419,9 +418,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   // own register allocation
   auto passes = [&](auto hv) __attribute__((always_inline)) {
   constexpr bool HV = decltype(hv)::value;
-  auto work = [&](int d, const uint4* ksb, const uint4* vsb, const uint4* ktsb) {
-    if constexpr (HV) compute_half(d, ksb, vsb, ktsb);
-    else compute(d, ksb, vsb, ktsb);
+  auto work = [&](int d, const uint4* ksb, const uint4* vsb) {
+    if constexpr (HV) compute_half(d, ksb, vsb);
+    else compute(d, ksb, vsb);
   };
   for (int64_t e0 = beg; e0 < end; e0 += kPassEntries) {
     const int m = int(min(int64_t(kPassEntries), end - e0));
@@ -443,19 +442,19 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     __syncthreads();
     const int T = __builtin_amdgcn_readfirstlane(ntl);
     if (T == 0) continue;
-    issue(__builtin_amdgcn_readfirstlane(tl[0]), ks0, vs0, kts0);
+    issue(__builtin_amdgcn_readfirstlane(tl[0]), ks0, vs0);
     wait_copies();
     __syncthreads();
     for (int n = 0; n < T; n += 2) {
       const int d0 = __builtin_amdgcn_readfirstlane(tl[n]);
       const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
-      if (n + 1 < T) issue(d1, ks1, vs1, kts1);
-      work(d0, ks0, vs0, kts0);
+      if (n + 1 < T) issue(d1, ks1, vs1);
+      work(d0, ks0, vs0);
       wait_copies();
       __syncthreads();
       if (n + 1 >= T) break;
-      if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), ks0, vs0, kts0);
-      work(d1, ks1, vs1, kts1);
+      if (n + 2 < T) issue(__builtin_amdgcn_readfirstlane(tl[n + 2]), ks0, vs0);
+      work(d1, ks1, vs1);
       wait_copies();
       __syncthreads();
     }
@@ -490,7 +489,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     }
   }
   // dQ rows (this wave's own 32 rows); pad query rows are written as zero
-  store_rows<F16>(acc, row_valid && !own_pad ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32,
+  store_rows_perm<F16>(acc, row_valid && !own_pad ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32,
                   half);
 }
 
@@ -500,11 +499,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 // of 16 data units and 1 pad unit (272 B), as the forward's K tiles.  They
 // are read as rows (ds_read_b128: the A operands of S = Q K^T and
 // dP = dO V^T; 8 consecutive rows at the same unit fall on distinct banks)
-// and as columns (ds_read_b64_tr_b16: the A operands of dK^T += Q^T dS and
-// dV^T += dO^T P).  In a column read the 16 lanes of a group address 4 rows
-// (68 dwords apart) and 4 segments of 8 bytes; the segments are taken at byte
-// offsets 0, 8, 64, 72 of a 128-byte window, so that the 16 two-dword spans
-// 4e + {0, 2, 16, 18} (mod 32) cover every bank once.
+// and as columns (tr_operand: the A operands of dK^T += Q^T dS and
+// dV^T += dO^T P).
 constexpr int kQRow = kKRow;
 constexpr int kQUnits = 64 * kQRow;    // 1088 16-byte units (17 KB)
 constexpr int kQChunks = kQUnits / 64;  // 17 wave-loads of 1 KB
@@ -514,33 +510,6 @@ constexpr int kQChunks = kQUnits / 64;  // 17 wave-loads of 1 KB
 __device__ inline uint32_t qtile_off(int pos) {
   const int row = pos / kQRow, unit = pos % kQRow;
   return kappa(row) * 16 + (unit < 16 ? unit : 0);
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// i%4 of the 8-byte segments addressed by lanes 4e + i/4, e = 0..3.
-__device__ inline v4i16 lds_read_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
-}
-
-// Store a 32 x 128 accumulator tile whose MFMA row m of tile dt holds column
-// d = 64(m/16) + 8dt + 32((m%16)/8) + 4((m/4)%2) + m%4 (the order the
-// transposing reads produce), times `mul`, as element rows: register j of
-// lane l holds key l%32 and d = 64(j/8) + 8dt + 32((j/4)%2) + 4(l/32) + j%4.
-template <bool F16>
-__device__ inline void store_rows_perm(const f32x16 (&acc)[4], float mul, uint4* rows_base,
-                                       int l32, int half) {
-  uint2* dst = reinterpret_cast<uint2*>(rows_base + int64_t(l32) * 16);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d0 = 64 * (jj / 2) + 8 * dt + 32 * (jj % 2) + 4 * half;
-      dst[d0 / 4] = make_uint2(pack2<F16>(acc[dt][4 * jj] * mul, acc[dt][4 * jj + 1] * mul),
-                               pack2<F16>(acc[dt][4 * jj + 2] * mul, acc[dt][4 * jj + 3] * mul));
-    }
 }
 
 // dK and dV of one key block in one pass over the query sub-tiles that
@@ -672,8 +641,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   // columns 64*((lane/16)%2) + 32*((lane%4)/2) + 4*(lane%2) .. +3, plus 8dt)
   const int qread = l32 * kQRow + half;
   const int vread = key * kKRow + half;
-  const int trb = (4 * half + (lane & 15) / 4) * (kQRow * 16) + 128 * ((lane >> 4) & 1) +
-                  64 * ((lane & 3) >> 1) + 8 * (lane & 1);
+  const int trb = tr_lane_base(lane);
 
   // one 32-query half hs of a sub-tile held in (qsb, dsb), lse / D in set
   auto half_tile = [&](int hs, const uint4* qsb, const uint4* dsb, int set, float mlane)
@@ -683,16 +651,10 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     for (int jj = 0; jj < 16; ++jj) s[jj] = dp[jj] = 0.f;
     uint32_t pw[2][4], dsw[2][4];
     const int rbase = qread + hs * 32 * kQRow;
-    const char* const tbq = reinterpret_cast<const char*>(qsb) + trb + hs * 32 * (kQRow * 16);
-    const char* const tbd = reinterpret_cast<const char*>(dsb) + trb + hs * 32 * (kQRow * 16);
-    // A operand of a transposed product, 16-query step cc, d tile dt: the
-    // first read takes queries 8*half + 0..3 of the step, the second 4..7
-    // (their rows lie 8 further on: kappa swaps bits 2 and 3)
-    auto tr_op = [&](const char* b, int cc, int dt) -> ev8 {
-      const char* p = b + cc * 16 * (kQRow * 16) + 16 * dt;
-      const v4i16 lo = lds_read_tr16(p);
-      const v4i16 hi = lds_read_tr16(p + 8 * (kQRow * 16));
-      return __builtin_bit_cast(ev8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const int hsoff = hs * 32 * (kQRow * 16);
+    // A operand of a transposed product, 16-query step cc, d tile dt
+    auto tr_op = [&](const uint4* tile, int hsoff, int cc, int dt) -> ev8 {
+      return tr_operand(tile, trb + hsoff + cc * 16 * (kQRow * 16) + 16 * dt);
     };
     // A operand of slot i, read 2 slots ahead, and the V operand of slots
     // 8..15 one slot ahead (longer leads spill at 256 registers)
@@ -704,10 +666,10 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
         opa[i % 3] = as_ev8(dsb[rbase + 2 * (i - 8)]);
       } else if (i < 24) {
         const int x = i - 16;
-        opa[i % 3] = tr_op(tbd, x / 4, x % 4);
+        opa[i % 3] = tr_op(dsb, hsoff, x / 4, x % 4);
       } else {
         const int x = i - 24;
-        opa[i % 3] = tr_op(tbq, x / 4, x % 4);
+        opa[i % 3] = tr_op(qsb, hsoff, x / 4, x % 4);
       }
     };
     // pair e holds registers 2e, 2e+1: queries 32hs + 16(e/4) + 8*half +
@@ -879,8 +841,7 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dq_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.kt),
-                     static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.row_ptr, a.col,
+                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.row_ptr, a.col,
                      a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), a.queues, g, scale_log2,
                      scale);
   if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
@@ -911,10 +872,6 @@ hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(rowdot_kernel<false>, dim3(unsigned((blocked_rows + 15) / 16)), dim3(256),
                        0, s, static_cast<const uint4*>(a.o), static_cast<const uint4*>(a.dout),
                        a.dsum, blocked_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned chunks = unsigned(blocked_rows / kKvChunk);
-  hipLaunchKernelGGL(transpose_kernel, dim3(chunks), dim3(256), 0, s,
-                     static_cast<const uint4*>(a.k), static_cast<uint4*>(a.kt));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(tmap_kernel, dim3(unsigned((int64_t(g.batch) * g.heads * g.nb + 3) / 4)),
                      dim3(256), 0, s, a.row_ptr, a.col, a.uniform_k, a.nnz, a.tlist, a.tcount, g);

@@ -105,16 +105,14 @@ const char* raster_unsupported(const VsaGeom& g) {
 }
 
 struct BwdWorkspace {
-  size_t dsum, kt, tlist, tcount, queue, total;
+  size_t dsum, tlist, tcount, queue, total;
 };
 BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
   const VsaGeom& g = p.g;
   const size_t heads = size_t(g.batch) * g.heads;
-  const size_t blk = heads * g.npad * g.head_dim * 2;
   BwdWorkspace w;
   size_t off = 0;
   w.dsum = off; off += align256(heads * g.npad * 4);
-  w.kt = off; off += align256(blk);
   w.tlist = off; off += align256(heads * g.nb * size_t(g.nb) * 4);
   w.tcount = off; off += align256(heads * g.nb * 4);
   w.queue = off; off += vsa::kAttnQueueBytes;
@@ -578,7 +576,6 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t p, const void* q, const void* k,
   a.row_ptr = row_ptr; a.col = col; a.uniform_k = row_ptr ? 0 : uniform_k; a.nnz = nnz;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsum = reinterpret_cast<float*>(base + w.dsum);
-  a.kt = base + w.kt;
   a.tlist = reinterpret_cast<int32_t*>(base + w.tlist);
   a.tcount = reinterpret_cast<int32_t*>(base + w.tcount);
   a.queues = reinterpret_cast<unsigned int*>(base + w.queue);

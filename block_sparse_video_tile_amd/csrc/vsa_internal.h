@@ -77,7 +77,6 @@ struct BwdArgs {
   void *dq, *dk, *dv;                 // token-major blocked outputs
   // workspace
   float* dsum;                        // rowsum(dO * O) [B,NH,Npad]
-  void* kt;                           // d-major 64-token chunks of K
   int32_t* tlist;                     // [B*NH*nb][nb] transposed block map
   int32_t* tcount;                    // [B*NH*nb]
   unsigned int* queues;               // row-queue counters (kAttnQueueBytes)

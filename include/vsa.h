@@ -300,8 +300,8 @@ vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t plan, const void* q_blk,
                                              float* lse, void* stream);
 
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
- * rowsum(dO*O) [B,NH,Npad] fp32, a d-major copy of K, and the
- * transposed block map (B*NH*nb*nb + B*NH*nb int32) and the row-queue
+ * rowsum(dO*O) [B,NH,Npad] fp32, the transposed block map
+ * (B*NH*nb*nb + B*NH*nb int32) and the row-queue
  * counters of its balanced launches (rows and columns are claimed per XCD at
  * run time, as in vsa_block_sparse_attn_fwd_ws), each 256-byte aligned. */
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t plan, size_t* bytes);

@@ -183,9 +183,9 @@ def test_backward_checks(plan):
     bad = vsa.VSA_ERR_INVALID_ARGUMENT
     need = vsa.vsa_block_sparse_attn_bwd_workspace_size(plan)
     info = plan.info
-    # rowsum, the d-major copy of K and the transposed map (nb x nb per head)
+    # rowsum and the transposed map (nb x nb per head)
     assert need >= (info["num_rows"] // info["num_blocks"]) * (
-        info["padded_len"] * 4 + info["num_blocks"] ** 2 * 4) + info["blocked_elems"] * 2
+        info["padded_len"] * 4 + info["num_blocks"] ** 2 * 4)
     f = "vsa_block_sparse_attn_bwd"
     # (plan, q, k, v, o, do, lse, row_ptr, col, uniform_k, nnz, dq, dk, dv, ws, ws_bytes, stream)
     args = [h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE,
