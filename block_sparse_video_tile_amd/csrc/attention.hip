@@ -1298,8 +1298,10 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
 __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ row_ptr,
                                                           int64_t nnz, int64_t nrows, int nb,
                                                           int32_t* __restrict__ order) {
-  constexpr int kBins = 2048;  // entry counts >= kBins - 1 share the first bin
+  constexpr int kBins = 2048;   // entry counts >= kBins - 1 share the first bin
+  constexpr int kCache = 4096;  // row lengths kept in LDS when the range has at most this many rows
   __shared__ long long wsum[16];
+  __shared__ int lens_sh[kCache];
   __shared__ int wcnt[16];
   __shared__ int bin_at[kBins];  // count, then first position, of each bin of a head
   __shared__ __align__(16) int keys[1024];
@@ -1307,14 +1309,22 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
   const uint32_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   const uint32_t count = per + (x < rem ? 1u : 0u);
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  auto len = [&](uint32_t r) -> int64_t {
+  auto len_of = [&](uint32_t r) -> int64_t {
     const int64_t beg = min(max(int64_t(row_ptr[r]), int64_t(0)), nnz);
     const int64_t end = min(max(int64_t(row_ptr[r + 1]), beg), nnz);
     return end - beg;
   };
+  // the lengths are read from global memory once and kept in LDS (the passes
+  // below read each several times); a longer range reads them each time
+  const bool cached = count <= uint32_t(kCache);
+  auto len = [&](uint32_t r) -> int64_t { return cached ? lens_sh[r - start] : len_of(r); };
   // total entries of the range
   long long part = 0;
-  for (uint32_t t = tid; t < count; t += 1024) part += len(start + t);
+  for (uint32_t t = tid; t < count; t += 1024) {
+    const int64_t l = len_of(start + t);
+    if (cached) lens_sh[t] = int(min(l, int64_t(0x7fffffff)));
+    part += l;
+  }
   for (int d = 32; d > 0; d /= 2) part += __shfl_xor(part, d);
   if (lane == 0) wsum[wave] = part;
   __syncthreads();
