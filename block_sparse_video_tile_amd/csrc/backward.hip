@@ -342,22 +342,25 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
     }
     const int valid = (d & 127) + 1;
     uint32_t dsw[2][4];
+    auto pairs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        float d2[2];
+        for (int t = 0; t < 8; t += 2) {
+          float d2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int jj = 8 * cc + t + u;
-          const int key = 32 * kh + 16 * cc + 8 * half + t + u;
-          const float p = key < valid
-                              ? __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -lse_l2))
-                              : 0.f;
-          d2[u] = p * (dp[jj] - dq_row);
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * cc + t + u;
+            const int key = 32 * kh + 16 * cc + 8 * half + t + u;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -lse_l2));
+            if constexpr (decltype(masked)::value) p = key < valid ? p : 0.f;
+            d2[u] = p * (dp[jj] - dq_row);
+          }
+          dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
         }
-        dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
-      }
+    };
+    if (valid == kKvChunk) pairs(std::false_type());
+    else pairs(std::true_type());
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
@@ -383,24 +386,28 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
         dp[mt] = mfma_32x32x16<F16>(as_ev8(vsb[kread + mt * 32 * kKRow + 2 * st]), df[st], dp[mt]);
       }
     const int valid = (d & 127) + 1;
-    // dS^T pairs, grouped by 16-key step cc (keys 16cc + 8*half + 0..7)
+    // dS^T pairs, grouped by 16-key step cc (keys 16cc + 8*half + 0..7); the
+    // comparison with the valid count only for a partial sub-tile
     uint32_t dsw[4][4];
+    auto pairs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+      for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-      for (int t = 0; t < 8; t += 2) {
-        float d2[2];
+        for (int t = 0; t < 8; t += 2) {
+          float d2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int jj = 8 * (cc % 2) + t + u;
-          const int key = 16 * cc + 8 * half + t + u;
-          const float p = key < valid
-                              ? __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2, -lse_l2))
-                              : 0.f;
-          d2[u] = p * (dp[cc / 2][jj] - dq_row);
+          for (int u = 0; u < 2; ++u) {
+            const int jj = 8 * (cc % 2) + t + u;
+            const int key = 16 * cc + 8 * half + t + u;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[cc / 2][jj], scale_log2, -lse_l2));
+            if constexpr (decltype(masked)::value) p = key < valid ? p : 0.f;
+            d2[u] = p * (dp[cc / 2][jj] - dq_row);
+          }
+          dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
         }
-        dsw[cc][t / 2] = pack2<F16>(d2[0], d2[1]);
-      }
+    };
+    if (valid == kKvChunk) pairs(std::false_type());
+    else pairs(std::true_type());
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       const ev8 b = __builtin_bit_cast(ev8, make_uint4(dsw[cc][0], dsw[cc][1], dsw[cc][2],
