@@ -527,16 +527,18 @@ __device__ inline uint32_t qtile_off(int pos) {
 // two 32-query halves of 32 fenced MFMA slots:
 //   slots  0.. 7  S   = Q K^T    (A: Q rows, B: K fragments)
 //   slots  8..15  dP  = dO V^T   (A: dO rows, B: V rows), with the 8
-//                 exponential pairs P = 2^(S log2(e)/sqrt(D) - lse log2(e)) x
-//                 multiplicity in slots 10..17
+//                 exponential pairs P = 2^(S log2(e)/sqrt(D) - lse log2(e) +
+//                 log2(multiplicity)) in slots 10..17
 //   slots 16..23  dV^T += dO^T P (A: dO columns), with the 8 pairs
 //                 dS = P (dP - D) in slots 18..25
 //   slots 24..31  dK^T += Q^T dS (A: Q columns)
 // so S and dP are formed once for both gradients.  The registers of S, dP,
 // P and dS of one half, the two accumulator sets and the K fragments fit the
 // 256 of two waves per SIMD; V, the largest operand held per wave otherwise,
-// is read from LDS.  Pad query rows carry lse = +inf (P = 0) and D = 0; pad
-// keys (zero K and V rows) take the factor 0 and their rows are stored as 0.
+// is read from LDS.  Pad query rows carry lse = +inf (P = 0) and D = 0.  A
+// pad key's P and dS reach only that key's own columns of dV^T and dK^T
+// (each column of these products is one key), and those rows are stored as
+// 0, so pad keys need no masking.
 // Edge key blocks of 5 or 6 key groups split waves 4..7 by query halves, as
 // the separate kernels did.
 template <int NW, bool F16>
@@ -634,10 +636,12 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     const int64_t row = int64_t(d >> 7) * kKvChunk + lane;
     return {lbase[row], dsbase[row]};
   };
-  auto put = [&](Raw r, int d, int set) {
+  // the sub-tile's query block is listed `mult` times: P carries that factor
+  // as -log2(mult) in the staged lse
+  auto put = [&](Raw r, int d, int set, float mult) {
     if (wave == 0) {
       const bool ok = lane <= (d & 127);
-      lse_sh[set][lane] = ok ? r.l * kLog2e : INFINITY;
+      lse_sh[set][lane] = ok ? r.l * kLog2e - __log2f(mult) : INFINITY;
       d_sh[set][lane] = ok ? r.d : 0.f;
     }
   };
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
   const int trb = tr_lane_base(lane);
 
   // one 32-query half hs of a sub-tile held in (qsb, dsb), lse / D in set
-  auto half_tile = [&](int hs, const uint4* qsb, const uint4* dsb, int set, float mlane)
+  auto half_tile = [&](int hs, const uint4* qsb, const uint4* dsb, int set)
       __attribute__((always_inline)) {
     f32x16 s, dp;
 #pragma unroll
@@ -720,8 +724,8 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
         const int e = i - 10, jj = 2 * e;
         const float2 l = lq[e % 3];
         if (e + 2 < 8) read_l(e + 2);
-        s[jj] = __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -l.x)) * mlane;
-        s[jj + 1] = __builtin_amdgcn_exp2f(fmaf(s[jj + 1], scale_log2, -l.y)) * mlane;
+        s[jj] = __builtin_amdgcn_exp2f(fmaf(s[jj], scale_log2, -l.x));
+        s[jj + 1] = __builtin_amdgcn_exp2f(fmaf(s[jj + 1], scale_log2, -l.y));
         pw[e / 4][e % 4] = pack2<F16>(s[jj], s[jj + 1]);
         pin_v(pw[e / 4][e % 4]);
       }
@@ -735,10 +739,9 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
       slot_fence();
     }
   };
-  auto work = [&](float mult, const uint4* qsb, const uint4* dsb, int set) {
+  auto work = [&](const uint4* qsb, const uint4* dsb, int set) {
     if (!active) return;
-    const float mlane = key < cj ? mult : 0.f;
-    for (int hs = hs_lo; hs <= hs_hi; ++hs) half_tile(hs, qsb, dsb, set, mlane);
+    for (int hs = hs_lo; hs <= hs_hi; ++hs) half_tile(hs, qsb, dsb, set);
   };
 
   const int nent = tcount[c];
@@ -767,11 +770,10 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
       issue(d0, qs0, ds0);
       const Raw r0 = raw_of(d0);
       wait_copies();  // also the V rows of the first pass
-      put(r0, d0, 0);
+      put(r0, d0, 0, float(tm[0]));
     }
     __syncthreads();
     for (int n = 0; n < T; n += 2) {
-      const float m0 = float(tm[n]);
       const int d1 = __builtin_amdgcn_readfirstlane(tl[min(n + 1, T - 1)]);
       const float m1 = float(tm[min(n + 1, T - 1)]);
       Raw r1 = {0.f, 0.f};
@@ -779,20 +781,21 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
         issue(d1, qs1, ds1);
         r1 = raw_of(d1);
       }
-      work(m0, qs0, ds0, 0);
+      work(qs0, ds0, 0);
       wait_copies();
-      if (n + 1 < T) put(r1, d1, 1);
+      if (n + 1 < T) put(r1, d1, 1, m1);
       __syncthreads();
       if (n + 1 >= T) break;
       const int d2 = __builtin_amdgcn_readfirstlane(tl[min(n + 2, T - 1)]);
+      const float m2 = float(tm[min(n + 2, T - 1)]);
       Raw r2 = {0.f, 0.f};
       if (n + 2 < T) {
         issue(d2, qs0, ds0);
         r2 = raw_of(d2);
       }
-      work(m1, qs1, ds1, 1);
+      work(qs1, ds1, 1);
       wait_copies();
-      if (n + 2 < T) put(r2, d2, 0);
+      if (n + 2 < T) put(r2, d2, 0, m2);
       __syncthreads();
     }
   }
