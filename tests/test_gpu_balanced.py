@@ -162,7 +162,7 @@ def test_rows_longer_than_one_list_pass():
     q, kk, v = make_qkv(wl)
     qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
     rp = torch.as_tensor(rp_h.astype(np.int32)).to(DEV)
-    col = torch.as_tensor(np.array(sum(lists, []), np.int32)).to(DEV)
+    col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
     _assert_same(plain, bal, "long rows")
@@ -186,11 +186,36 @@ def test_claim_order_across_heads():
     q, kk, v = make_qkv(wl)
     qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
     rp = torch.as_tensor(rp_h.astype(np.int32)).to(DEV)
-    col = torch.as_tensor(np.array(sum(lists, []), np.int32)).to(DEV)
+    col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
     _assert_same(plain, bal, "order across heads")
     _check_claim_order(ws, rp_h, nt, "order across heads")
+
+
+def test_claim_order_of_ranges_longer_than_the_length_cache():
+    """Queue ranges of 4125 rows (33000 one-tile rows of one head), more than
+    the 4096 row lengths the order kernel keeps in LDS, so it reads them from
+    the map at every pass.  Seeded Q, K, V drawn on the device (the check is
+    the claim order and the balanced launch equal to the plain one)."""
+    nt = 33000
+    wl = Workload("order_long", (1, 1, nt * 64), (1, 1, 64), 1, 1, 128, None, seed=23)
+    rng = np.random.default_rng(23)
+    lens = rng.integers(0, 9, size=nt)
+    lists = [sorted(rng.choice(nt, size=int(k), replace=False).tolist()) for k in lens]
+    rp_h = np.zeros(nt + 1, np.int64)
+    rp_h[1:] = np.cumsum(lens)
+    plan = _plan(wl)
+    gen = torch.Generator(DEV).manual_seed(23)
+    q, kk, v = (torch.randn((1, nt * 64, 1, 128), generator=gen, device=DEV).to(torch.bfloat16)
+                for _ in range(3))
+    qb, kb, vb, _, _ = _gather_all(plan, q, kk, v)
+    rp = torch.as_tensor(rp_h.astype(np.int32)).to(DEV)
+    col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
+    _assert_same(plain, bal, "long ranges")
+    _check_claim_order(ws, rp_h, nt, "long ranges")
 
 
 @pytest.mark.parametrize("gated", [False, True])
