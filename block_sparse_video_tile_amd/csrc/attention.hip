@@ -1399,11 +1399,21 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
       int same = 0;
       if (key >= 0) {
         const int4* k4 = reinterpret_cast<const int4*>(keys);
-        for (int j = 0; j < tid / 4; ++j) {
+        const int n4 = tid / 4;
+        int j = 0;
+        for (; j + 8 <= n4; j += 8) {  // eight reads in flight at a time
+          int4 kk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) kk[u] = k4[j + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            same += (kk[u].x == key) + (kk[u].y == key) + (kk[u].z == key) + (kk[u].w == key);
+        }
+        for (; j < n4; ++j) {
           const int4 kk = k4[j];
           same += (kk.x == key) + (kk.y == key) + (kk.z == key) + (kk.w == key);
         }
-        for (int j = tid & ~3; j < tid; ++j) same += keys[j] == key;
+        for (int x = tid & ~3; x < tid; ++x) same += keys[x] == key;
         order[start + base + bin_at[key] + same] = int32_t(t);
       }
       __syncthreads();  // every row of the chunk has read bin_at
