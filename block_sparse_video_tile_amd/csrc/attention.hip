@@ -1293,8 +1293,12 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
 // value blocks of one head of a random map are several times the L2, and
 // rows at different points of their lists would each miss.
 // order[start .. start + count) of range x is a permutation of the range's
-// rows; claim_row hands positions out in that order.  One workgroup per
-// range; offsets are sanitised as the attention kernel sanitises them.
+// rows; claim_row hands positions out in that order.  Range x has G
+// workgroups (G = gridDim.x / 8, at most 32): workgroup g sorts the heads g,
+// g + G, g + 2G, ... that the range touches, in that order, counting the rows
+// between them as it goes (so each reads the range's lengths about once), and
+// workgroup 0 also places the long rows.  Offsets are sanitised as the
+// attention kernel sanitises them.
 __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restrict__ row_ptr,
                                                           int64_t nnz, int64_t nrows, int nb,
                                                           int32_t* __restrict__ order) {
@@ -1305,7 +1309,8 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
   __shared__ int wcnt[16];
   __shared__ int bin_at[kBins];  // count, then first position, of each bin of a head
   __shared__ __align__(16) int keys[1024];
-  const uint32_t n = uint32_t(nrows), per = n / 8, rem = n % 8, x = blockIdx.x;
+  const uint32_t n = uint32_t(nrows), per = n / 8, rem = n % 8, x = blockIdx.x % 8,
+                 seg = blockIdx.x / 8, nseg = gridDim.x / 8;
   const uint32_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
   const uint32_t count = per + (x < rem ? 1u : 0u);
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -1335,8 +1340,14 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
   // bin of a row that is not long: 0 for the largest counts
   auto bin_of = [&](int64_t l) { return kBins - 1 - int(min(l, int64_t(kBins - 1))); };
 
-  // the long rows, ascending (ballot compaction, 1024 rows at a time)
-  uint32_t base = 0;
+  if (count == 0 || nb <= 0) return;
+  const uint32_t last = start + count;
+  const uint32_t head0 = start - start % uint32_t(nb);  // first row of the range's first head
+  if (uint64_t(head0) + uint64_t(seg) * uint32_t(nb) >= last) return;  // workgroup-uniform
+
+  // the long rows, ascending (ballot compaction, 1024 rows at a time), placed
+  // by workgroup 0; every workgroup counts them
+  uint32_t nlong = 0;
   for (uint32_t chunk = 0; chunk < count; chunk += 1024) {
     const uint32_t t = chunk + tid;
     const bool flag = t < count && is_long(len(start + t));
@@ -1350,15 +1361,29 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
       woff += w < wave ? wcnt[w] : 0;
       ctot += wcnt[w];
     }
-    if (flag) order[start + base + woff + before] = int32_t(start + t);
-    base += ctot;
+    if (flag && seg == 0) order[start + nlong + woff + before] = int32_t(start + t);
+    nlong += ctot;
   }
-  if (count == 0 || nb <= 0) return;
 
-  // the other rows, head by head: a counting sort by bin
-  const uint32_t last = start + count;
-  for (uint32_t h0 = start - start % uint32_t(nb); h0 < last; h0 += uint32_t(nb)) {
-    const uint32_t s0 = max(h0, start), s1 = min(h0 + uint32_t(nb), last);
+  // this workgroup's heads, ascending; `prior` counts the rows that are not
+  // long in [start, scanned)
+  uint32_t scanned = start, prior = 0;
+  for (uint32_t hs = seg;; hs += nseg) {
+    const uint64_t h0 = uint64_t(head0) + uint64_t(hs) * uint32_t(nb);  // no wrap-around
+    if (h0 >= last) break;  // workgroup-uniform
+    const uint32_t s0 = max(uint32_t(h0), start);
+    const uint32_t s1 = uint32_t(min(h0 + uint32_t(nb), uint64_t(last)));
+    int c = 0;
+    for (uint32_t t = scanned + tid; t < s0; t += 1024) c += is_long(len(t)) ? 0 : 1;
+    for (int d = 32; d > 0; d /= 2) c += __shfl_xor(c, d);
+    __syncthreads();  // wcnt of the previous pass has been read
+    if (lane == 0) wcnt[wave] = c;
+    __syncthreads();
+    for (int w = 0; w < 16; ++w) prior += uint32_t(wcnt[w]);
+    scanned = s0;
+    const uint32_t base = nlong + prior;
+
+    // the head's other rows: a counting sort by bin
     for (int b = tid; b < kBins; b += 1024) bin_at[b] = 0;
     __syncthreads();
     for (uint32_t t = s0 + tid; t < s1; t += 1024) {
@@ -1373,14 +1398,11 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
       const int up = __shfl_up(incl, d);
       if (lane >= d) incl += up;
     }
-    __syncthreads();  // wcnt of the long-row pass or the previous head has been read
+    __syncthreads();  // wcnt of the counts above has been read
     if (lane == 63) wcnt[wave] = incl;
     __syncthreads();
-    int woff = 0, htot = 0;
-    for (int w = 0; w < 16; ++w) {
-      woff += w < wave ? wcnt[w] : 0;
-      htot += wcnt[w];
-    }
+    int woff = 0;
+    for (int w = 0; w < 16; ++w) woff += w < wave ? wcnt[w] : 0;
     const int excl = woff + incl - (c0 + c1);
     bin_at[2 * tid] = excl;
     bin_at[2 * tid + 1] = excl + c0;
@@ -1413,14 +1435,13 @@ __global__ __launch_bounds__(1024) void order_rows_kernel(const int32_t* __restr
           const int4 kk = k4[j];
           same += (kk.x == key) + (kk.y == key) + (kk.z == key) + (kk.w == key);
         }
-        for (int x = tid & ~3; x < tid; ++x) same += keys[x] == key;
+        for (int q = tid & ~3; q < tid; ++q) same += keys[q] == key;
         order[start + base + bin_at[key] + same] = int32_t(t);
       }
       __syncthreads();  // every row of the chunk has read bin_at
       if (key >= 0) atomicAdd(&bin_at[key], 1);
       __syncthreads();
     }
-    base += uint32_t(htot);
   }
 }
 
@@ -1442,8 +1463,12 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (row_ptr != nullptr && order != nullptr) {
-      hipLaunchKernelGGL(order_rows_kernel, dim3(8), dim3(1024), 0, s, row_ptr, nnz, rows, g.nb,
-                         order);
+      // workgroups per queue range: the heads a range can touch (its rows,
+      // plus one for a range that starts inside a head), at most 32
+      const int64_t per_max = (rows + 7) / 8;
+      const int64_t segs = std::min<int64_t>(32, (per_max + g.nb - 1) / g.nb + 1);
+      hipLaunchKernelGGL(order_rows_kernel, dim3(unsigned(8 * segs)), dim3(1024), 0, s, row_ptr,
+                         nnz, rows, g.nb, order);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       claim_order = order;
