@@ -30,7 +30,11 @@
 //   step and share them in L2); for a
 //   layer whose heads' key/value blocks outgrow the memory-side cache when
 //   the XCDs work on 8 different heads, the queues interleave the heads
-//   instead (claim_row_strided).
+//   instead (claim_row_strided).  Launches of at most 256 rows per queue
+//   (a few rounds of rows per CU) hand out the last rows of each queue as
+//   two halves of their entries, merged by the half that finishes second
+//   (the tail split, see TailSplit), so the kernel's last round is made of
+//   half rows.
 //   The row's key blocks are streamed in 64-key sub-tiles (a block with c
 //   valid tokens has ceil(c/64) of them; trailing all-pad sub-tiles are never
 //   loaded).  The workgroup first flattens its CSR entries into a list of
@@ -99,8 +103,9 @@
 #include "attn_common.h"
 #include "vsa_internal.h"
 
-// Device scratch of vsa_block_sparse_attn_fwd_noalloc: the row-queue counters
-// of the balanced launch, in a fixed library-owned array (one copy per GPU,
+// Device scratch of vsa_block_sparse_attn_fwd_noalloc: the row-queue counters,
+// claim order and tail-split region of the balanced launch, in a fixed
+// library-owned array (one copy per GPU,
 // held until the process ends) for callers that cannot allocate.  In host
 // code this name only stands for the symbol; kernels receive the device
 // address that vsa::noalloc_scratch looks up per device.
@@ -175,8 +180,12 @@ __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-__global__ void queue_reset_kernel(unsigned int* queues) {
+// Clears the row-queue counters and the tail-split counters of a balanced
+// launch (a kernel rather than a memset, so that the launch can be recorded
+// into a graph).
+__global__ void queue_reset_kernel(unsigned int* queues, unsigned int* flags, int nflags) {
   if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
+  for (int x = threadIdx.x; x < nflags; x += blockDim.x) flags[x] = 0u;
 }
 
 // Row max over the 16 scores of one tile.
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int uniform_k,
     int64_t nnz, uint4* __restrict__ o, float* __restrict__ lse, const uint4* __restrict__ gate,
     const float* __restrict__ oc, unsigned int* __restrict__ queues,
-    const int32_t* __restrict__ order, VsaGeom g, float scale_log2, float scale) {
+    const int32_t* __restrict__ order, VsaGeom g, float scale_log2, float scale, TailSplit ts) {
   static_assert(NW == NQ || (NQ == 2 && NW == 4), "waves: one per query group, or 4 for 2 groups");
   static_assert(NW * 32 * kORow <= 2 * (kKUnits + kVUnits) && 8 * 32 * kORow <= 4 * kKUnits,
                 "O staging must fit in LDS");
@@ -249,11 +258,16 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   // `queues`, claimed at start-up (claim_row); a workgroup that finds every
   // row taken leaves at once (workgroup-uniform, before any other barrier).
   __shared__ int64_t row_sh;
+  __shared__ int part_sh;
+  const uint32_t tail_split = queues == nullptr ? 0u : uint32_t(ts.per_queue);
   const int64_t r = queues == nullptr ? xcd_remap(blockIdx.x, nrows)
                     : (row_ptr == nullptr && g.head_interleave)
-                        ? claim_row_strided(queues, nrows, g, &row_sh)
-                        : claim_row(queues, nrows, g, &row_sh, order);
+                        ? claim_row_strided(queues, nrows, g, &row_sh, tail_split, &part_sh)
+                        : claim_row(queues, nrows, g, &row_sh, order, tail_split, &part_sh);
   if (r < 0) return;
+  // -1: the whole row; else this workgroup computes half (part & 1) of the
+  // row's entries for split slot part / 2 (workgroup-uniform)
+  const int part = tail_split != 0 ? part_sh : -1;
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
@@ -294,6 +308,12 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
   } else {
     beg = r * uniform_k;
     end = beg + uniform_k;
+  }
+  if (part >= 0) {
+    // a half of a split row: the first or the second half of its entries
+    const int64_t mid = beg + (end - beg) / 2;
+    if (part & 1) beg = mid;
+    else end = mid;
   }
   const int32_t* rcol = col + beg;
   const int len = int(end - beg);
@@ -1200,6 +1220,67 @@ __global__ __launch_bounds__(NW * 64, NW == 2 * NQ ? 2 : 1) void attn_fwd_kernel
     }
   }
 
+  // ---- tail split: both halves of a split row leave their unnormalised
+  // (O^T, m, l) in the slot's part of the workspace (every wave holding rows
+  // stores its registers lane by lane); the half whose count comes second
+  // reads the other's and merges, with the first half as a and the second
+  // as b whichever merges: m = max(m_a, m_b), O = O_a w_a + O_b w_b,
+  // l = l_a w_a + l_b w_b, w = 2^((m_x - m) c), each product and sum rounded
+  // on its own, so the row's bits do not depend on which half finishes last.
+  // The halves may run on different XCDs, whose L2 caches are not coherent
+  // with each other: the partials are written and read with device-coherent
+  // accesses (relaxed atomic stores and loads at agent scope, which go past
+  // the non-coherent L2), the stores drained before the count.  A release or
+  // acquire fence would instead write back or invalidate the whole L2 of the
+  // XCD, under every other workgroup running there.
+  if (part >= 0) {
+    const int slot = part >> 1, hf = part & 1;
+    const bool holds = active && !own_pad;
+    float* const mine = ts.part + (size_t(2 * slot + hf) * NW + wave) * kSplitHalfFloatsPerWave;
+    auto put = [](float* p, float x) { __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    auto get = [](const float* p) {
+      return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (holds) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) put(mine + (dt * 16 + j) * 64 + lane, oacc[dt][j]);
+      put(mine + 64 * 64 + lane, m_run);
+      put(mine + 65 * 64 + lane, l_run);
+    }
+    // every store of this wave has reached the coherent level before any
+    // wave of the workgroup counts the half as done
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __shared__ unsigned int done_sh;
+    if (tid == 0) done_sh = atomicAdd(&ts.flags[slot], 1u);
+    __syncthreads();
+    if (done_sh == 0) return;  // the other half merges (workgroup-uniform)
+    if (tid == 0) ts.rows[slot] = int32_t(r);
+    const float* const other =
+        ts.part + (size_t(2 * slot + (1 - hf)) * NW + wave) * kSplitHalfFloatsPerWave;
+    if (holds) {
+      const float m_o = get(other + 64 * 64 + lane);
+      const float l_o = get(other + 65 * 64 + lane);
+      const float ma = hf == 0 ? m_run : m_o, mb = hf == 0 ? m_o : m_run;
+      const float la = hf == 0 ? l_run : l_o, lb = hf == 0 ? l_o : l_run;
+      const float m_new = fmaxf(ma, mb);
+      const float wa = ma == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ma - m_new) * scale_log2);
+      const float wb = mb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mb - m_new) * scale_log2);
+      m_run = m_new;
+      l_run = __fadd_rn(__fmul_rn(la, wa), __fmul_rn(lb, wb));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float ov = get(other + (dt * 16 + j) * 64 + lane);
+          const float oa = hf == 0 ? oacc[dt][j] : ov, ob = hf == 0 ? ov : oacc[dt][j];
+          oacc[dt][j] = __fadd_rn(__fmul_rn(oa, wa), __fmul_rn(ob, wb));
+        }
+    }
+  }
+
   // ---- epilogue: combine the two lane halves' partial sums, normalise, and
   // store O through LDS so that every global store is a full 256-byte row.
   {
@@ -1449,17 +1530,28 @@ template <int NW, int NQ, bool F16, bool RASTER>
 hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void* v,
                      const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
                      void* o, float* lse, const void* gate, const float* oc,
-                     unsigned int* queues, int32_t* order, hipStream_t s) {
+                     unsigned int* queues, int32_t* order, TailSplit ts, hipStream_t s) {
   const int64_t rows = int64_t(g.batch) * g.heads * g.nb;
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * 1.4426950408889634f;
   int64_t grid = rows;
   const int32_t* claim_order = nullptr;
+  if (queues == nullptr || ts.flags == nullptr) ts.per_queue = 0;
+  {
+    // rows of the longest queue under the claim rule the kernel will use
+    const bool strided = row_ptr == nullptr && g.head_interleave;
+    const int64_t qmax =
+        strided ? int64_t((g.nb + 7) / 8) * g.batch * g.heads : (rows + 7) / 8;
+    if (qmax > kSplitMaxQueueRows) ts.per_queue = 0;
+  }
   if (queues != nullptr) {
-    // a quarter more workgroups than rows, so that each XCD can take up to
-    // 1.25 times its share; the counters are cleared first on the same stream
-    grid = rows + std::max<int64_t>(8, rows / 4);
-    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, s, queues);
+    // a quarter more workgroups than items (rows, plus one more for each
+    // split row), so that each XCD can take up to 1.25 times its share; the
+    // counters are cleared first on the same stream
+    const int64_t items = rows + split_slots_max(g, ts.per_queue);
+    grid = items + std::max<int64_t>(8, items / 4);
+    const int nflags = int(split_slots_max(g, ts.per_queue));
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(256), 0, s, queues, ts.flags, nflags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (row_ptr != nullptr && order != nullptr) {
@@ -1478,7 +1570,7 @@ hipError_t launch_nw(const VsaGeom& g, const void* q, const void* k, const void*
                      0, s, static_cast<const uint4*>(q), static_cast<const uint4*>(k),
                      static_cast<const uint4*>(v), row_ptr, col, uniform_k, nnz,
                      static_cast<uint4*>(o), lse, static_cast<const uint4*>(gate), oc, queues,
-                     claim_order, g, scale_log2, scale);
+                     claim_order, g, scale_log2, scale, ts);
   return hipGetLastError();
 }
 
@@ -1486,14 +1578,15 @@ template <bool RASTER>
 hipError_t launch_any(const VsaGeom& g, const void* q, const void* k, const void* v,
                       const int32_t* row_ptr, const int32_t* col, int uniform_k, int64_t nnz,
                       void* o, float* lse, const void* gate, const float* oc,
-                      unsigned int* queues, int32_t* order, hipStream_t s) {
+                      unsigned int* queues, int32_t* order, const TailSplit& ts,
+                      hipStream_t s) {
   auto launch = [&](auto nw, auto nq) {
     constexpr int NW = decltype(nw)::value, NQ = decltype(nq)::value;
     return g.dtype == VSA_DTYPE_FP16
                ? launch_nw<NW, NQ, true, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o,
-                                                 lse, gate, oc, queues, order, s)
+                                                 lse, gate, oc, queues, order, ts, s)
                : launch_nw<NW, NQ, false, RASTER>(g, q, k, v, row_ptr, col, uniform_k, nnz, o,
-                                                  lse, gate, oc, queues, order, s);
+                                                  lse, gate, oc, queues, order, ts, s);
   };
   using std::integral_constant;
   switch (g.vol / 32) {
@@ -1531,18 +1624,18 @@ hipError_t noalloc_scratch(void** ptr) {
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,
                            const int32_t* row_ptr, const int32_t* col, int uniform_k,
                            int64_t nnz, void* o, float* lse, unsigned int* queues,
-                           int32_t* order, hipStream_t s) {
+                           int32_t* order, const TailSplit& ts, hipStream_t s) {
   return launch_any<false>(g, q, k, vt, row_ptr, col, uniform_k, nnz, o, lse, nullptr, nullptr,
-                           queues, order, s);
+                           queues, order, ts, s);
 }
 
 hipError_t launch_attn_fwd_raster(const VsaGeom& g, const void* q, const void* k, const void* v,
                                   const int32_t* row_ptr, const int32_t* col, int uniform_k,
                                   int64_t nnz, void* o, float* lse, const void* gate,
                                   const float* oc, unsigned int* queues, int32_t* order,
-                                  hipStream_t s) {
+                                  const TailSplit& ts, hipStream_t s) {
   return launch_any<true>(g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc, queues,
-                          order, s);
+                          order, ts, s);
 }
 
 }  // namespace vsa

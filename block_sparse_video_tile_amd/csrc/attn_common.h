@@ -99,35 +99,58 @@ __device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
 // cheaper edge blocks last: the workgroups running at once on an XCD have
 // about equal cost (they stream the head's key blocks in step, which keeps
 // shared blocks in L2), and the rows left at the end of the kernel are the
-// cheap ones.  queues[8] hands out tickets and queues[x] counts the rows
+// cheap ones.  queues[8] hands out tickets and queues[x] counts the items
 // taken from queue x; all start at zero.  The launch has more workgroups
-// than rows; a workgroup whose ticket is below the row count takes the next
-// row of its own XCD's queue or, once that is empty, of the other queues in
-// turn, and the others leave at once.  Each XCD works through its share of
-// the workgroups as its CUs free up, so an XCD that runs faster takes more
-// rows.  A ticket holder always finds a row: a queue it finds empty stays
-// empty, and if all 8 were empty every row would already be held by one of
-// the fewer-than-nrows other ticket holders.  Thread 0 claims; the row
-// reaches the workgroup through LDS.  With `order` (block maps of their own
-// row lengths), position p of the queues is row order[p] instead of the
-// cost order above: the rows of each queue range in the claim order of a
-// block map (order_rows_kernel).
+// than items; a workgroup whose ticket is below the item count takes the
+// next item of its own XCD's queue or, once that is empty, of the other
+// queues in turn, and the others leave at once.  Each XCD works through its
+// share of the workgroups as its CUs free up, so an XCD that runs faster
+// takes more rows.  A ticket holder always finds an item: a queue it finds
+// empty stays empty, and if all 8 were empty every item would already be
+// held by one of the fewer-than-items other ticket holders.  Thread 0
+// claims; the row reaches the workgroup through LDS.  With `order` (block
+// maps of their own row lengths), position p of the queues is row order[p]
+// instead of the cost order above: the rows of each queue range in the claim
+// order of a block map (order_rows_kernel).
+//   Tail split (split > 0): the last s = min(count, split) rows of a queue
+// of `count` rows are handed out as two items each, their first and second
+// halves, one after the other; *part_sh receives 2 * slot + half for such an
+// item (slots numbered queue by queue, split_slots in all) and -1 for a
+// whole row.
+struct QueueItem {
+  uint32_t p;  // position of the row within its queue
+  int part;    // -1, or 2 * slot + half
+};
+__device__ inline QueueItem queue_item(uint32_t t, uint32_t count, uint32_t s, uint32_t slot0) {
+  if (t < count - s) return {t, -1};
+  const uint32_t u = t - (count - s);
+  return {count - s + u / 2, int(2 * (slot0 + u / 2) + (u & 1))};
+}
+
 __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const VsaGeom& g,
-                                    int64_t* row_sh, const int32_t* order = nullptr) {
+                                    int64_t* row_sh, const int32_t* order = nullptr,
+                                    uint32_t split = 0, int* part_sh = nullptr) {
   if (threadIdx.x == 0) {
     int64_t row = -1;
+    int part = -1;
     // rows number at most 2^30 (the plan's limit): 32-bit arithmetic
     const uint32_t n = uint32_t(nrows);
-    if (atomicAdd(&queues[8], 1u) < n) {
+    const uint32_t per = n / 8, rem = n % 8;
+    const uint32_t s_hi = min(split, per + 1), s_lo = min(split, per);
+    const uint32_t items = n + rem * s_hi + (8 - rem) * s_lo;
+    if (atomicAdd(&queues[8], 1u) < items) {
       const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
-      const uint32_t per = n / 8, rem = n % 8;
       for (int j = 0; j < 8; ++j) {
         const uint32_t x = (home + j) & 7;
         const uint32_t count = per + (x < rem ? 1 : 0);
         if (count == 0) continue;
+        const uint32_t s = x < rem ? s_hi : s_lo;
         const uint32_t t = atomicAdd(&queues[x], 1u);
-        if (t < count) {
-          const uint32_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + t;
+        if (t < count + s) {
+          const QueueItem it =
+              queue_item(t, count, s, x < rem ? x * s_hi : rem * s_hi + (x - rem) * s_lo);
+          part = it.part;
+          const uint32_t pos = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + it.p;
           const uint32_t nb = uint32_t(g.nb);
           if (order != nullptr) {
             // a permutation of the rows; anything else leaves the row undone
@@ -142,6 +165,7 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const V
       }
     }
     *row_sh = row;
+    if (part_sh != nullptr) *part_sh = part;
   }
   __syncthreads();
   return *row_sh;
@@ -152,29 +176,45 @@ __device__ inline int64_t claim_row(unsigned int* queues, int64_t nrows, const V
 // each work on a different head): queue x holds, for every head in turn, the
 // blocks at positions x, x+8, x+16, ... of the head's cost order, so all
 // XCDs work on the same one or two heads at a time and the blocks they
-// stream stay cached.  Same tickets, stealing and exit rule as claim_row.
+// stream stay cached.  Same tickets, stealing, exit rule and tail split as
+// claim_row; queue x here holds heads * ceil((nb - x) / 8) rows, so its
+// split slots are numbered from the sum over the queues before it.
 __device__ inline int64_t claim_row_strided(unsigned int* queues, int64_t nrows,
-                                            const VsaGeom& g, int64_t* row_sh) {
+                                            const VsaGeom& g, int64_t* row_sh,
+                                            uint32_t split = 0, int* part_sh = nullptr) {
   if (threadIdx.x == 0) {
     int64_t row = -1;
+    int part = -1;
     const uint32_t n = uint32_t(nrows);
     const uint32_t nb = uint32_t(g.nb), heads = n / nb;
-    if (atomicAdd(&queues[8], 1u) < n) {
+    uint32_t items = 0;
+    for (uint32_t x = 0; x < 8; ++x) {
+      const uint32_t count = (nb / 8 + (x < nb % 8 ? 1u : 0u)) * heads;
+      items += count + min(split, count);
+    }
+    if (atomicAdd(&queues[8], 1u) < items) {
       const int home = int(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u);  // HW_REG_XCC_ID
       for (int j = 0; j < 8; ++j) {
         const uint32_t x = (home + j) & 7;
         const uint32_t cx = nb / 8 + (x < nb % 8 ? 1u : 0u);   // positions of x per head
         const uint32_t count = cx * heads;
         if (count == 0) continue;
+        const uint32_t s = min(split, count);
         const uint32_t t = atomicAdd(&queues[x], 1u);
-        if (t < count) {
-          const uint32_t head = t / cx, p = (t % cx) * 8 + x;
+        if (t < count + s) {
+          uint32_t slot0 = 0;
+          for (uint32_t y = 0; y < x; ++y)
+            slot0 += min(split, (nb / 8 + (y < nb % 8 ? 1u : 0u)) * heads);
+          const QueueItem it = queue_item(t, count, s, slot0);
+          part = it.part;
+          const uint32_t head = it.p / cx, p = (it.p % cx) * 8 + x;
           row = int64_t(head) * nb + block_in_cost_order(g, int(p));
           break;
         }
       }
     }
     *row_sh = row;
+    if (part_sh != nullptr) *part_sh = part;
   }
   __syncthreads();
   return *row_sh;

@@ -49,7 +49,7 @@ bool misaligned(uintptr_t a, std::initializer_list<const void*> ptrs) {
 }
 
 struct Workspace {
-  size_t q, k, v, o, qp, kp, vp, oc, col, queue, total;
+  size_t q, k, v, o, qp, kp, vp, oc, col, queue, split, total;
 };
 
 Workspace workspace_layout(const vsa_plan_s& p) {
@@ -69,6 +69,7 @@ Workspace workspace_layout(const vsa_plan_s& p) {
   w.oc = off; off += align256(pooled);
   w.col = off; off += align256(col);
   w.queue = off; off += vsa::kAttnQueueBytes;
+  w.split = off; off += align256(vsa::split_layout(g).total);
   w.total = off;
   return w;
 }
@@ -76,7 +77,7 @@ Workspace workspace_layout(const vsa_plan_s& p) {
 // Workspace of the raster (gather-free) forward: pooled Q, K (and V and the
 // coarse output for the gated branch) and the selected block ids.
 struct FusedWorkspace {
-  size_t qp, kp, vp, oc, col, queue, total;
+  size_t qp, kp, vp, oc, col, queue, split, total;
 };
 FusedWorkspace fused_workspace_layout(const vsa_plan_s& p) {
   const VsaGeom& g = p.g;
@@ -90,6 +91,7 @@ FusedWorkspace fused_workspace_layout(const vsa_plan_s& p) {
   w.oc = off; off += align256(pooled);
   w.col = off; off += align256(col);
   w.queue = off; off += vsa::kAttnQueueBytes;
+  w.split = off; off += align256(vsa::split_layout(g).total);
   w.total = off;
   return w;
 }
@@ -412,9 +414,23 @@ vsa_status check_raster_args(const char* fn, vsa_plan_t p, const void* gate, con
 }
 
 // Workspace of the balanced attention launches: the row-queue counters, then
-// one int32 per row for the claim order of a block map's rows.
+// one int32 per row for the claim order of a block map's rows, then the
+// tail-split region (counters, rows, and the halves' partial results).
+size_t attn_order_bytes(const VsaGeom& g) { return align256(size_t(g.batch) * g.heads * g.nb * 4); }
 size_t attn_ws_bytes(const VsaGeom& g) {
-  return vsa::kAttnQueueBytes + align256(size_t(g.batch) * g.heads * g.nb * 4);
+  return vsa::kAttnQueueBytes + attn_order_bytes(g) + align256(vsa::split_layout(g).total);
+}
+// The three parts of a balanced launch's workspace (or of the fixed scratch).
+struct AttnWs {
+  unsigned int* queues;
+  int32_t* order;
+  vsa::TailSplit split;
+};
+AttnWs attn_ws_at(const VsaGeom& g, void* ws, size_t order_bytes) {
+  char* b = static_cast<char*>(ws);
+  return AttnWs{reinterpret_cast<unsigned int*>(b),
+                reinterpret_cast<int32_t*>(b + vsa::kAttnQueueBytes),
+                vsa::split_at(g, b + vsa::kAttnQueueBytes + order_bytes)};
 }
 
 vsa_status check_queue_workspace(const char* fn, vsa_plan_t p, void* ws, size_t ws_bytes) {
@@ -439,7 +455,7 @@ vsa_status vsa_block_sparse_attn_fwd(vsa_plan_t p, const void* q, const void* k,
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
   return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                                         nullptr, nullptr, hipStream_t(stream)),
+                                         nullptr, nullptr, vsa::TailSplit{}, hipStream_t(stream)),
                     fn);
 }
 
@@ -457,12 +473,10 @@ vsa_status vsa_block_sparse_attn_fwd_ws(vsa_plan_t p, const void* q, const void*
   if (vsa_status st = check_attn_args(fn, p, q, k, v, row_ptr, col, uniform_k, nnz, o)) return st;
   if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_queue_workspace(fn, p, ws, ws_bytes)) return st;
-  return hip_status(
-      vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                           static_cast<unsigned int*>(ws),
-                           reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
-                           hipStream_t(stream)),
-      fn);
+  const AttnWs a = attn_ws_at(p->g, ws, attn_order_bytes(p->g));
+  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                         a.queues, a.order, a.split, hipStream_t(stream)),
+                    fn);
 }
 
 vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const void* k,
@@ -484,12 +498,15 @@ vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t p, const void* q, const 
   void* ws = nullptr;
   if (hipError_t e = vsa::noalloc_scratch(&ws); e != hipSuccess)
     return hip_status(e, "vsa_block_sparse_attn_fwd_noalloc: scratch address");
-  return hip_status(
-      vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
-                           static_cast<unsigned int*>(ws),
-                           reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
-                           hipStream_t(stream)),
-      fn);
+  // the split region follows the order array of kNoAllocMaxMapRows rows; it
+  // is sized for 8 x kSplitPerQueue slots of 8-wave halves, every plan's most
+  if (vsa::split_layout(p->g).total > vsa::kNoAllocSplitBytes)
+    return fail(VSA_ERR_UNSUPPORTED, "%s: tail-split region of %zu bytes exceeds the scratch's %zu",
+                fn, vsa::split_layout(p->g).total, vsa::kNoAllocSplitBytes);
+  const AttnWs a = attn_ws_at(p->g, ws, size_t(vsa::kNoAllocMaxMapRows) * 4);
+  return hip_status(vsa::launch_attn_fwd(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse,
+                                         a.queues, a.order, a.split, hipStream_t(stream)),
+                    fn);
 }
 
 vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const void* k,
@@ -503,7 +520,7 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t p, const void* q, const v
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
                                                 lse, gate, oc, nullptr, nullptr,
-                                                hipStream_t(stream)),
+                                                vsa::TailSplit{}, hipStream_t(stream)),
                     fn);
 }
 
@@ -518,13 +535,11 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t p, const void* q, cons
   if (vsa_status st = check_lse(fn, lse)) return st;
   if (vsa_status st = check_raster_args(fn, p, gate, oc)) return st;
   if (vsa_status st = check_queue_workspace(fn, p, ws, ws_bytes)) return st;
-  return hip_status(
-      vsa::launch_attn_fwd_raster(
-          p->g, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, gate, oc,
-          static_cast<unsigned int*>(ws),
-          reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vsa::kAttnQueueBytes),
-          hipStream_t(stream)),
-      fn);
+  const AttnWs a = attn_ws_at(p->g, ws, attn_order_bytes(p->g));
+  return hip_status(vsa::launch_attn_fwd_raster(p->g, q, k, v, row_ptr, col, uniform_k, nnz, o,
+                                                lse, gate, oc, a.queues, a.order, a.split,
+                                                hipStream_t(stream)),
+                    fn);
 }
 
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t p, size_t* bytes) {
@@ -631,8 +646,7 @@ vsa_status vsa_forward(vsa_plan_t p, const void* q, const void* k, const void* v
     return hip_status(e, "vsa_forward: score/top-k");
   unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
   if ((e = vsa::launch_attn_fwd(g, qb, kb, vb, nullptr, col, p->topk, nnz, ob, lse, queues,
-                                nullptr, s)) !=
-      hipSuccess)
+                                nullptr, vsa::split_at(g, base + w.split), s)) != hipSuccess)
     return hip_status(e, "vsa_forward: attention");
   if (gate && (e = vsa::launch_compress_attn(g, qp, kp, vp, oc, s)) != hipSuccess)
     return hip_status(e, "vsa_forward: coarse attention");
@@ -694,7 +708,8 @@ vsa_status vsa_forward_fused(vsa_plan_t p, const void* q, const void* k, const v
   }
   unsigned int* queues = reinterpret_cast<unsigned int*>(base + w.queue);
   if ((e = vsa::launch_attn_fwd_raster(g, q, k, v, nullptr, col, p->topk, nnz, out, lse, gate,
-                                       gate ? oc : nullptr, queues, nullptr, s)) != hipSuccess)
+                                       gate ? oc : nullptr, queues, nullptr,
+                                       vsa::split_at(g, base + w.split), s)) != hipSuccess)
     return hip_status(e, "vsa_forward_fused: attention");
   return ok();
 }

@@ -249,22 +249,36 @@ vsa_status vsa_block_sparse_attn_fwd_raster(vsa_plan_t plan, const void* q, cons
                                             void* stream);
 
 /* Balanced launches of the two attention forwards above: the same operation
- * and the same arguments, bit-identical results, plus a small device
- * workspace.  Instead of a fixed row per workgroup, each workgroup of a
- * launch with a quarter more workgroups than rows takes the next row from
- * one of 8 row queues (one per XCD, each a contiguous range of rows, i.e.
- * whole heads): its own XCD's queue, or once that is empty the others', and
- * the workgroups left over when every row is taken exit at once.  XCDs that
- * run faster thus finish more rows and the kernel does not wait for the
- * slowest one.  Within a head the queue hands out the query blocks in cost
- * order: blocks the grid edge does not cut first, then the edge blocks by
- * descending valid-token count, so the workgroups running together cost
- * about the same (they share key blocks in L2) and the cheap rows come last.  The queue counters live in the workspace and are cleared
- * by a kernel on `stream` before the attention kernel, so the workspace needs
- * no initialisation; it must not be used by another call while this one runs
+ * and the same arguments, plus a device workspace.  Instead of a fixed row
+ * per workgroup, each workgroup of a launch with a quarter more workgroups
+ * than rows takes the next row from one of 8 row queues (one per XCD, each a
+ * contiguous range of rows, i.e. whole heads): its own XCD's queue, or once
+ * that is empty the others', and the workgroups left over when every row is
+ * taken exit at once.  XCDs that run faster thus finish more rows and the
+ * kernel does not wait for the slowest one.  Within a head the queue hands
+ * out the query blocks in cost order: blocks the grid edge does not cut
+ * first, then the edge blocks by descending valid-token count, so the
+ * workgroups running together cost about the same (they share key blocks in
+ * L2) and the cheap rows come last; a block map's rows are handed out long
+ * rows first, then head by head by entry count.
+ * Tail split: when no queue holds more than 256 rows (a launch of a few
+ * rounds of rows per CU, such as one GPU's share of a head-sharded layer),
+ * the last min(16, rows of the queue) rows of each queue are handed out as
+ * two halves, the first and the second half of the row's entries, each
+ * computed by its own workgroup; each half leaves its unnormalised output,
+ * running max and sum in the workspace and the half that finishes second
+ * merges the two (the softmax merge of two key sets) and writes the row.
+ * Rows handed out whole are bit-identical to the unbalanced launch; split
+ * rows sum in another order and agree with it to within the last bit of the
+ * element type, independently of which half finishes last.
+ * The queue and split counters live in the workspace and are cleared by a
+ * kernel on `stream` before the attention kernel, so the workspace needs no
+ * initialisation; it must not be used by another call while this one runs
  * (concurrent calls need their own workspaces).
- * vsa_attn_fwd_workspace_size writes the bytes needed (a few hundred, the
- *   same for every plan).
+ * vsa_attn_fwd_workspace_size writes the bytes needed: 256 bytes of queue
+ *   counters, 4 bytes per row (the claim order of a block map), and the
+ *   split region (8 bytes per split slot plus two halves of waves x 16.5 KB,
+ *   at most 128 slots: 34.6 MB for 256-token blocks), each 256-byte aligned.
  * ws: device memory, 256-byte aligned, ws_bytes at least that size; owned by
  *   the caller.
  * Errors: as the unbalanced entry points, plus INVALID_ARGUMENT for a null,
@@ -284,10 +298,12 @@ vsa_status vsa_block_sparse_attn_fwd_raster_ws(vsa_plan_t plan, const void* q, c
 
 /* vsa_block_sparse_attn_fwd_ws without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight serving
- * loops, harnesses that forbid hipMalloc).  The row-queue counters live in a
- * library-owned static device array of 256 bytes per GPU, which stays
- * allocated until the process ends; the call itself allocates nothing and
- * clears the counters with a small kernel on `stream` (no memset).  Every
+ * loops, harnesses that forbid hipMalloc).  The row-queue counters, the claim
+ * order of a block map of at most 65536 rows and the tail-split region of at
+ * most 128 slots live in a library-owned static device array of 34.9 MB per
+ * GPU, which stays allocated until the process ends; the call itself
+ * allocates nothing and clears the counters with a small kernel on `stream`
+ * (no memset); its results equal vsa_block_sparse_attn_fwd_ws bit for bit.  Every
  * call on a GPU shares that GPU's array: calls that may overlap on one GPU
  * (other streams or threads without ordering between them) race and must be
  * serialised by the caller.  Arguments, outputs and errors as
@@ -332,8 +348,9 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t plan, const void* q_blk, const v
                                      size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace vsa_forward needs for this plan (blocked Q, K,
- * V, O, pooled Q, K and V, the coarse output, the selected block ids and the
- * row queues of the balanced attention launch, each 256-byte aligned). */
+ * V, O, pooled Q, K and V, the coarse output, the selected block ids, and the
+ * row queues and tail-split region of the balanced attention launch, each
+ * 256-byte aligned). */
 vsa_status vsa_forward_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path for a plan with topk >= 1, raster in and raster out:
@@ -357,7 +374,8 @@ vsa_status vsa_forward(vsa_plan_t plan, const void* q, const void* k, const void
 
 /* Bytes of device workspace vsa_forward_fused needs for this plan (pooled Q,
  * K and V, the coarse output, the selected block ids and the attention row
- * queues, each 256-byte aligned; no blocked copies of the tensors). */
+ * queues and tail-split region, each 256-byte aligned; no blocked copies of
+ * the tensors). */
 vsa_status vsa_forward_fused_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* The whole hot path without the gather and scatter passes: the block means

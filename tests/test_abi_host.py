@@ -235,7 +235,7 @@ def test_raster_attention_and_fused_forward_checks(plan):
     need = vsa.vsa_forward_fused_workspace_size(plan)
     info = plan.info
     assert need % 256 == 0
-    assert 4 * info["pooled_elems"] * 4 <= need < info["blocked_elems"] * 2
+    assert 4 * info["pooled_elems"] * 4 <= need < info["blocked_elems"] * 2 + _split_region_bytes(plan)
     g = "vsa_forward_fused"   # (plan, q, k, v, gate, out, ws, ws_bytes, col_out, lse, stream)
     assert _raw(g, h, FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, None, None, None) == bad
     assert _raw(g, h, FAKE, FAKE, FAKE, None, FAKE, FAKE + 16, need, None, None, None) == bad
@@ -247,6 +247,25 @@ def test_raster_attention_and_fused_forward_checks(plan):
     assert _raw("vsa_gather", h, 2, FAKE, None, None, None) == bad
 
 
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
+def _split_region_bytes(p):
+    """Tail-split part of a balanced launch's workspace, from its rule: the
+    last min(rows of the queue, 16) rows of each of the 8 queues are split,
+    under either queue cut; a counter and a row id per slot, and two halves
+    of (O^T, m, l) per slot (waves x 66 x 64 fp32)."""
+    rows, nb, heads = p.num_rows(), p.num_blocks, p.batch * p.heads
+    per, rem = divmod(rows, 8)
+    plain = rem * min(16, per + 1) + (8 - rem) * min(16, per)
+    strided = sum(min(16, (nb // 8 + (x < nb % 8)) * heads) for x in range(8))
+    slots = max(plain, strided)
+    vol = p.padded_len // nb
+    waves = 4 if vol == 64 else vol // 32
+    return _a256(2 * _a256(slots * 4) + slots * 2 * waves * 66 * 64 * 4)
+
+
 def test_balanced_attention_workspace_checks(plan):
     """The balanced (queued) attention launches: a fixed small workspace, the
     same argument checks as the plain entry points, and a null, short or
@@ -254,12 +273,15 @@ def test_balanced_attention_workspace_checks(plan):
     h = plan.handle
     bad = vsa.VSA_ERR_INVALID_ARGUMENT
     need = vsa.vsa_attn_fwd_workspace_size(plan)
-    # 9 row-queue counters (256 bytes), then one int32 per row for the
-    # longest-first order of a block map, 256-byte aligned
+    # 9 row-queue counters (256 bytes), then one int32 per row for the claim
+    # order of a block map, then the tail split: a counter and a row per
+    # split slot, and two halves of (O^T, m, l) per slot (waves x 66 x 64
+    # fp32), each part 256-byte aligned.  A queue splits min(its rows, 16).
     rows = plan.num_rows()
-    assert need == 256 + (rows * 4 + 255) // 256 * 256
+    assert need == 256 + _a256(rows * 4) + _split_region_bytes(plan)
     big = vsa.vsa_plan(27280, (31, 22, 40), (4, 8, 8), batch=1, num_heads=24, topk=64)
-    assert vsa.vsa_attn_fwd_workspace_size(big) == 256 + 2880 * 4   # 11520 = 45 * 256
+    # 2880 rows: 128 split slots of 8-wave halves
+    assert vsa.vsa_attn_fwd_workspace_size(big) == 256 + 11520 + 1024 + 128 * 2 * 135168
     f = "vsa_block_sparse_attn_fwd_ws"
     # (plan, q, k, v, row_ptr, col, uniform_k, nnz, o, lse, ws, ws_bytes, stream)
     ok_args = (FAKE, FAKE, FAKE, None, FAKE, 4, rows * 4, FAKE, None)

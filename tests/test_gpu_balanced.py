@@ -1,9 +1,16 @@
 """GPU parity of the balanced attention launches (vsa_block_sparse_attn_fwd_ws
 and vsa_block_sparse_attn_fwd_raster_ws): workgroups claim their rows from
-per-XCD queues instead of taking a fixed row, and every row is computed
-exactly as before, so O and LSE must equal the plain launches bit for bit.
-The plain launches are compared with the oracle elsewhere; one small case
-here is also compared with the oracle directly.  Cases: every
+per-XCD queues instead of taking a fixed row.  Every row the queues hand
+out whole is computed exactly as before, so its O and LSE must equal the
+plain launches bit for bit; the rows split in halves at the end of each
+queue (the tail split, for launches of at most 256 rows per queue: each
+half computed by its own workgroup over half of the row's entries, then
+merged) sum in another order, so theirs must
+agree to within the last bit of the element type (|a - b| <= 2^-7 max(1,
+|b|)) and LSE to 1e-4.  The split rows are read from the workspace, where
+each merge records its row; their number must be the launch's split slot
+count.  The plain launches are compared with the oracle elsewhere; the
+small cases here are also compared with the oracle directly.  Cases: every
 workgroup size (2, 4, 6 and 8 waves), both element types, CSR maps with
 empty rows and rows longer than one LDS list pass, raster inputs with and
 without the gate, a workspace left full of junk, and repeated calls.
@@ -93,14 +100,89 @@ def _check_claim_order(ws, rp_h, nb, what):
     _say(f"    {what}: claim order of {rows} rows as expected")
 
 
-def _assert_same(a, b, what):
-    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16)), f"{what}: O differs"
-    assert torch.equal(a[1], b[1]), f"{what}: LSE differs"
+_SPLIT_PER_QUEUE = 16
+
+
+def _a256(n):
+    return (n + 255) & ~255
+
+
+_SPLIT_MAX_QUEUE_ROWS = 256
+
+
+def _split_slots(plan, strided):
+    """Split slots of a launch, from the rule: the last min(count, 16) rows of
+    each of the 8 queues; the queues cut the rows as the XCD ranges do, or
+    (heads interleaved) queue x holds heads * ceil((nb - x) / 8) rows; none
+    when the longest queue holds more than 256 rows."""
+    heads, nb = plan.batch * plan.heads, plan.num_blocks
+    if strided:
+        counts = [(nb // 8 + (1 if x < nb % 8 else 0)) * heads for x in range(8)]
+    else:
+        per, rem = divmod(heads * nb, 8)
+        counts = [per + (1 if x < rem else 0) for x in range(8)]
+    if max(counts) > _SPLIT_MAX_QUEUE_ROWS:
+        return 0
+    return sum(min(_SPLIT_PER_QUEUE, c) for c in counts)
+
+
+def _split_cap(plan):
+    """Slots the workspace holds (either queue cut, no length limit)."""
+    heads, nb = plan.batch * plan.heads, plan.num_blocks
+    per, rem = divmod(heads * nb, 8)
+    plain = sum(min(_SPLIT_PER_QUEUE, per + (1 if x < rem else 0)) for x in range(8))
+    strided = sum(min(_SPLIT_PER_QUEUE, (nb // 8 + (1 if x < nb % 8 else 0)) * heads)
+                  for x in range(8))
+    return max(plain, strided)
+
+
+def _split_rows(ws, plan, strided=False):
+    """Rows the last launch on `ws` split (recorded by their merges), checked
+    against the slot count of the rule."""
+    rows = plan.num_rows()
+    cap = _split_cap(plan)
+    off = _ORDER_OFFSET + _a256(rows * 4) + _a256(cap * 4)
+    got = ws[off:off + 4 * cap].cpu().view(torch.int32).numpy().astype(np.int64)
+    n = _split_slots(plan, strided)
+    used = got[:n]
+    assert np.all((used >= 0) & (used < rows)), "split slot without a valid row"
+    assert len(np.unique(used)) == n, "a row split twice"
+    return used
+
+
+def _assert_same(a, b, what, split_rows=(), plan=None):
+    """a: plain launch, b: balanced; blocked O [B,NH,Npad,D] and LSE [B,NH,Npad]."""
+    oa, ob = a[0].view(torch.int16), b[0].view(torch.int16)
+    la, lb = a[1], b[1]
+    if len(split_rows) == 0:
+        assert torch.equal(oa, ob), f"{what}: O differs"
+        assert torch.equal(la, lb), f"{what}: LSE differs"
+        return
+    nb, heads = plan.num_blocks, plan.heads
+    vol = plan.padded_len // nb
+    mask = torch.zeros((plan.batch, heads, plan.padded_len), dtype=torch.bool)
+    for r in split_rows:
+        bb, rem = divmod(int(r), heads * nb)
+        h, i = divmod(rem, nb)
+        mask[bb, h, i * vol:(i + 1) * vol] = True
+    mask = mask.to(oa.device)
+    assert torch.equal(oa[~mask], ob[~mask]), f"{what}: O of a whole row differs"
+    assert torch.equal(la[~mask], lb[~mask]), f"{what}: LSE of a whole row differs"
+    fa, fb = a[0][mask].float(), b[0][mask].float()
+    tol = 2.0 ** -7 * torch.clamp(fb.abs(), min=1.0)
+    assert bool(((fa - fb).abs() <= tol).all()), f"{what}: O of a split row beyond the last bit"
+    sa, sb = la[mask], lb[mask]
+    assert torch.equal(torch.isinf(sa), torch.isinf(sb)), f"{what}: LSE -inf differs"
+    fin = torch.isfinite(sb)
+    if bool(fin.any()):
+        assert float((sa[fin] - sb[fin]).abs().max()) <= 1e-4, f"{what}: LSE of a split row"
+    _say(f"    {what}: {len(split_rows)} split rows within the last bit, the rest bitwise")
 
 
 @pytest.mark.parametrize("name,dtype", [("wan5b_k64", vsa.VSA_DTYPE_BF16),
                                         ("wan5b_k64", vsa.VSA_DTYPE_FP16),
-                                        ("wan13b_long", vsa.VSA_DTYPE_BF16)])
+                                        ("wan13b_long", vsa.VSA_DTYPE_BF16),
+                                        ("wan5b_k64_h3", vsa.VSA_DTYPE_BF16)])
 def test_full_size_blocked_equals_plain_launch(name, dtype):
     wl = WORKLOADS[name]
     plan = _plan(wl, dtype=dtype)
@@ -109,11 +191,14 @@ def test_full_size_blocked_equals_plain_launch(name, dtype):
     col = _selection(plan, wl, qp, kp)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, ws)
-    _assert_same(plain, bal, name)
+    strided = name == "wan13b_long"   # its heads' K and V outgrow the memory-side cache
+    split = _split_rows(ws, plan, strided)
+    _assert_same(plain, bal, name, split, plan)
     # a second call on the same workspace (its counters now hold the last
-    # call's counts) gives the same result again
+    # call's counts) gives the same result again, bit for bit
     again = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, ws)[1]
-    _assert_same(plain, again, f"{name} repeated")
+    assert np.array_equal(_split_rows(ws, plan, strided), split)
+    _assert_same(bal, again, f"{name} repeated")
     _say(f"    {name}: balanced == plain, {plan.num_rows()} rows")
 
 
@@ -126,8 +211,9 @@ def test_small_volumes_equal_plain_launch_and_oracle(name):
     ref = oracle.vsa_reference(*(bf16_to_f64(t) for t in (q, kk, v)), wl.dit_seq_shape,
                                wl.block_size, wl.topk)
     col = torch.as_tensor(ref["col_idx"], dtype=torch.int32).to(DEV)
-    plain, bal = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, _junk_workspace(plan))
-    _assert_same(plain, bal, name)
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, ws)
+    _assert_same(plain, bal, name, _split_rows(ws, plan), plan)
     oplan = ref["plan"]
     mx, mean, lerr = _compare_rows(oplan, _host(bal[0]), _host(bal[1]), ref["out"], ref["lse"],
                                    range(plan.num_rows()), wl.heads, oplan.block_volume)
@@ -146,7 +232,7 @@ def test_csr_maps_with_empty_rows(name):
     col = torch.as_tensor(ci_h, dtype=torch.int32).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
-    _assert_same(plain, bal, name)
+    _assert_same(plain, bal, name, _split_rows(ws, plan), plan)
     _check_claim_order(ws, rp_h, plan.info["num_blocks"], name)
 
 
@@ -165,7 +251,7 @@ def test_rows_longer_than_one_list_pass():
     col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
-    _assert_same(plain, bal, "long rows")
+    _assert_same(plain, bal, "long rows", _split_rows(ws, plan), plan)
     _check_claim_order(ws, rp_h, nt, "long rows")
 
 
@@ -189,7 +275,7 @@ def test_claim_order_across_heads():
     col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
-    _assert_same(plain, bal, "order across heads")
+    _assert_same(plain, bal, "order across heads", _split_rows(ws, plan), plan)
     _check_claim_order(ws, rp_h, nt, "order across heads")
 
 
@@ -214,7 +300,7 @@ def test_claim_order_of_ranges_longer_than_the_length_cache():
     col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
-    _assert_same(plain, bal, "long ranges")
+    _assert_same(plain, bal, "long ranges", _split_rows(ws, plan), plan)
     _check_claim_order(ws, rp_h, nt, "long ranges")
 
 
@@ -250,4 +336,33 @@ def test_raster_equals_plain_raster_launch(gated):
                                                  out, lse, gate=gate, o_coarse=oc)
         res.append((out, lse))
     torch.cuda.synchronize()
-    _assert_same(res[0], res[1], f"raster gated={gated}")
+    split = _split_rows(ws, plan)
+    # O is raster [B,S,NH,D]: the tokens of the split rows' query blocks may
+    # differ in the last bit, every other token must be equal bit for bit
+    lists = oracle.block_token_lists(oracle.make_plan(wl.seq_len, wl.dit_seq_shape,
+                                                      wl.block_size))
+    nb = plan.num_blocks
+    mask = torch.zeros((plan.batch, wl.seq_len, plan.heads), dtype=torch.bool)
+    for r in split:
+        bb, rem = divmod(int(r), plan.heads * nb)
+        h, i = divmod(rem, nb)
+        mask[bb, torch.as_tensor(lists[i]), h] = True
+    mask = mask.to(DEV)
+    oa, ob = res[0][0], res[1][0]
+    assert torch.equal(oa[~mask], ob[~mask]), f"raster gated={gated}: O of a whole row differs"
+    fa, fb = oa[mask].float(), ob[mask].float()
+    assert bool(((fa - fb).abs() <= 2.0 ** -7 * torch.clamp(fb.abs(), min=1.0)).all())
+    # LSE keeps the blocked row order
+    rows_mask = torch.zeros(plan.num_rows(), dtype=torch.bool)
+    rows_mask[torch.as_tensor(split)] = True
+    vol = plan.padded_len // nb
+    tok_mask = rows_mask.repeat_interleave(vol).view(plan.batch, plan.heads, plan.padded_len)
+    tok_mask = tok_mask.to(DEV)
+    la, lb = res[0][1], res[1][1]
+    assert torch.equal(la[~tok_mask], lb[~tok_mask])
+    sa, sb = la[tok_mask], lb[tok_mask]
+    assert torch.equal(torch.isinf(sa), torch.isinf(sb))
+    fin = torch.isfinite(sb)
+    if bool(fin.any()):
+        assert float((sa[fin] - sb[fin]).abs().max()) <= 1e-4
+    _say(f"    raster gated={gated}: {len(split)} split rows within the last bit, the rest bitwise")

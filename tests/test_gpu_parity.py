@@ -268,6 +268,14 @@ def test_full_size_forward_every_row(name, k):
     check_full_forward(name, k)
 
 
+def test_head_shard_with_split_rows_every_row():
+    """One GPU's share of an 8-way head shard of the 27280-token layer (3
+    heads, 360 rows): the balanced launch splits the last 16 rows of each
+    queue into halves merged across workgroups; every row of all three heads
+    against the float32 and the float64 oracle."""
+    check_full_forward("wan5b_k64_h3", fp64_heads=(0, 1, 2))
+
+
 def test_full_size_attention_fed_oracle_map_every_row():
     """Attention fed the float64 oracle's own selection (not the GPU's), every row."""
     wl = WORKLOADS["wan5b_k64"]

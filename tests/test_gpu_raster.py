@@ -222,6 +222,6 @@ def test_fused_forward_gated(name, dtype):
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
 
 
-@pytest.mark.parametrize("name", ["wan5b_k64", "wan13b_long"])
+@pytest.mark.parametrize("name", ["wan5b_k64", "wan13b_long", "wan5b_k64_h3"])
 def test_fused_forward_full_size_every_row(name):
     check_full_forward(name, fused=True)
