@@ -194,9 +194,63 @@ __device__ inline void scan_counts(int* cnt, int m, int* total, int wave, int la
 __device__ inline void slot_fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin_v(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
-// Clears the row-queue counters of the balanced launches (claim_row).
-__global__ void bwd_queue_reset_kernel(unsigned int* queues) {
+// Clears the row-queue counters and the tail-split counters of the balanced
+// launches (claim_row).
+__global__ void bwd_queue_reset_kernel(unsigned int* queues, unsigned int* flags, int nflags) {
   if (threadIdx.x < 9) queues[threadIdx.x] = 0u;
+  for (int x = threadIdx.x; x < nflags; x += blockDim.x) flags[x] = 0u;
+}
+
+// Tail split of the balanced launches (the rule of the forward's, TailSplit):
+// with at most 256 rows per queue, the last rows of each queue are handed out
+// as two halves of their entries, so that the kernel's last round is made of
+// half rows.  A gradient row is a plain sum over the entries, so the halves
+// merge by addition: each half stores its accumulators (NT = 4 or 8 tiles
+// per lane of every wave holding rows) with device-coherent stores (relaxed
+// agent-scope atomics, past the XCD's non-coherent L2; a fence would write
+// back or invalidate the whole L2 under the other workgroups), drains them,
+// and counts itself done; the half that counts second adds the other's
+// partial, a + b (the same bits whichever half adds), and writes the rows.
+// Returns false for the half that finished first, which then leaves.
+template <int NW, bool TWO>
+__device__ __attribute__((always_inline)) inline bool bwd_tail_merge(
+    unsigned int* flags, int32_t* ids, float* parts, int part, int wave, int lane, bool holds,
+    f32x16 (&a)[4], f32x16 (&b)[4], int64_t id, unsigned int* done_sh) {
+  const int slot = part >> 1, hf = part & 1;
+  float* const mine = parts + (size_t(2 * slot + hf) * NW + wave) * kBwdSplitHalfFloatsPerWave;
+  if (holds) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        __hip_atomic_store(mine + (dt * 16 + j) * 64 + lane, a[dt][j], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (TWO)
+          __hip_atomic_store(mine + (64 + dt * 16 + j) * 64 + lane, b[dt][j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) *done_sh = atomicAdd(&flags[slot], 1u);
+  __syncthreads();
+  if (*done_sh == 0) return false;
+  if (threadIdx.x == 0) ids[slot] = int32_t(id);
+  float* const other =
+      parts + (size_t(2 * slot + (1 - hf)) * NW + wave) * kBwdSplitHalfFloatsPerWave;
+  if (holds) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        a[dt][j] += __hip_atomic_load(other + (dt * 16 + j) * 64 + lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (TWO)
+          b[dt][j] += __hip_atomic_load(other + (64 + dt * 16 + j) * 64 + lane,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  return true;
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -252,13 +306,15 @@ __device__ inline ev8 tr_operand(const uint4* tile, int off) {
 
 // ------------------------------------------------------------------ dQ
 
-template <int NW, bool F16>
+template <int NW, bool F16, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dsum, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ col, int uniform_k, int64_t nnz, uint4* __restrict__ dq,
-    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale) {
+    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale,
+    unsigned int* __restrict__ split_flags, int32_t* __restrict__ split_ids,
+    float* __restrict__ split_part, int tail_split) {
   constexpr int kThreads = NW * 64;
   constexpr int kPassTiles = kPassEntries * (NW / 2);  // <= vol/64 sub-tiles per block
   // two buffer sets: K rows and V rows (kappa, padded); K^T is read from the
@@ -272,9 +328,15 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
   __shared__ int ntl;
   const int64_t nrows = int64_t(g.batch) * g.heads * g.nb;
   __shared__ int64_t row_sh;   // row claimed from the queues (balanced launch)
-  const int64_t r = queues != nullptr ? claim_row(queues, nrows, g, &row_sh)
-                                      : xcd_remap(blockIdx.x, nrows);
+  __shared__ int part_sh;      // -1, or 2 * split slot + half
+  __shared__ unsigned int done_sh;
+  const int64_t r = queues != nullptr
+                        ? claim_row(queues, nrows, g, &row_sh, nullptr, SPLIT ? uint32_t(tail_split) : 0u,
+                                    SPLIT ? &part_sh : nullptr)
+                        : xcd_remap(blockIdx.x, nrows);
   if (r < 0) return;
+  // -1 (whole), or 2 * split slot + half; SPLIT: the launch splits rows
+  const int part = SPLIT && queues != nullptr ? part_sh : -1;  // workgroup-uniform
   const int i = int(r % g.nb);
   const int64_t bh = r / g.nb;
   const int cq = block_count(g, i);
@@ -421,6 +483,12 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
 
   int64_t beg, end;
   row_bounds(row_ptr, uniform_k, nnz, r, beg, end);
+  if (part >= 0) {
+    // a half of a split row: the first or the second half of its entries
+    const int64_t mid = beg + (end - beg) / 2;
+    if (part & 1) beg = mid;
+    else end = mid;
+  }
   // the passes are compiled twice (full and key-half waves), each with its
   // own register allocation
   auto passes = [&](auto hv) __attribute__((always_inline)) {
@@ -495,6 +563,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(
         for (int j = 0; j < 16; ++j) acc[dt][j] = 0.f;
     }
   }
+  if (SPLIT && part >= 0 && !bwd_tail_merge<NW, false>(split_flags, split_ids, split_part, part, wave,
+                                                lane, active && !own_pad, acc, acc, r, &done_sh))
+    return;
   // dQ rows (this wave's own 32 rows); pad query rows are written as zero
   store_rows_perm<F16>(acc, row_valid && !own_pad ? scale : 0.f, dq + (row0 + wave * 32) * 16, l32,
                   half);
@@ -541,13 +612,15 @@ __device__ inline uint32_t qtile_off(int pos) {
 // 0, so pad keys need no masking.
 // Edge key blocks of 5 or 6 key groups split waves 4..7 by query halves, as
 // the separate kernels did.
-template <int NW, bool F16>
+template <int NW, bool F16, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     const uint4* __restrict__ q, const uint4* __restrict__ k, const uint4* __restrict__ v,
     const uint4* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ dsum, const int32_t* __restrict__ tlist,
     const int32_t* __restrict__ tcount, uint4* __restrict__ dk, uint4* __restrict__ dv,
-    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale) {
+    unsigned int* __restrict__ queues, VsaGeom g, float scale_log2, float scale,
+    unsigned int* __restrict__ split_flags, int32_t* __restrict__ split_ids,
+    float* __restrict__ split_part, int tail_split) {
   constexpr int kThreads = NW * 64;
   constexpr int kEntries = kPassEntries / 2;       // query blocks per pass
   constexpr int kTiles = kEntries * (NW / 2);      // <= vol/64 sub-tiles per query block
@@ -568,9 +641,15 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
                 "the fused kernel's LDS must fit one CU");
   const int64_t ncols = int64_t(g.batch) * g.heads * g.nb;
   __shared__ int64_t col_sh;  // column claimed from the queues (balanced launch)
-  const int64_t c = queues != nullptr ? claim_row(queues, ncols, g, &col_sh)
-                                      : xcd_remap(blockIdx.x, ncols);
+  __shared__ int part_sh;     // -1, or 2 * split slot + half
+  __shared__ unsigned int done_sh;
+  const int64_t c = queues != nullptr
+                        ? claim_row(queues, ncols, g, &col_sh, nullptr, SPLIT ? uint32_t(tail_split) : 0u,
+                                    SPLIT ? &part_sh : nullptr)
+                        : xcd_remap(blockIdx.x, ncols);
   if (c < 0) return;
+  // -1 (whole), or 2 * split slot + half; SPLIT: the launch splits rows
+  const int part = SPLIT && queues != nullptr ? part_sh : -1;  // workgroup-uniform
   const int j = int(c % g.nb);
   const int64_t bh = c / g.nb;
   const int cj = block_count(g, j);
@@ -744,10 +823,17 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
     for (int hs = hs_lo; hs <= hs_hi; ++hs) half_tile(hs, qsb, dsb, set);
   };
 
-  const int nent = tcount[c];
+  // the column's query blocks (a half of a split column: the first or the
+  // second half of them)
+  int e_lo = 0, e_hi = tcount[c];
+  if (part >= 0) {
+    const int mid = e_hi / 2;
+    if (part & 1) e_lo = mid;
+    else e_hi = mid;
+  }
   const int32_t* list = tlist + c * int64_t(g.nb);
-  for (int e0 = 0; e0 < nent; e0 += kEntries) {
-    const int m = min(kEntries, nent - e0);
+  for (int e0 = e_lo; e0 < e_hi; e0 += kEntries) {
+    const int m = min(kEntries, e_hi - e0);
     for (int x = tid; x < m; x += kThreads)
       esc[x] = (block_count(g, list[e0 + x] & 0xffff) + kKvChunk - 1) / kKvChunk;
     __syncthreads();
@@ -828,6 +914,9 @@ __global__ __launch_bounds__(NW * 64) void dkv_kernel(
         }
     }
   }
+  if (SPLIT && part >= 0 && !bwd_tail_merge<NW, true>(split_flags, split_ids, split_part, part, wave,
+                                               lane, active && !own_pad, accv, acck, c, &done_sh))
+    return;
   // rows of this wave's own keys; pad key rows (and waves 6, 7) write zeros
   const bool keep = key < cj && !own_pad;
   store_rows_perm<F16>(accv, keep ? 1.f : 0.f, dv + (key0 + wave * 32) * 16, l32, half);
@@ -840,27 +929,42 @@ hipError_t launch_bwd_nw(const VsaGeom& g, const BwdArgs& a, hipStream_t s) {
   const float scale = 1.0f / sqrtf(float(g.head_dim));
   const float scale_log2 = scale * kLog2e;
   // Balanced launches (claim_row): a quarter more workgroups than rows or
-  // columns, the queue counters cleared before each of the three kernels
-  // (they run one after another on `s`, so one counter block serves all).
-  const unsigned grid = unsigned(rows + std::max<int64_t>(8, rows / 4));
+  // columns (plus one per split row), the queue and split counters cleared
+  // before each kernel (they run one after another on `s`, so one counter
+  // block and one split region serve both).  The tail split applies when no
+  // queue holds more than kSplitMaxQueueRows rows.
+  const int split =
+      a.split_flags != nullptr && (rows + 7) / 8 <= kSplitMaxQueueRows ? kSplitPerQueue : 0;
+  const int nflags = int(split_slots(rows, split));
+  const int64_t items = rows + nflags;
+  const unsigned grid = unsigned(items + std::max<int64_t>(8, items / 4));
   auto reset = [&] {
-    hipLaunchKernelGGL(bwd_queue_reset_kernel, dim3(1), dim3(64), 0, s, a.queues);
+    hipLaunchKernelGGL(bwd_queue_reset_kernel, dim3(1), dim3(256), 0, s, a.queues, a.split_flags,
+                       nflags);
     return hipGetLastError();
   };
   hipError_t e = reset();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
-                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse, a.dsum, a.row_ptr, a.col,
-                     a.uniform_k, a.nnz, static_cast<uint4*>(a.dq), a.queues, g, scale_log2,
-                     scale);
-  if ((e = hipGetLastError()) != hipSuccess || (e = reset()) != hipSuccess) return e;
-  hipLaunchKernelGGL((dkv_kernel<NW, F16>), dim3(grid), dim3(NW * 64), 0, s,
-                     static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
-                     static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse,
-                     a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk),
-                     static_cast<uint4*>(a.dv), a.queues, g, scale_log2, scale);
-  return hipGetLastError();
+  // launches that split no rows run instantiations without the merge code
+  auto run = [&](auto split_t) {
+    constexpr bool SPLIT = decltype(split_t)::value;
+    hipLaunchKernelGGL((dq_kernel<NW, F16, SPLIT>), dim3(grid), dim3(NW * 64), 0, s,
+                       static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
+                       static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse,
+                       a.dsum, a.row_ptr, a.col, a.uniform_k, a.nnz, static_cast<uint4*>(a.dq),
+                       a.queues, g, scale_log2, scale, a.split_flags, a.split_rows,
+                       a.split_part, split);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || (err = reset()) != hipSuccess) return err;
+    hipLaunchKernelGGL((dkv_kernel<NW, F16, SPLIT>), dim3(grid), dim3(NW * 64), 0, s,
+                       static_cast<const uint4*>(a.q), static_cast<const uint4*>(a.k),
+                       static_cast<const uint4*>(a.v), static_cast<const uint4*>(a.dout), a.lse,
+                       a.dsum, a.tlist, a.tcount, static_cast<uint4*>(a.dk),
+                       static_cast<uint4*>(a.dv), a.queues, g, scale_log2, scale,
+                       a.split_flags, a.split_rows, a.split_part, split);
+    return hipGetLastError();
+  };
+  return split > 0 ? run(std::true_type()) : run(std::false_type());
 }
 
 template <int NW>

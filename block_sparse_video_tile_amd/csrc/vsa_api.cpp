@@ -107,7 +107,7 @@ const char* raster_unsupported(const VsaGeom& g) {
 }
 
 struct BwdWorkspace {
-  size_t dsum, tlist, tcount, queue, total;
+  size_t dsum, tlist, tcount, queue, split, total;
 };
 BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
   const VsaGeom& g = p.g;
@@ -118,6 +118,7 @@ BwdWorkspace bwd_workspace_layout(const vsa_plan_s& p) {
   w.tlist = off; off += align256(heads * g.nb * size_t(g.nb) * 4);
   w.tcount = off; off += align256(heads * g.nb * 4);
   w.queue = off; off += vsa::kAttnQueueBytes;
+  w.split = off; off += align256(vsa::bwd_split_layout(g).total);
   w.total = off;
   return w;
 }
@@ -594,6 +595,10 @@ vsa_status vsa_block_sparse_attn_bwd(vsa_plan_t p, const void* q, const void* k,
   a.tlist = reinterpret_cast<int32_t*>(base + w.tlist);
   a.tcount = reinterpret_cast<int32_t*>(base + w.tcount);
   a.queues = reinterpret_cast<unsigned int*>(base + w.queue);
+  const vsa::BwdSplitLayout sl = vsa::bwd_split_layout(p->g);
+  a.split_flags = reinterpret_cast<unsigned int*>(base + w.split + sl.flags);
+  a.split_rows = reinterpret_cast<int32_t*>(base + w.split + sl.rows);
+  a.split_part = reinterpret_cast<float*>(base + w.split + sl.part);
   return hip_status(vsa::launch_attn_bwd(p->g, a, hipStream_t(stream)),
                     "vsa_block_sparse_attn_bwd");
 }

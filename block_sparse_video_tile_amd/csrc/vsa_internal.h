@@ -66,6 +66,11 @@ hipError_t launch_gather_v(const VsaGeom& g, const void* x, void* xbt, float* po
 // gate == nullptr: plain scatter; otherwise O + gate * oc[block] (oc fp32 [B,NH,nb,D])
 hipError_t launch_scatter(const VsaGeom& g, const void* ob, const float* oc, const void* gate,
                           void* o, hipStream_t s);
+// Tail split of the backward's balanced launches (TailSplit below, with the
+// same rule as the forward's): a split dQ row or dK/dV column leaves two
+// partial sums over halves of its entries, NW waves x 128 x 64 lanes fp32
+// per half (dkv: dV^T and dK^T tiles; dq: the first half of that).
+constexpr size_t kBwdSplitHalfFloatsPerWave = 128 * 64;
 // Device buffers of one backward call (blocked layouts; see vsa.h).
 struct BwdArgs {
   const void *q, *k, *v, *o, *dout;   // token-major blocked inputs
@@ -80,6 +85,9 @@ struct BwdArgs {
   int32_t* tlist;                     // [B*NH*nb][nb] transposed block map
   int32_t* tcount;                    // [B*NH*nb]
   unsigned int* queues;               // row-queue counters (kAttnQueueBytes)
+  unsigned int* split_flags;          // tail split: a counter per slot,
+  int32_t* split_rows;                //   the row / column of each slot,
+  float* split_part;                  //   two partial sums per slot
 };
 hipError_t launch_attn_bwd(const VsaGeom& g, const BwdArgs& a, hipStream_t s);
 
@@ -159,6 +167,22 @@ inline TailSplit split_at(const VsaGeom& g, void* base) {
   char* b = static_cast<char*>(base);
   return TailSplit{reinterpret_cast<unsigned int*>(b + l.flags), reinterpret_cast<float*>(b + l.part),
                    reinterpret_cast<int32_t*>(b + l.rows), kSplitPerQueue};
+}
+
+// Bytes of the backward's tail-split region (counters, ids, partial sums of
+// workgroups of vol/32 waves), 256-byte aligned parts.
+struct BwdSplitLayout {
+  size_t flags, rows, part, total;
+};
+inline BwdSplitLayout bwd_split_layout(const VsaGeom& g) {
+  const int64_t slots = split_slots(int64_t(g.batch) * g.heads * g.nb, kSplitPerQueue);
+  auto a256 = [](size_t n) { return (n + 255) & ~size_t(255); };
+  BwdSplitLayout l;
+  l.flags = 0;
+  l.rows = a256(size_t(slots) * 4);
+  l.part = l.rows + a256(size_t(slots) * 4);
+  l.total = l.part + size_t(slots) * 2 * (g.vol / 32) * kBwdSplitHalfFloatsPerWave * 4;
+  return l;
 }
 
 hipError_t launch_attn_fwd(const VsaGeom& g, const void* q, const void* k, const void* vt,

@@ -317,9 +317,12 @@ vsa_status vsa_block_sparse_attn_fwd_noalloc(vsa_plan_t plan, const void* q_blk,
 
 /* Bytes of device workspace vsa_block_sparse_attn_bwd needs for this plan:
  * rowsum(dO*O) [B,NH,Npad] fp32, the transposed block map
- * (B*NH*nb*nb + B*NH*nb int32) and the row-queue
- * counters of its balanced launches (rows and columns are claimed per XCD at
- * run time, as in vsa_block_sparse_attn_fwd_ws), each 256-byte aligned. */
+ * (B*NH*nb*nb + B*NH*nb int32), the row-queue counters of its balanced
+ * launches (rows and columns are claimed per XCD at run time, as in
+ * vsa_block_sparse_attn_fwd_ws) and their tail-split region (at most 128
+ * split rows or columns, each leaving two partial gradient sums of vol/32
+ * waves x 32 KB; the gradients of a split row are the sum of its halves,
+ * added in an order-independent way), each 256-byte aligned. */
 vsa_status vsa_block_sparse_attn_bwd_workspace_size(vsa_plan_t plan, size_t* bytes);
 
 /* Gradients of vsa_block_sparse_attn_fwd (h3-perf-stack log, sm_100a route

@@ -139,10 +139,13 @@ def test_backward_fp16():
     _check("fp16", got, want, blocked, ref["plan"])
 
 
-def test_backward_full_size_two_heads():
-    # the heads are independent: the oracle runs on heads 0 and 23 of the
-    # 27280-token layer with the GPU's own selection for those heads
-    wl = WORKLOADS["wan5b_k64"]
+@pytest.mark.parametrize("name,heads", [("wan5b_k64", (0, 23)), ("wan5b_k64_h3", (0, 1, 2))])
+def test_backward_full_size_whole_heads(name, heads):
+    # the heads are independent: the oracle runs on whole heads of the
+    # 27280-token layer (two of 24; all three of the 3-head shard, whose 360
+    # rows and columns the balanced launches hand out with the tail split)
+    # with the GPU's own selection for those heads
+    wl = WORKLOADS[name]
     q, kk, v = make_qkv(wl)
     do = _dout(wl, torch.bfloat16)
     plan = _plan(wl)
@@ -158,7 +161,7 @@ def test_backward_full_size_two_heads():
     vsa.vsa_score_topk(plan, qp, kp, k, col)
     ci = col.cpu().numpy()
     got, blocked = _run(plan, q, kk, v, do, None, ci, k)
-    for h in (0, wl.heads - 1):
+    for h in heads:
         hs = slice(h, h + 1)
         sub = ci.reshape(wl.heads, nb * k)[h]
         rp = np.arange(nb + 1, dtype=np.int64) * k
