@@ -456,6 +456,22 @@ def bench_backward(args, wl, plan, elem, dq, dk, dv):
     }), flush=True)
 
 
+def stage_bandwidth(plan, wl, stage_ms, fused):
+    """Algorithmic GB/s of the data-movement stages at their mean times: a
+    gather reads the raster tensor and writes the padded blocked copy (the
+    fused path's pooling passes read the raster tensor only); the scatter
+    reads the blocked output and writes the raster one (16-bit elements; the
+    fp32 means and the selected ids are negligible)."""
+    raster = wl.batch * wl.seq_len * wl.heads * wl.head_dim * 2
+    blocked = wl.batch * wl.heads * plan.padded_len * wl.head_dim * 2
+    moved = {"gather_q": raster + blocked, "gather_k": raster + blocked,
+             "gather_v": raster + blocked, "scatter": raster + blocked}
+    if fused:
+        moved = {"pool_q": raster, "pool_k": raster, "pool_v": raster}
+    return {n: round(b / (float(np.mean(stage_ms[n])) * 1e-3) / 1e9, 1)
+            for n, b in moved.items() if n in stage_ms}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -680,6 +696,9 @@ def main():
                                else "attn_fwd_kernel (fixed order)"},
         "measured_denominators": den,
         "stage_ms": {n: round(float(np.mean(v)), 4) for n, v in stage_ms.items()},
+        "stage_ms_median": {n: round(float(np.median(v)), 4) for n, v in stage_ms.items()},
+        "stage_ms_min": {n: round(float(np.min(v)), 4) for n, v in stage_ms.items()},
+        "stage_gbs": stage_bandwidth(plan, wl, stage_ms, args.fused),
         "flops_valid": f_valid,
         "flops_nominal": f_nominal,
         "attention_tflops_nominal": round(f_nominal / (t_attn * 1e-3) / 1e12, 2),
