@@ -202,6 +202,24 @@ def test_full_size_blocked_equals_plain_launch(name, dtype):
     _say(f"    {name}: balanced == plain, {plan.num_rows()} rows")
 
 
+def test_interleaved_heads_with_split_rows():
+    """One head of the (81,30,52) layer (a 12-way head shard): its K and V
+    times 8 outgrow the memory-side cache, so the queues interleave the
+    head's blocks (queue x takes positions x, x+8, ... of the cost order: 74
+    or 73 rows), and with at most 256 rows per queue the last 16 of each are
+    split: 128 split slots numbered queue by queue over unequal queues."""
+    wl = Workload("long_h1", (81, 30, 52), (4, 8, 8), 1, 1, 128, 64, seed=4)
+    plan = _plan(wl)
+    q, kk, v = make_qkv(wl)
+    qb, kb, vb, qp, kp = _gather_all(plan, q, kk, v)
+    col = _selection(plan, wl, qp, kp)
+    ws = _junk_workspace(plan)
+    plain, bal = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, ws)
+    split = _split_rows(ws, plan, strided=True)
+    assert len(split) == 128
+    _assert_same(plain, bal, "long_h1", split, plan)
+
+
 @pytest.mark.parametrize("name", ["tiny", "vol128_b2", "vol192_padded", "vol64_3d"])
 def test_small_volumes_equal_plain_launch_and_oracle(name):
     wl = WORKLOADS[name]
