@@ -62,9 +62,11 @@ __device__ inline int64_t xcd_remap(int64_t wg, int64_t n) {
 }
 
 // Block at position p of a head's cost order: blocks grouped by edge class
-// (which of the T, H and W extents the grid edge cuts: bit 2, 1, 0), the
-// classes by descending valid-token count (then class number), the blocks
-// of a class ascending.  A bijection on [0, nb).
+// (bit 2, 1, 0: the block is the last along T, H, W, the place where the
+// grid edge cuts a block if it cuts one; a grid that divides an axis has
+// last blocks of full size there), the classes by descending valid-token
+// count (then class number), the blocks of a class ascending.  A bijection
+// on [0, nb).
 __device__ inline int block_in_cost_order(const VsaGeom& g, int p) {
   // the class holding p: the last k whose start is <= p (an empty class
   // shares its start with the next one, so it is passed over)

@@ -140,10 +140,11 @@ const char* vsa_status_string(vsa_status st) {
 const char* vsa_last_error(void) { return g_last_error.c_str(); }
 
 // Class order of a head's blocks for the balanced launches: the blocks of
-// edge class c (bit 2, 1, 0: the grid edge cuts the T, H, W extent) number
-// the product over the axes of 1 (cut) or blocks-along-the-axis - 1 (not cut),
-// and hold the product of the cut extents and full block sizes as valid
-// tokens.  Classes go by descending valid-token count, ties by class number.
+// edge class c (bit 2, 1, 0: the block is the last along T, H, W, where the
+// grid edge cuts it if it cuts one) number the product over the axes of 1
+// (last) or blocks-along-the-axis - 1 (not last), and hold the product of
+// the last extents (full where the grid divides the axis) and full block
+// sizes as valid tokens.  Classes go by descending valid-token count, ties by class number.
 static void fill_cost_order(VsaGeom& g) {
   const int nbd[3] = {g.nbt, g.nbh, g.nbw};
   const int full[3] = {g.bt, g.bh, g.bw};

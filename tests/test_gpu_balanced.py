@@ -150,6 +150,44 @@ def _split_rows(ws, plan, strided=False):
     return used
 
 
+def _expected_split_rows(order, n):
+    """The rows the tail split takes, from its rule: in queue x (the rows
+    xcd_remap gives XCD x, in claim order `order`), the last min(16, count)
+    positions, slots numbered queue by queue in claim order; none when a
+    queue holds more than 256 rows."""
+    per, rem = divmod(n, 8)
+    counts = [per + (1 if x < rem else 0) for x in range(8)]
+    if max(counts) > _SPLIT_MAX_QUEUE_ROWS:
+        return np.zeros(0, np.int64)
+    out, start = [], 0
+    for c in counts:
+        s = min(_SPLIT_PER_QUEUE, c)
+        out += [int(r) for r in order[start + c - s:start + c]]
+        start += c
+    return np.array(out, np.int64)
+
+
+def _uniform_claim_order(wl):
+    """Claim order of uniform rows (queues cut as xcd_remap cuts the rows),
+    from its rule: within each head the blocks grouped by edge class (bit 2,
+    1, 0: the block is the last along T, H, W, where the grid edge may cut
+    it), the classes by descending valid-token count, then class number, the
+    blocks of a class ascending."""
+    (T, H, W), (bt, bh, bw) = wl.dit_seq_shape, wl.block_size
+    nbt, nbh, nbw = -(-T // bt), -(-H // bh), -(-W // bw)
+    keys = []
+    for b in range(nbt * nbh * nbw):
+        it, rem = divmod(b, nbh * nbw)
+        ih, iw = divmod(rem, nbw)
+        cls = (4 if it == nbt - 1 else 0) | (2 if ih == nbh - 1 else 0) | (1 if iw == nbw - 1 else 0)
+        cnt = min(bt, T - it * bt) * min(bh, H - ih * bh) * min(bw, W - iw * bw)
+        keys.append((-cnt, cls, b))
+    head = [b for _, _, b in sorted(keys)]
+    nb = len(head)
+    heads = wl.batch * wl.heads
+    return np.array([h * nb + head[p] for h in range(heads) for p in range(nb)], np.int64)
+
+
 def _assert_same(a, b, what, split_rows=(), plan=None):
     """a: plain launch, b: balanced; blocked O [B,NH,Npad,D] and LSE [B,NH,Npad]."""
     oa, ob = a[0].view(torch.int16), b[0].view(torch.int16)
@@ -194,6 +232,11 @@ def test_full_size_blocked_equals_plain_launch(name, dtype):
     strided = name == "wan13b_long"   # its heads' K and V outgrow the memory-side cache
     split = _split_rows(ws, plan, strided)
     _assert_same(plain, bal, name, split, plan)
+    if not strided:
+        # the split rows are those the rule names: the last 16 of each queue
+        # in cost order (none for queues of more than 256 rows)
+        want = _expected_split_rows(_uniform_claim_order(wl), plan.num_rows())
+        assert np.array_equal(split, want), f"{name}: split rows differ from the rule"
     # a second call on the same workspace (its counters now hold the last
     # call's counts) gives the same result again, bit for bit
     again = _both_blocked(plan, qb, kb, vb, None, col, wl.topk, ws)[1]
@@ -293,8 +336,13 @@ def test_claim_order_across_heads():
     col = torch.as_tensor(np.array([c for x in lists for c in x], np.int32)).to(DEV)
     ws = _junk_workspace(plan)
     plain, bal = _both_blocked(plan, qb, kb, vb, rp, col, 0, ws)
-    _assert_same(plain, bal, "order across heads", _split_rows(ws, plan), plan)
+    split = _split_rows(ws, plan)
+    _assert_same(plain, bal, "order across heads", split, plan)
     _check_claim_order(ws, rp_h, nt, "order across heads")
+    # 1500 rows, queues of 188 and 187: the split rows are the last 16 of
+    # each queue's claim order, slot by slot
+    want = _expected_split_rows(_expected_claim_order(rp_h, nt), len(rp_h) - 1)
+    assert len(want) == 128 and np.array_equal(split, want)
 
 
 def test_claim_order_of_ranges_longer_than_the_length_cache():
