@@ -190,8 +190,9 @@ def check_full_forward(name, k=None, dtype=vsa.VSA_DTYPE_BF16, fused=False, fp64
     Block ids: bit-exact against the float64 oracle outside near-ties.
     Attention: EVERY output row and LSE of every head against the float32
     oracle block loop run on the GPU's own map, and every row of the heads in
-    `fp64_heads` (default: the first and the last) against the float64
-    oracle, each within max-abs 2e-2 / mean-abs 2e-3 and LSE 1e-3.
+    `fp64_heads` (default: four heads spread over the layer, the first and
+    the last among them) against the float64 oracle, each within max-abs
+    2e-2 / mean-abs 2e-3 and LSE 1e-3.
     """
     wl, k, q, kk, v, plan, out, col, lse = _full_forward(name, k, dtype, fused)
     oplan = oracle.make_plan(wl.seq_len, wl.dit_seq_shape, wl.block_size, k)
@@ -202,7 +203,10 @@ def check_full_forward(name, k=None, dtype=vsa.VSA_DTYPE_BF16, fused=False, fp64
     rp, ci = oracle.selection_to_csr(gsel)
     o32, l32 = oracle.block_sparse_attention_f32(q, kk, v, oplan, rp, ci)
     compare_all_rows("all rows vs float32 oracle", out, o32, lse, l32.numpy(), oplan)
-    heads = (0, wl.heads - 1) if fp64_heads is None else fp64_heads
+    if fp64_heads is None:
+        heads = tuple(sorted({0, wl.heads // 3, (2 * wl.heads) // 3, wl.heads - 1}))
+    else:
+        heads = fp64_heads
     nb = oplan.num_blocks
     rows = [(b * wl.heads + h) * nb + i for b in range(wl.batch) for h in heads
             for i in range(nb)]

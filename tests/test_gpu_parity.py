@@ -264,7 +264,7 @@ def test_forward_tiny_end_to_end_and_deterministic():
 @pytest.mark.parametrize("name,k", [("wan5b_k64", None), ("wan5b_k16", None), ("wan5b_k32", None),
                                     ("wan13b_long", None)])
 def test_full_size_forward_every_row(name, k):
-    # every row of every head vs the float32 oracle, two whole heads vs float64
+    # every row of every head vs the float32 oracle, four whole heads vs float64
     check_full_forward(name, k)
 
 
